@@ -1,0 +1,319 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+The pages print no worked numeric example, so each oracle function is pinned
+by closed forms, brute-force characterisations on tiny inputs, and library
+routines that compute the same definition independently (torch's scaled
+dot-product attention, scipy's logsumexp, torch's fp32->bf16 conversion).
+Each pin is chosen so that a plausible slip (dividing by P instead of the
+valid-token count, a wrong head-to-group map, a reversed tie-break, a missed
+mask) fails it.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import vx_oracle as O
+
+
+# ---------------------------------------------------------------- centroids
+
+def _keys_equal_position(cap, Hkv, P, D, L, garbage=1e6):
+    """Key of token t (every dim) = t + 1000*g; invalid slots hold garbage."""
+    k = np.full((cap, Hkv, P, D), garbage)
+    for p in range(cap):
+        for g in range(Hkv):
+            for s in range(P):
+                t = p * P + s
+                if t < L:
+                    k[p, g, s, :] = t + 1000.0 * g
+    return k
+
+
+@pytest.mark.parametrize("P,L", [(16, 1024), (16, 1000), (4, 9), (64, 65), (16, 1)])
+def test_centroid_closed_form_partial_last_page(P, L):
+    cap = -(-L // P) + 2  # page-table headroom beyond the pages in use
+    k = _keys_equal_position(cap, 2, P, 3, L)
+    c = O.centroids(k, L, P)
+    n = -(-L // P)
+    assert c.shape == (n, 2, 3)
+    for p in range(n):
+        nv = min(P, L - p * P)
+        first = p * P
+        mean_t = first + (nv - 1) / 2.0  # mean of an arithmetic run
+        for g in range(2):
+            np.testing.assert_allclose(c[p, g], mean_t + 1000.0 * g, rtol=0, atol=1e-9)
+
+
+def test_centroid_identical_keys_is_the_key():
+    rng = np.random.default_rng(1)
+    P, L = 16, 40
+    key = rng.standard_normal((1, 2, 1, 8))
+    k = np.broadcast_to(key, (3, 2, P, 8)).copy()
+    c = O.centroids(k, L, P)
+    for p in range(3):
+        np.testing.assert_allclose(c[p], key[0, :, 0, :], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- bf16
+
+def test_round_to_bf16_matches_torch_conversion():
+    rng = np.random.default_rng(2)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).float().double().numpy()
+    got = O.round_to_bf16(x32.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_round_to_bf16_ties_to_even():
+    s = 2.0 ** -7  # bf16 spacing on [1, 2)
+    cases = {1.0 + s / 2: 1.0, 1.0 + 3 * s / 2: 1.0 + 2 * s, -(1.0 + s / 2): -1.0,
+             1.0 + s / 2 + 1e-12: 1.0 + s, 0.0: 0.0, 3.0: 3.0}
+    for x, want in cases.items():
+        assert O.round_to_bf16(np.array([x]))[0] == want, x
+
+
+# ---------------------------------------------------------------- scores
+
+def test_scores_one_hot_query_picks_group_and_dim():
+    rng = np.random.default_rng(3)
+    Hq, Hkv, D, n = 6, 2, 5, 7  # G = 3: heads 0-2 -> KV head 0, 3-5 -> 1
+    cent = rng.standard_normal((n, Hkv, D))
+    for h in range(Hq):
+        for d in (0, 3):
+            q = np.zeros((Hq, D))
+            q[h, d] = 1.0
+            s = O.page_scores(q, cent, Hkv, 0.25)
+            g = h // 3
+            np.testing.assert_allclose(s[g], 0.25 * cent[:, g, d], rtol=1e-15)
+            np.testing.assert_array_equal(s[1 - g], 0.0)
+
+
+def test_scores_sum_over_group_heads_and_zero_query():
+    rng = np.random.default_rng(4)
+    Hq, Hkv, D, n = 4, 2, 8, 5
+    cent = rng.standard_normal((n, Hkv, D))
+    q = rng.standard_normal((Hq, D))
+    s = O.page_scores(q, cent, Hkv, 1.0)
+    # a group's score is additive in its heads: zero one head, add it back
+    for h in range(Hq):
+        qa = q.copy(); qa[h] = 0
+        qb = np.zeros_like(q); qb[h] = q[h]
+        np.testing.assert_allclose(O.page_scores(qa, cent, Hkv, 1.0) +
+                                   O.page_scores(qb, cent, Hkv, 1.0), s, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(O.page_scores(np.zeros((Hq, D)), cent, Hkv, 1.0), 0.0)
+
+
+# ---------------------------------------------------------------- selection
+
+def test_forced_pages_cases():
+    assert O.forced_pages(0, 1, 1) == []
+    assert O.forced_pages(1, 1, 1) == [0]
+    assert O.forced_pages(2, 1, 2) == [0, 1]
+    assert O.forced_pages(5, 1, 2) == [0, 3, 4]
+    assert O.forced_pages(64, 0, 1) == [63]
+    assert O.forced_pages(10, 0, 0) == []
+
+
+def _beats(s, x, y):
+    return s[x] > s[y] or (s[x] == s[y] and x < y)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_exact_rank_characterisation(seed):
+    """Brute force: a candidate is chosen iff fewer than k candidates beat it
+    (higher score, or equal score and lower index)."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 65))
+    k = int(rng.integers(0, 20))
+    n_sink, n_local = int(rng.integers(0, 2)), int(rng.integers(0, 3))
+    s = rng.integers(-3, 4, size=n).astype(np.float64)  # many duplicates
+    if seed % 3 == 0:
+        s = rng.standard_normal(n)
+    sel = O.topk_exact(s, k, n_sink, n_local)
+    assert sel.shape == (k + n_sink + n_local,)
+    got = [int(x) for x in sel if x >= 0]
+    assert got == sorted(set(got))  # ascending, no repeats
+    assert all(x == -1 for x in sel[len(got):])  # padding after the ids
+    forced = O.forced_pages(n, n_sink, n_local)
+    assert set(forced) <= set(got)
+    cand = [p for p in range(n) if p not in forced]
+    chosen = set(got) - set(forced)
+    assert len(chosen) == min(k, len(cand))
+    for c in cand:
+        nbeat = sum(_beats(s, x, c) for x in cand if x != c)
+        assert (c in chosen) == (nbeat < k), (c, nbeat, k)
+
+
+def test_topk_exact_ties_and_signed_zero():
+    s = np.zeros(10)
+    assert list(O.topk_exact(s, 3, 0, 1)) == [0, 1, 2, 9]
+    assert list(O.topk_exact(s, 3, 1, 1)) == [0, 1, 2, 3, 9]
+    s2 = np.array([-0.0, 0.0, -0.0, 0.0])
+    assert list(O.topk_exact(s2, 2, 0, 0)) == [0, 1]
+    s3 = np.array([0.0, -0.0, 1.0])
+    assert list(O.topk_exact(s3, 2, 0, 0)) == [0, 2]
+    # k at least the candidate count -> every page
+    assert list(O.topk_exact(np.arange(5.0), 9, 1, 1)) == [0, 1, 2, 3, 4] + [-1] * 6
+
+
+# ---------------------------------------------------------------- approx
+
+def test_approx_equals_exact_without_bucket_collisions():
+    for n in (5, 50, 200, 257):
+        s = np.arange(n, dtype=np.float32)[::-1].copy()  # one candidate per bucket
+        for k in (1, 4, 16, 64):
+            for rnd in (0, 7, 2**32 - 1):
+                a = O.topk_approx(s, k, 1, 1, rnd)
+                e = O.topk_exact(s.astype(np.float64), k, 1, 1)
+                np.testing.assert_array_equal(a, e)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_approx_invariants(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(2, 1100))
+    k = int(rng.integers(1, 70))
+    s = rng.standard_normal(n).astype(np.float32)
+    if seed % 4 == 0:
+        s = np.round(s * 3).astype(np.float32)  # heavy ties
+    rnd = int(rng.integers(0, 2**32))
+    sel = O.topk_approx(s, k, 0, 1, rnd)
+    got = set(int(x) for x in sel if x >= 0)
+    forced = set(O.forced_pages(n, 0, 1))
+    cand = np.array([p for p in range(n) if p not in forced])
+    chosen = got - forced
+    assert len(chosen) == min(k, len(cand))
+    if len(cand) <= k:
+        return
+    b = O.approx_buckets(s[cand])
+    # buckets are monotone in the score
+    order = np.argsort(s[cand], kind="stable")
+    assert np.all(np.diff(b[order]) >= 0)
+    t = min(b[np.isin(cand, list(chosen))])
+    assert set(cand[b > t]) <= chosen  # everything above the boundary
+    assert not (chosen & set(cand[b < t]))  # nothing below it
+    members = list(cand[b == t])
+    r = len(chosen & set(members))
+    off = rnd % len(members)
+    want = {members[(off + j) % len(members)] for j in range(r)}
+    assert chosen & set(members) == want
+
+
+def test_approx_recall_on_normal_scores():
+    rng = np.random.default_rng(7)
+    rec = []
+    for _ in range(40):
+        s = rng.standard_normal(1024).astype(np.float32)
+        a = set(O.topk_approx(s, 64, 0, 0, int(rng.integers(0, 2**32))))
+        e = set(O.topk_exact(s.astype(np.float64), 64, 0, 0))
+        rec.append(len(a & e) / 64)
+    assert np.mean(rec) > 0.97
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa(q, K, V, scale):
+    """torch's scaled dot-product attention, fp64 on the CPU."""
+    qt = torch.from_numpy(q)[None, None, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, torch.from_numpy(K)[None, None], torch.from_numpy(V)[None, None], scale=scale)
+    return out[0, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("mla", [False, True])
+def test_full_selection_equals_dense_attention(mla):
+    rng = np.random.default_rng(11)
+    P, L, Hkv, Hq = 8, 53, (1 if mla else 2), 4
+    Dk, Dv = (12, 8) if mla else (6, 5)
+    cap = -(-L // P) + 1
+    q = rng.standard_normal((Hq, Dk))
+    k = rng.standard_normal((cap, Hkv, P, Dk))
+    v = None if mla else rng.standard_normal((cap, Hkv, P, Dv))
+    n = -(-L // P)
+    res = O.decode_sequence({"q": q, "k": k, "v": v, "seq_len": L,
+                             "rand_u32": np.zeros(Hkv, np.uint32)},
+                            page_size=P, num_kv_heads=Hkv, k=n, n_sink=1,
+                            n_local=1, score_scale=0.3, sm_scale=0.7, mla=mla,
+                            head_dim_v=Dv)
+    vv = k[..., :Dv] if mla else v
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        K = k[:, g].reshape(cap * P, Dk)[:L]
+        V = vv[:, g].reshape(cap * P, Dv)[:L]
+        np.testing.assert_allclose(res["out"][h], _sdpa(q[h], K, V, 0.7), rtol=1e-12, atol=1e-12)
+        z = 0.7 * K @ q[h]
+        np.testing.assert_allclose(res["lse"][h], scipy.special.logsumexp(z), rtol=1e-13)
+
+
+def test_attention_equal_keys_gives_mean_of_values():
+    rng = np.random.default_rng(12)
+    P, L = 4, 10  # pages 0,1 full, page 2 has 2 tokens
+    k = np.broadcast_to(rng.standard_normal(3), (3, 1, P, 3)).copy()
+    v = rng.standard_normal((3, 1, P, 2))
+    v[2, 0, 2:, :] = 1e9  # invalid slots must not leak in
+    q = rng.standard_normal((2, 3))
+    sel = np.array([[0, 2, -1]])
+    out, lse = O.attention(q, k, v, L, P, sel, 0.5, 1)
+    want = np.concatenate([v[0, 0], v[2, 0, :2]]).mean(axis=0)
+    for h in range(2):
+        np.testing.assert_allclose(out[h], want, rtol=1e-13)
+        z = 0.5 * float(k[0, 0, 0] @ q[h])
+        np.testing.assert_allclose(lse[h], z + math.log(6), rtol=1e-13)
+
+
+def test_attention_single_token_and_empty_selection():
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((1, 1, 16, 4))
+    v = rng.standard_normal((1, 1, 16, 3))
+    q = rng.standard_normal((1, 4))
+    out, lse = O.attention(q, k, v, 1, 16, np.array([[0]]), 1.0, 1)
+    np.testing.assert_array_equal(out[0], v[0, 0, 0])
+    np.testing.assert_allclose(lse[0], float(k[0, 0, 0] @ q[0]), rtol=1e-15)
+    out, lse = O.attention(q, k, v, 1, 16, np.array([[-1]]), 1.0, 1)
+    assert np.all(out == 0) and lse[0] == -np.inf
+
+
+def test_hand_worked_example():
+    """Worked by hand: P=2, L=5, Hq=2, Hkv=1, D=2, scale 1, sm_scale 1.
+    keys t0..t4 = (1,0) (3,0) | (0,2) (0,4) | (-2,-2)
+      centroids: page0 (2,0), page1 (0,3), page2 (-2,-2) (one valid token)
+    q = h0 (1,0), h1 (0,1): group sum (1,1) -> scores 2, 3, -4
+    k=1 ranked page + last page: candidates {0,1} -> page 1; sel = [1, 2]
+    values t2 (1,0), t3 (-1,0), t4 (0,5)
+    h0 logits over t2,t3,t4 = 0, 0, -2 -> out = (0, 5e^-2) / (2 + e^-2)
+    h1 logits = 2, 4, -2 -> weights e^2, e^4, e^-2
+    """
+    k = np.zeros((3, 1, 2, 2)); v = np.zeros((3, 1, 2, 2))
+    keys = [(1, 0), (3, 0), (0, 2), (0, 4), (-2, -2)]
+    vals = [(9, 9), (9, 9), (1, 0), (-1, 0), (0, 5)]
+    for t in range(5):
+        k[t // 2, 0, t % 2] = keys[t]
+        v[t // 2, 0, t % 2] = vals[t]
+    k[2, 0, 1] = (50, 50)  # invalid slot
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    r = O.decode_sequence({"q": q, "k": k, "v": v, "seq_len": 5,
+                           "rand_u32": np.zeros(1, np.uint32)}, page_size=2,
+                          num_kv_heads=1, k=1, n_sink=0, n_local=1,
+                          score_scale=1.0, sm_scale=1.0)
+    np.testing.assert_allclose(r["centroids"][:, 0], [[2, 0], [0, 3], [-2, -2]])
+    np.testing.assert_allclose(r["scores"][0], [2, 3, -4])
+    assert list(r["sel"][0]) == [1, 2]
+    e = math.exp
+    np.testing.assert_allclose(r["out"][0], [0, 5 * e(-2) / (2 + e(-2))], rtol=1e-14)
+    den = e(2) + e(4) + e(-2)
+    np.testing.assert_allclose(r["out"][1], [(e(2) - e(4)) / den, 5 * e(-2) / den], rtol=1e-14)
+    np.testing.assert_allclose(r["lse"][1], math.log(den), rtol=1e-14)
+
+
+def test_approx_buckets_closed_form():
+    # w = 4 -> 256 / 4 = 64 buckets per unit; the maximum clamps to 255
+    np.testing.assert_array_equal(
+        O.approx_buckets(np.array([0, 1, 2, 3, 4], np.float32)), [0, 64, 128, 192, 255])
+    np.testing.assert_array_equal(
+        O.approx_buckets(np.array([-1.0, -0.75, -0.5, 1.0], np.float32)), [0, 32, 64, 255])
+    np.testing.assert_array_equal(O.approx_buckets(np.full(7, 2.5, np.float32)), 0)
