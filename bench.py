@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of one block top-k sparse-attention decode step on one MI355X.
+
+A step is the whole hot path over one batch: cache-stage refresh of each
+sequence's newest page, page scoring, top-k selection, split-K attention and
+its log-sum-exp merge. Inputs are seeded synthetic tensors already resident
+in HBM. Several replicas of the workload (same values, different memory)
+rotate from step to step so that the 256 MB Infinity Cache cannot hold a
+step's working set between two uses. Each step of a replica is captured once
+in a HIP graph; the timed region replays them K times between two
+synchronisations.
+
+Prints one JSON line: seqs/s (value), KV tokens/s, achieved HBM GB/s of the
+step and, in "roofline", of its dominant kernel stage (algorithmic bytes /
+its average duration from HIP events around graph replays of that stage
+alone), and "cpu_baseline", the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode seqs/s + KV tokens/s + achieved HBM GB/s vs peak"
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+DESCR = {
+    "tiny_fp32": "B=1 Hq=2 Hkv=1 D=64 P=16 L=1024 fp32, top-8 + last page",
+    "gqa_bf16": "B=32 Hq=16 Hkv=8 D=128 P=16 L~U[2048,4096] bf16, top-16 + sink + last",
+    "longgen_bf16": "B=64 Hq=32 Hkv=8 D=128 P=16 L~U[8192,32768] bf16, top-128 + sink + last 2",
+    "mla_bf16": "B=32 Hq=32 latent 576 (512+64 rope) Dv=512 P=64 L~U[16384,65536] bf16, top-32 + sink + last",
+    "largebatch_bf16": "B=256 Hq=64 Hkv=8 D=128 P=64 L~lognormal(16384, ln2) in [4096,65536] bf16, top-64",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_bf16", choices=sorted(DESCR))
+    ap.add_argument("--mode", default="exact", choices=["exact", "approx"])
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 1 GB touched")
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(w, step):
+    """Algorithmic bytes of one step: every in-use page's centroid row once,
+    plus the valid tokens of every selected page (K and V rows)."""
+    s = w.spec
+    sel = step.sel.cpu().numpy()
+    cnt = step.sel_count.cpu().numpy()
+    P = s.page_size
+    kv_elt = 4 if s.kv_dtype == "f32" else 2
+    cent_elt = 2 if s.mla else 4
+    n_pages = np.array([w.n_pages(b) for b in range(s.batch)])
+    cent_bytes = int(n_pages.sum()) * s.num_kv_heads * s.head_dim_k * cent_elt
+    row = (s.head_dim_k if s.mla else s.head_dim_k + s.head_dim_v) * kv_elt
+    tokens = 0
+    for b in range(s.batch):
+        L = int(w.seq_lens[b])
+        for g in range(s.num_kv_heads):
+            ids = sel[b, g, :cnt[b, g]]
+            tokens += int(np.clip(L - ids.astype(np.int64) * P, 0, P).sum())
+    return cent_bytes, tokens * row, tokens
+
+
+def cpu_baseline(w, step, seconds):
+    """The oracle as it stands, single-threaded, on whole sequences of the same
+    workload until `seconds` of CPU work have run (or the batch is done)."""
+    from oracle import vx_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    s = w.spec
+    done, t_total = 0, 0.0
+    try:
+        for b in range(s.batch):
+            seq = w.host_sequence(b)
+            t0 = time.perf_counter()
+            O.decode_sequence(seq, page_size=s.page_size, num_kv_heads=s.num_kv_heads,
+                              k=step.k, n_sink=step.n_sink, n_local=step.n_local,
+                              score_scale=step.score_scale, sm_scale=step.sm_scale, mla=s.mla,
+                              head_dim_v=s.head_dim_v, approx=step.mode == 1)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= seconds:
+                break
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    return {"value": done / t_total, "unit": "seqs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {s.batch} sequences of the same workload, whole decode step "
+                      f"each (centroids, scores, selection, attention), numpy fp64, "
+                      f"{t_total:.1f} s"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log("copy calibration: 5 launches, each reads 1 GiB and writes 1 GiB")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              f"(the path shards by sequence with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if a.copy_calibration:
+        copy_calibration()
+        return
+
+    from sparse_attention_decode_amd import binding as V
+    from sparse_attention_decode_amd import workloads as W
+    from sparse_attention_decode_amd.step import DecodeStep
+
+    torch.cuda.set_device(0)
+    mode = V.VX_TOPK_APPROX if a.mode == "approx" else V.VX_TOPK_EXACT
+    sp = W.spec(a.workload)
+    log(f"workload {a.workload}: generating on cuda:0")
+    w0 = W.make(sp, "cuda", seed=0)
+    base = DecodeStep(w0, mode=mode)
+    base.rebuild_centroids()
+    base.run()
+    torch.cuda.synchronize()
+    cent_b, kv_b, tokens = step_bytes(w0, base)
+    total_b = cent_b + kv_b
+    R = a.replicas or max(1, min(16, math.ceil(1.0e9 / total_b)))
+    log(f"step touches {total_b / 1e6:.1f} MB (centroids {cent_b / 1e6:.1f}, selected KV "
+        f"{kv_b / 1e6:.1f}); {R} replica(s)")
+    ws, steps = [w0], [base]
+    for _ in range(R - 1):
+        w = w0.replicate()
+        st = DecodeStep(w, mode=mode)
+        st.rebuild_centroids()
+        ws.append(w)
+        steps.append(st)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def capture(fn_per_replica):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for st in steps:  # one eager pass before capture
+                fn_per_replica(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream, capture_error_mode="thread_local"):
+            for st in steps:
+                fn_per_replica(st)
+        torch.cuda.synchronize()
+        return g
+
+    g_step = capture(lambda st: st.run())
+    # single-replica graphs for a remainder of K not divisible by R
+    singles = []
+    for st in steps:
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=stream, capture_error_mode="thread_local"):
+            st.run()
+        singles.append(g1)
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(stream):
+        for i in range(max(1, a.warmup // R)):
+            g_step.replay()
+    torch.cuda.synchronize()
+    full, rem = divmod(a.steps, R)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i in range(full):
+            g_step.replay()
+        for i in range(rem):
+            singles[i].replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+    log(f"{a.steps} steps: {ms_step * 1e3:.2f} us/step (host wall {wall * 1e3 / a.steps * 1e3:.2f} us)")
+
+    # per-stage durations (each stage alone, graph replays of all replicas)
+    stages = {
+        "cache_refresh": lambda st: st.refresh_centroids(),
+        "page_scores": lambda st: st.score(),
+        "topk": lambda st: st.select(),
+        "attention_merge": lambda st: st.attend(),
+    }
+    stage_us = {}
+    for name, fn in stages.items():
+        g = capture(fn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0.record(stream)
+            for _ in range(a.stage_reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        stage_us[name] = e0.elapsed_time(e1) * 1e3 / (a.stage_reps * R)
+        del g
+    log("stage us: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+
+    t_step = ms_step / 1e3
+    s = sp
+    seqs_per_s = s.batch / t_step
+    kv_tokens_per_s = tokens / s.num_kv_heads / t_step
+    step_gbps = total_b / t_step / 1e9
+    stage_bytes = {"page_scores": cent_b, "attention_merge": kv_b}
+    dom = max(stage_bytes, key=lambda k: stage_us[k])
+    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": seqs_per_s,
+        "unit": "seqs/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if s.kv_dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{a.workload}: {DESCR[a.workload]}", "topk_mode": a.mode,
+                   "replicas": R, "hip_graph": True},
+        "kv_tokens_per_s": kv_tokens_per_s,
+        "step_bytes": total_b,
+        "step_hbm_GBps": step_gbps,
+        "step_frac_of_peak": step_gbps / PEAK_GBPS,
+        "stage_us": stage_us,
+        "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_GBPS, "traffic": None, "kernel": dom,
+                     "bytes_per_launch": stage_bytes[dom]},
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w0, base, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

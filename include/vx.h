@@ -1,0 +1,213 @@
+/*
+ * vx.h -- C ABI of the block top-k sparse-attention decode step (gfx950).
+ *
+ * The step is the block top-k method of the Vortex paper note
+ * ("Vortex: Efficient and Programmable Sparse Attention Serving for AI
+ * Agents", papers.chlience.com), section "System design > 1. vFlow":
+ *   cache stage    per-page key centroid, query independent  -> vx_centroid_update
+ *   indexer        query x centroid scores                    -> vx_page_scores
+ *                  top-k pages per (sequence, KV head)        -> vx_topk_pages
+ *   attention      exact softmax over the selected pages      -> vx_sparse_decode
+ * Section "System design > 2. vTensor" gives the paged layout (a tensor with
+ * batch size, a pointer array and a page-index structure): vx_pages below.
+ * Section "System design > 3. Execution backend" gives the workload planner
+ * (vx_plan_decode) and the radix top-k with its approximate mode.
+ *
+ * Conventions shared by every entry point
+ *   - Every buffer argument is DEVICE memory owned by the caller, unless the
+ *     comment says "host". The library allocates nothing and keeps no
+ *     pointer after a call returns.
+ *   - Calls are asynchronous and ordered on `stream`; none synchronises the
+ *     host. A call returns once its kernels are enqueued.
+ *   - Arguments are validated on the host before any GPU work. A bad
+ *     argument returns VX_ERR_INVALID_ARG, an unsupported shape or dtype
+ *     VX_ERR_UNSUPPORTED, a short workspace VX_ERR_WORKSPACE; nothing is
+ *     launched then. A failed launch returns VX_ERR_HIP. vx_last_error()
+ *     returns a thread-local message for the last failure.
+ *   - Device-side contract (not checked on the host, which never reads device
+ *     memory): 1 <= seq_lens[b] <= (indptr[b+1]-indptr[b]) * page_size and
+ *     0 <= page_ids[j] < num_pool_pages. Kernels clamp both so that no access
+ *     leaves its buffer; results for a sequence that breaks them are
+ *     unspecified.
+ *   - Entry points are reentrant; the only library state is a per-device
+ *     cache of the compute-unit count.
+ *
+ * Memory layouts (row-major, innermost last)
+ *   q          [B][Hq][Dk]                     q_dtype
+ *   k_pool     [num_pool_pages][Hkv][P][Dk]    kv_dtype
+ *   v_pool     [num_pool_pages][Hkv][P][Dv]    kv_dtype  (MLA: unused, V = K[..., :Dv])
+ *   centroids  [num_pool_pages][Hkv][Dk]       fp32      (indexed by physical page)
+ *   cent_bf16  [num_pool_pages][Hkv][Dk]       bf16      (RNE of the fp32 centroid)
+ *   scores     [Hkv][total_pages]              fp32      (entry j of page table)
+ *   sel        [B][Hkv][sel_stride]            int32     logical page ids, ascending, -1 padded
+ *   sel_count  [B][Hkv]                        int32
+ *   out        [B][Hq][Dv]                     fp32
+ *   lse        [B][Hq]                         fp32      natural log
+ * Query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef VX_H_
+#define VX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vx_status {
+  VX_OK = 0,
+  VX_ERR_INVALID_ARG = 1,
+  VX_ERR_UNSUPPORTED = 2,
+  VX_ERR_WORKSPACE = 3,
+  VX_ERR_HIP = 4
+} vx_status;
+
+typedef enum vx_dtype { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
+
+typedef enum vx_topk_mode {
+  VX_TOPK_EXACT = 0,  /* radix select, exact ranking */
+  VX_TOPK_APPROX = 1  /* remap + one digit pass + stochastic boundary fill */
+} vx_topk_mode;
+
+/* Paged, ragged batch metadata (the page-index structure of a vTensor).
+ * Device arrays: indptr[B+1] (indptr[0] = 0, non-decreasing), page_ids
+ * [total_pages] physical page of each page-table entry, seq_lens[B] valid
+ * tokens. Sequence b owns entries indptr[b] .. indptr[b+1]-1; its logical
+ * page p (p < ceil(seq_lens[b] / page_size)) is physical page
+ * page_ids[indptr[b] + p]. Entries past the pages in use are capacity for
+ * appended tokens. Host ints total_pages (= indptr[B]) and max_pages
+ * (= max_b indptr[b+1]-indptr[b]) size the launches without a device read. */
+typedef struct vx_pages {
+  int32_t batch;
+  int32_t page_size;      /* 16 or 64 */
+  int32_t num_pool_pages;
+  int32_t total_pages;    /* host copy of indptr[B] */
+  int32_t max_pages;      /* host copy of the largest per-sequence capacity */
+  const int32_t* indptr;
+  const int32_t* page_ids;
+  const int32_t* seq_lens;
+} vx_pages;
+
+/* Head geometry. GQA: Hkv KV heads, Dk == Dv in {64, 128}. MLA (mla = 1):
+ * one latent stream (Hkv = 1), Dk = 576 (512 latent + 64 rope), Dv = 512,
+ * values are the first Dv columns of the key rows. */
+typedef struct vx_geom {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim_k;
+  int32_t head_dim_v;
+  int32_t mla;
+  vx_dtype q_dtype;
+  vx_dtype kv_dtype;
+} vx_geom;
+
+/* Launch plan chosen by the workload planner (host only). */
+typedef struct vx_plan {
+  int32_t num_splits;        /* attention work items per (sequence, KV head) */
+  int32_t pages_per_split;   /* selected pages each split streams */
+  int32_t score_pages_per_block;
+  int32_t score_blocks;
+  int32_t topk_threads;      /* threads per (sequence, KV head) segment */
+  int32_t num_cus;
+  size_t workspace_bytes;    /* what vx_sparse_decode needs for this plan */
+} vx_plan;
+
+/* Cache stage: refresh the key centroids of pages.
+ * (Vortex paper note, "System design > 1. vFlow": the cache stage precomputes
+ * a query-independent statistic per block; for block top-k the key centroid.)
+ *
+ * centroid[pid][g][:] = (sum over the page's valid tokens t, in token order,
+ * of K[pid][g][t][:] in fp32) / n_valid, one IEEE fp32 divide;
+ * cent_bf16 (nullable) receives its round-to-nearest-even bf16 copy.
+ * Pages past a sequence's last token get zeros.
+ *
+ * first_token == NULL: rebuild every page-table entry (setup / resume).
+ * first_token != NULL ([B] device): refresh, for each sequence b, the pages
+ *   holding tokens first_token[b] .. seq_lens[b]-1. A negative value counts
+ *   from the end (seq_lens[b] + first_token[b]), so a constant -1 refreshes
+ *   only the newest token's page at every decode step. Each refreshed page is
+ *   recomputed from its tokens, so the result equals a rebuild bit for bit.
+ * k_new / v_new (nullable, require first_token): [B][Hkv][Dk] and
+ *   [B][Hkv][Dv] in kv_dtype; written first into the slot of token
+ *   seq_lens[b]-1 of k_pool / v_pool (v_new needs v_pool, and is ignored for
+ *   MLA). k_pool is only written when k_new is given. */
+vx_status vx_centroid_update(const vx_pages* pages, const vx_geom* geom,
+                             void* k_pool, void* v_pool,
+                             const int32_t* first_token,
+                             const void* k_new, const void* v_new,
+                             float* centroids, void* cent_bf16,
+                             hipStream_t stream);
+
+/* Indexer scoring (Vortex paper note, "System design > 1. vFlow": a matrix
+ * product of the query with the centroids).
+ * GQA: scores[g][j] = score_scale * sum_{h in group g} q[b][h] . centroids[pid][g]
+ *   with fp32 centroids, evaluated as the dot of the fp32 group-summed query
+ *   with the centroid row.
+ * MLA: centroids is the bf16 copy [pool][576]; the [Hq x 576] x [576 x pages]
+ *   product runs on bf16 MFMA with fp32 accumulation and is summed over the
+ *   query heads: scores[0][j] = score_scale * sum_h q[b][h] . cent_bf16[pid].
+ * j runs over the entries of sequence b that are in use (p < ceil(L/P));
+ * other entries of `scores` are left untouched. */
+vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom,
+                         const void* q, const void* centroids,
+                         float score_scale, float* scores, hipStream_t stream);
+
+/* Indexer selection: per (sequence b, KV head g), keep the forced pages (the
+ * first n_sink pages and the last n_local pages) plus the top-k other pages
+ * ranked by (score descending, logical page index ascending); -0.0 and +0.0
+ * rank equal. (Vortex paper note, "System design > 1. vFlow": keep the top-k
+ * blocks; "System design > 3. Execution backend": radix top-k, with
+ * stochastic early termination and remapping as an approximate option.)
+ * sel[b][g][0..sel_count[b][g]) = chosen logical ids ascending, -1 after.
+ * sel_stride >= k + n_sink + n_local. Scores must be finite.
+ * mode VX_TOPK_APPROX: candidates' scores are mapped affinely onto 256
+ *   buckets (fp32: w = max-min, bucket = min(255, floor((s-min)*(256/w))));
+ *   one histogram pass finds the boundary bucket; every candidate above it is
+ *   kept and the remaining r places go to r members of the boundary bucket
+ *   taken cyclically in index order from offset rand_u32[b*Hkv+g] mod
+ *   (members). rand_u32 ([B][Hkv] device) is required in this mode only. */
+vx_status vx_topk_pages(const vx_pages* pages, int32_t num_kv_heads,
+                        const float* scores, int32_t k, int32_t n_sink,
+                        int32_t n_local, int32_t mode, const uint32_t* rand_u32,
+                        int32_t* sel, int32_t sel_stride, int32_t* sel_count,
+                        hipStream_t stream);
+
+/* Sparse attention (Vortex paper note, "System design > 1. vFlow": exact
+ * softmax attention on the selected blocks). For query head h of sequence b
+ * (KV head g = h / G) over the valid tokens t of the pages in
+ * sel[b][g][0..sel_count[b][g]):
+ *   z_t = sm_scale * q[b][h] . K_t,  out[b][h] = sum_t softmax(z)_t V_t,
+ *   lse[b][h] = ln sum_t exp(z_t) (nullable).
+ * Split-K: the planner (or num_splits > 0) cuts each selection into splits
+ * processed in parallel; their partial results are merged by log-sum-exp.
+ * A (b, h) with an empty selection gets out = 0, lse = -inf.
+ * workspace == NULL: only writes the bytes needed to *workspace_bytes and
+ * returns VX_OK. Otherwise *workspace_bytes must be at least that size.
+ * The workspace holds partial results only; its contents need no setup. */
+vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom,
+                           const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* sel,
+                           int32_t sel_stride, const int32_t* sel_count,
+                           float sm_scale, float* out, float* lse,
+                           int32_t num_splits, void* workspace,
+                           size_t* workspace_bytes, hipStream_t stream);
+
+/* Workload planner (Vortex paper note, "System design > 3. Execution
+ * backend": plan by batch size, sequence length, layout and operator).
+ * Host only: fills *plan from host sizes; num_cus <= 0 queries the current
+ * device, num_splits <= 0 lets the planner choose. */
+vx_status vx_plan_decode(const vx_pages* pages, const vx_geom* geom,
+                         int32_t sel_stride, int32_t num_splits,
+                         int32_t num_cus, vx_plan* plan);
+
+const char* vx_status_string(vx_status status);
+const char* vx_last_error(void);
+int32_t vx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VX_H_ */

@@ -1,0 +1,318 @@
+// C ABI of the block top-k sparse-attention decode step: argument checks,
+// the workload planner, and kernel dispatch. Every check here runs on the
+// host before any HIP call, so a rejected call touches no GPU state.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "vx_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+vx_status fail(vx_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+vx_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return VX_OK;
+  return fail(VX_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define VX_CHECK(cond, st, ...) \
+  do {                          \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+vx_status check_pages(const vx_pages* p) {
+  VX_CHECK(p, VX_ERR_INVALID_ARG, "pages is NULL");
+  VX_CHECK(p->batch >= 0, VX_ERR_INVALID_ARG, "batch < 0");
+  VX_CHECK(p->page_size == 16 || p->page_size == 64, VX_ERR_UNSUPPORTED,
+           "page_size %d (supported: 16, 64)", p->page_size);
+  VX_CHECK(p->total_pages >= 0, VX_ERR_INVALID_ARG, "total_pages < 0");
+  VX_CHECK(p->max_pages >= 0 && p->max_pages <= p->total_pages, VX_ERR_INVALID_ARG,
+           "max_pages %d outside [0, total_pages=%d]", p->max_pages, p->total_pages);
+  VX_CHECK(p->total_pages == 0 || p->num_pool_pages >= 1, VX_ERR_INVALID_ARG,
+           "num_pool_pages < 1");
+  VX_CHECK(p->batch == 0 || (p->indptr && p->seq_lens), VX_ERR_INVALID_ARG,
+           "indptr or seq_lens is NULL");
+  VX_CHECK(p->total_pages == 0 || p->page_ids, VX_ERR_INVALID_ARG, "page_ids is NULL");
+  VX_CHECK(p->batch > 0 || p->total_pages == 0, VX_ERR_INVALID_ARG,
+           "total_pages > 0 with batch 0");
+  return VX_OK;
+}
+
+vx_status check_geom(const vx_geom* g) {
+  VX_CHECK(g, VX_ERR_INVALID_ARG, "geom is NULL");
+  VX_CHECK(g->num_q_heads >= 1 && g->num_kv_heads >= 1, VX_ERR_INVALID_ARG, "heads < 1");
+  VX_CHECK(g->num_q_heads % g->num_kv_heads == 0, VX_ERR_INVALID_ARG,
+           "num_q_heads %d not a multiple of num_kv_heads %d", g->num_q_heads, g->num_kv_heads);
+  VX_CHECK(g->q_dtype == VX_F32 || g->q_dtype == VX_BF16, VX_ERR_INVALID_ARG, "q_dtype");
+  VX_CHECK(g->kv_dtype == VX_F32 || g->kv_dtype == VX_BF16, VX_ERR_INVALID_ARG, "kv_dtype");
+  if (g->mla) {
+    VX_CHECK(g->num_kv_heads == 1, VX_ERR_INVALID_ARG, "MLA has one latent stream (num_kv_heads 1)");
+    VX_CHECK(g->head_dim_k == 576 && g->head_dim_v == 512, VX_ERR_UNSUPPORTED,
+             "MLA geometry %dx%d (supported: 576 key, 512 value)", g->head_dim_k, g->head_dim_v);
+    VX_CHECK(g->q_dtype == VX_BF16 && g->kv_dtype == VX_BF16, VX_ERR_UNSUPPORTED,
+             "MLA needs bf16 q and KV");
+  } else {
+    VX_CHECK(g->head_dim_k == g->head_dim_v, VX_ERR_UNSUPPORTED, "GQA needs head_dim_k == head_dim_v");
+    VX_CHECK(g->head_dim_k == 64 || g->head_dim_k == 128, VX_ERR_UNSUPPORTED,
+             "head_dim %d (supported: 64, 128)", g->head_dim_k);
+    VX_CHECK(g->q_dtype == g->kv_dtype, VX_ERR_UNSUPPORTED, "q and KV dtypes differ");
+    VX_CHECK(g->num_kv_heads * g->head_dim_k <= 2048, VX_ERR_UNSUPPORTED,
+             "num_kv_heads * head_dim > 2048");
+  }
+  return VX_OK;
+}
+
+vx::Meta meta_of(const vx_pages* p) {
+  vx::Meta m;
+  m.batch = p->batch;
+  m.page_size = p->page_size;
+  m.pool = p->num_pool_pages;
+  m.nnz = p->total_pages;
+  m.indptr = p->indptr;
+  m.page_ids = p->page_ids;
+  m.seq_lens = p->seq_lens;
+  return m;
+}
+
+int g_cus[64];  // per-device compute-unit count, 0 = not queried yet
+
+vx_status device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64 && __atomic_load_n(&g_cus[dev], __ATOMIC_ACQUIRE) > 0) {
+    *out = g_cus[dev];
+    return VX_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute");
+  if (dev >= 0 && dev < 64) __atomic_store_n(&g_cus[dev], n, __ATOMIC_RELEASE);
+  *out = n;
+  return VX_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kScorePagesPerWave = 4;
+
+// The planner. Attention work items are (sequence, KV head, split) for GQA
+// and (sequence, split) for MLA. Splits are sized so the launch holds about
+// kWavesPerCU waves per compute unit when the batch alone cannot fill the
+// chip, never more than kMaxPagesPerSplit pages per split.
+vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num_splits,
+                    int num_cus, vx_plan* out) {
+  *out = vx_plan{};
+  out->num_cus = num_cus;
+  const int stride = sel_stride < 1 ? 1 : sel_stride;
+  const long items0 = (long)p->batch * (g->mla ? 1 : g->num_kv_heads);
+  int S;
+  if (num_splits > 0) {
+    S = num_splits;
+  } else {
+    // Enough waves in flight to cover HBM latency: 8 per CU for 16-token
+    // pages; large pages carry more bytes per wave, 4 per CU suffice.
+    const long target = (long)num_cus * (p->page_size >= 64 ? 4 : 8) * (g->mla ? 1 : 1);
+    long s = items0 > 0 ? (target + items0 - 1) / items0 : 1;
+    S = (int)(s < 1 ? 1 : s);
+  }
+  if (S > stride) S = stride;
+  int pps = (stride + S - 1) / S;
+  if (pps > vx::kMaxPagesPerSplit) pps = vx::kMaxPagesPerSplit;
+  S = (stride + pps - 1) / pps;
+  out->num_splits = S;
+  out->pages_per_split = pps;
+  out->score_pages_per_block = 4 * kScorePagesPerWave;
+  out->score_blocks = (p->total_pages + out->score_pages_per_block - 1) / out->score_pages_per_block;
+  const int cap_keys = (p->max_pages + 63) / 64 * 64;
+  int wpb = (int)(65536 / ((size_t)(cap_keys + 256) * 4));
+  out->topk_threads = 64 * (wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb));
+  const int hq = g->num_q_heads, dv = g->head_dim_v;
+  size_t ws = 0;
+  if (S > 1) {
+    ws = align_up((size_t)p->batch * hq * S * dv * sizeof(float), 256);
+    ws += align_up((size_t)p->batch * hq * S * 2 * sizeof(float), 256);
+  }
+  out->workspace_bytes = ws;
+  return VX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vx_abi_version(void) { return 1; }
+
+const char* vx_status_string(vx_status s) {
+  switch (s) {
+    case VX_OK: return "VX_OK";
+    case VX_ERR_INVALID_ARG: return "VX_ERR_INVALID_ARG";
+    case VX_ERR_UNSUPPORTED: return "VX_ERR_UNSUPPORTED";
+    case VX_ERR_WORKSPACE: return "VX_ERR_WORKSPACE";
+    case VX_ERR_HIP: return "VX_ERR_HIP";
+  }
+  return "VX_ERR_UNKNOWN";
+}
+
+const char* vx_last_error(void) { return g_err.c_str(); }
+
+vx_status vx_plan_decode(const vx_pages* pages, const vx_geom* geom, int32_t sel_stride,
+                         int32_t num_splits, int32_t num_cus, vx_plan* plan) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(plan, VX_ERR_INVALID_ARG, "plan is NULL");
+  VX_CHECK(sel_stride >= 1, VX_ERR_INVALID_ARG, "sel_stride < 1");
+  if (num_cus <= 0 && (st = device_cus(&num_cus)) != VX_OK) return st;
+  return make_plan(pages, geom, sel_stride, num_splits, num_cus, plan);
+}
+
+vx_status vx_centroid_update(const vx_pages* pages, const vx_geom* geom, void* k_pool,
+                             void* v_pool, const int32_t* first_token, const void* k_new,
+                             const void* v_new, float* centroids, void* cent_bf16,
+                             hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(pages->total_pages == 0 || k_pool, VX_ERR_INVALID_ARG, "k_pool is NULL");
+  VX_CHECK(centroids, VX_ERR_INVALID_ARG, "centroids is NULL");
+  VX_CHECK(!k_new || first_token, VX_ERR_INVALID_ARG, "k_new needs first_token (append mode)");
+  VX_CHECK(!v_new || (first_token && v_pool && !geom->mla), VX_ERR_INVALID_ARG,
+           "v_new needs first_token and v_pool (and no MLA)");
+  VX_CHECK(!(geom->mla && v_pool), VX_ERR_INVALID_ARG, "MLA has no separate v_pool");
+  if (pages->batch == 0) return VX_OK;
+  const vx::Meta m = meta_of(pages);
+  hipError_t e;
+  if (!first_token)
+    e = vx::launch_centroid_rebuild(m, *geom, k_pool, centroids, (uint16_t*)cent_bf16, stream);
+  else
+    e = vx::launch_centroid_append(m, *geom, k_pool, v_new ? v_pool : nullptr, first_token,
+                                   k_new, v_new, centroids, (uint16_t*)cent_bf16, stream);
+  return hip_status(e, "centroid kernel launch");
+}
+
+vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom, const void* q,
+                         const void* centroids, float score_scale, float* scores,
+                         hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
+  VX_CHECK(pages->total_pages == 0 || (centroids && scores), VX_ERR_INVALID_ARG,
+           "centroids or scores is NULL");
+  VX_CHECK(std::isfinite(score_scale), VX_ERR_INVALID_ARG, "score_scale not finite");
+  if (pages->total_pages == 0) return VX_OK;
+  const vx::Meta m = meta_of(pages);
+  hipError_t e;
+  if (geom->mla)
+    e = vx::launch_scores_mla(m, *geom, q, (const uint16_t*)centroids, score_scale, scores, stream);
+  else
+    e = vx::launch_scores_gqa(m, *geom, q, (const float*)centroids, score_scale, scores,
+                              kScorePagesPerWave, stream);
+  return hip_status(e, "score kernel launch");
+}
+
+vx_status vx_topk_pages(const vx_pages* pages, int32_t num_kv_heads, const float* scores,
+                        int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
+                        const uint32_t* rand_u32, int32_t* sel, int32_t sel_stride,
+                        int32_t* sel_count, hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  VX_CHECK(num_kv_heads >= 1, VX_ERR_INVALID_ARG, "num_kv_heads < 1");
+  VX_CHECK(k >= 0 && n_sink >= 0 && n_local >= 0, VX_ERR_INVALID_ARG,
+           "k, n_sink, n_local must be >= 0");
+  VX_CHECK((long)k + n_sink + n_local <= sel_stride && sel_stride >= 1, VX_ERR_INVALID_ARG,
+           "sel_stride %d < max(1, k + n_sink + n_local)", sel_stride);
+  VX_CHECK(mode == VX_TOPK_EXACT || mode == VX_TOPK_APPROX, VX_ERR_INVALID_ARG, "mode %d", mode);
+  VX_CHECK(mode != VX_TOPK_APPROX || rand_u32, VX_ERR_INVALID_ARG, "approx mode needs rand_u32");
+  VX_CHECK(pages->max_pages <= vx::kMaxTopkPages, VX_ERR_UNSUPPORTED,
+           "max_pages %d > %d", pages->max_pages, vx::kMaxTopkPages);
+  VX_CHECK(pages->batch == 0 || (sel && sel_count), VX_ERR_INVALID_ARG, "sel or sel_count is NULL");
+  VX_CHECK(pages->total_pages == 0 || scores, VX_ERR_INVALID_ARG, "scores is NULL");
+  if (pages->batch == 0) return VX_OK;
+  const vx::Meta m = meta_of(pages);
+  const int cap_keys = (pages->max_pages + 63) / 64 * 64;
+  int wpb = (int)(65536 / ((size_t)(cap_keys + 256) * 4));
+  wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
+  hipError_t e = vx::launch_topk_sized(m, num_kv_heads, scores, k, n_sink, n_local, mode, rand_u32,
+                                       sel, sel_stride, sel_count, pages->max_pages, wpb, stream);
+  return hip_status(e, "top-k kernel launch");
+}
+
+vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const void* q,
+                           const void* k_pool, const void* v_pool, const int32_t* sel,
+                           int32_t sel_stride, const int32_t* sel_count, float sm_scale,
+                           float* out, float* lse, int32_t num_splits, void* workspace,
+                           size_t* workspace_bytes, hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(workspace_bytes, VX_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  VX_CHECK(sel_stride >= 1, VX_ERR_INVALID_ARG, "sel_stride < 1");
+  VX_CHECK(std::isfinite(sm_scale), VX_ERR_INVALID_ARG, "sm_scale not finite");
+  if (!geom->mla) {
+    const int G = geom->num_q_heads / geom->num_kv_heads;
+    VX_CHECK(G == 1 || G == 2 || G == 4 || G == 8, VX_ERR_UNSUPPORTED,
+             "GQA group %d (supported: 1, 2, 4, 8)", G);
+  } else {
+    VX_CHECK(geom->num_q_heads == 32 || geom->num_q_heads == 16, VX_ERR_UNSUPPORTED,
+             "MLA query heads %d (supported: 16, 32)", geom->num_q_heads);
+    VX_CHECK(pages->page_size == 64, VX_ERR_UNSUPPORTED, "MLA needs page_size 64");
+  }
+  if (workspace) {
+    VX_CHECK(pages->batch == 0 || (q && k_pool && sel && sel_count && out), VX_ERR_INVALID_ARG,
+             "q, k_pool, sel, sel_count or out is NULL");
+    VX_CHECK(geom->mla || pages->batch == 0 || v_pool, VX_ERR_INVALID_ARG, "v_pool is NULL");
+  }
+  int cus = 0;
+  if ((st = device_cus(&cus)) != VX_OK) return st;
+  vx_plan plan;
+  if ((st = make_plan(pages, geom, sel_stride, num_splits, cus, &plan)) != VX_OK) return st;
+  if (!workspace) {
+    *workspace_bytes = plan.workspace_bytes;
+    return VX_OK;
+  }
+  VX_CHECK(*workspace_bytes >= plan.workspace_bytes, VX_ERR_WORKSPACE,
+           "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
+  VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
+  if (pages->batch == 0) return VX_OK;
+  const vx::Meta m = meta_of(pages);
+  const int S = plan.num_splits;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (S > 1) {
+    part_o = (float*)workspace;
+    part_ml = (float*)((char*)workspace +
+                       align_up((size_t)pages->batch * geom->num_q_heads * S * geom->head_dim_v *
+                                    sizeof(float),
+                                256));
+  }
+  hipError_t e;
+  if (geom->mla)
+    e = vx::launch_attention_mla(m, *geom, q, k_pool, sel, sel_stride, sel_count, sm_scale, S,
+                                 plan.pages_per_split, out, lse, part_o, part_ml, stream);
+  else
+    e = vx::launch_attention_gqa(m, *geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                                 S, plan.pages_per_split, out, lse, part_o, part_ml, stream);
+  if (e != hipSuccess) return hip_status(e, "attention kernel launch");
+  if (S > 1) {
+    e = vx::launch_merge(pages->batch, geom->num_q_heads, geom->head_dim_v, S, part_o, part_ml, out,
+                         lse, stream);
+    if (e != hipSuccess) return hip_status(e, "merge kernel launch");
+  }
+  return VX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+// Nothing here is part of the public ABI (include/vx.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vx.h"
+
+namespace vx {
+
+// Launch-side copy of the paged metadata (passed to kernels by value).
+struct Meta {
+  int32_t batch;
+  int32_t page_size;
+  int32_t pool;
+  int32_t nnz;
+  const int32_t* indptr;
+  const int32_t* page_ids;
+  const int32_t* seq_lens;
+};
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIP_DEVICE_COMPILE__)
+#define VX_DEV __device__ __forceinline__
+#else
+#define VX_DEV __device__ inline
+#endif
+
+VX_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+VX_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+VX_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs; NaN stays NaN).
+VX_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Sequence owning page-table entry j: largest b with indptr[b] <= j.
+VX_DEV int find_seq(const int32_t* __restrict__ indptr, int batch, int j) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (indptr[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Valid tokens of sequence b, clamped to its page-table capacity.
+VX_DEV int seq_len_clamped(const Meta& m, int b) {
+  int cap = (m.indptr[b + 1] - m.indptr[b]) * m.page_size;
+  int L = m.seq_lens[b];
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+VX_DEV int phys_page(const Meta& m, int j) {
+  int p = m.page_ids[j];
+  return p < 0 ? 0 : (p >= m.pool ? m.pool - 1 : p);
+}
+
+// DPP lane moves inside rows of 16 lanes.
+template <int CTRL>
+VX_DEV float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROR4 = 0x124;  // row_ror:4
+constexpr int DPP_ROR8 = 0x128;  // row_ror:8
+
+// Sum over aligned groups of W lanes; every lane of the group gets the sum.
+template <int W>
+VX_DEV float group_sum(float x) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "W");
+  if constexpr (W >= 2) x += dpp<DPP_XOR1>(x);
+  if constexpr (W >= 4) x += dpp<DPP_XOR2>(x);
+  if constexpr (W == 8) x += __shfl_xor(x, 4);
+  if constexpr (W >= 16) { x += dpp<DPP_ROR4>(x); x += dpp<DPP_ROR8>(x); }
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int W>
+VX_DEV float group_max(float x) {
+  if constexpr (W >= 2) x = fmaxf(x, dpp<DPP_XOR1>(x));
+  if constexpr (W >= 4) x = fmaxf(x, dpp<DPP_XOR2>(x));
+  if constexpr (W == 8) x = fmaxf(x, __shfl_xor(x, 4));
+  if constexpr (W >= 16) { x = fmaxf(x, dpp<DPP_ROR4>(x)); x = fmaxf(x, dpp<DPP_ROR8>(x)); }
+  if constexpr (W >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (W >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error. Shapes are validated by the
+// caller (vx_capi.hip) before these run.
+
+hipError_t launch_centroid_rebuild(const Meta& m, const vx_geom& g, const void* k_pool,
+                                   float* cent, uint16_t* cent_bf16, hipStream_t s);
+hipError_t launch_centroid_append(const Meta& m, const vx_geom& g, void* k_pool, void* v_pool,
+                                  const int32_t* first_token, const void* k_new,
+                                  const void* v_new, float* cent, uint16_t* cent_bf16,
+                                  hipStream_t s);
+hipError_t launch_scores_gqa(const Meta& m, const vx_geom& g, const void* q, const float* cent,
+                             float scale, float* scores, int pages_per_wave, hipStream_t s);
+hipError_t launch_scores_mla(const Meta& m, const vx_geom& g, const void* q,
+                             const uint16_t* cent_bf16, float scale, float* scores,
+                             hipStream_t s);
+hipError_t launch_topk_sized(const Meta& m, int hkv, const float* scores, int k, int n_sink,
+                             int n_local, int mode, const uint32_t* rand_u32, int32_t* sel,
+                             int sel_stride, int32_t* sel_count, int max_pages,
+                             int waves_per_block, hipStream_t s);
+hipError_t launch_attention_gqa(const Meta& m, const vx_geom& g, const void* q,
+                                const void* k_pool, const void* v_pool, const int32_t* sel,
+                                int sel_stride, const int32_t* sel_count, float sm_scale,
+                                int num_splits, int pages_per_split, float* out, float* lse,
+                                float* part_o, float* part_ml, hipStream_t s);
+hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
+                                const void* k_pool, const int32_t* sel, int sel_stride,
+                                const int32_t* sel_count, float sm_scale, int num_splits,
+                                int pages_per_split, float* out, float* lse, float* part_o,
+                                float* part_ml, hipStream_t s);
+hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* part_o,
+                        const float* part_ml, float* out, float* lse, hipStream_t s);
+
+// Largest selection one split may stream (lane-distributed page list).
+constexpr int kMaxPagesPerSplit = 64;
+// Largest per-sequence page count the top-k supports (LDS resident keys).
+constexpr int kMaxTopkPages = 16000;
+
+}  // namespace vx

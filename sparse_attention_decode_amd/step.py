@@ -1,0 +1,94 @@
+"""One block top-k sparse-attention decode step on the GPU.
+
+Owns the device buffers of a workload (centroid cache, scores, selection,
+outputs, workspace) and issues the library's calls in the step's order:
+cache stage (refresh of the newest token's page), scoring, selection,
+attention. Python only marshals arguments; every stage is a gfx950 kernel.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as V
+from .workloads import Workload
+
+__all__ = ["DecodeStep"]
+
+
+class DecodeStep:
+    def __init__(self, w: Workload, mode: int = V.VX_TOPK_EXACT, num_splits: int = 0,
+                 k: Optional[int] = None, n_sink: Optional[int] = None,
+                 n_local: Optional[int] = None, with_lse: bool = True):
+        s = w.spec
+        dev = w.device
+        self.w = w
+        self.mode = mode
+        self.num_splits = num_splits
+        self.k = s.topk if k is None else k
+        self.n_sink = s.n_sink if n_sink is None else n_sink
+        self.n_local = s.n_local if n_local is None else n_local
+        self.k_out = max(1, self.k + self.n_sink + self.n_local)
+        self.score_scale, self.sm_scale = s.scales()
+        self.pages = V.make_pages(s.batch, s.page_size, w.pool_pages, w.nnz, w.max_pages,
+                                  w.d_indptr, w.d_page_ids, w.d_seq_lens)
+        self.geom = V.make_geom(s.num_q_heads, s.num_kv_heads, s.head_dim_k, s.head_dim_v,
+                                s.mla, w.q.dtype, w.k_pool.dtype)
+        H = s.num_kv_heads
+        self.centroids = torch.zeros((w.pool_pages, H, s.head_dim_k), dtype=torch.float32,
+                                     device=dev)
+        self.cent_bf16 = (torch.zeros((w.pool_pages, H, s.head_dim_k), dtype=torch.bfloat16,
+                                      device=dev) if s.mla else None)
+        self.scores = torch.zeros((H, max(1, w.nnz)), dtype=torch.float32, device=dev)
+        self.sel = torch.full((s.batch, H, self.k_out), -1, dtype=torch.int32, device=dev)
+        self.sel_count = torch.zeros((s.batch, H), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((s.batch, s.num_q_heads, s.head_dim_v), dtype=torch.float32,
+                               device=dev)
+        self.lse = (torch.zeros((s.batch, s.num_q_heads), dtype=torch.float32, device=dev)
+                    if with_lse else None)
+        # -1: refresh the page holding each sequence's newest token
+        self.newest = torch.full((s.batch,), -1, dtype=torch.int32, device=dev)
+        nbytes = V.vx_sparse_decode(self.pages, self.geom, None, None, None, None, self.k_out,
+                                    None, self.sm_scale, None, None, num_splits)
+        self.workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
+        self.workspace_bytes = nbytes
+
+    # -- stages ---------------------------------------------------------
+    def rebuild_centroids(self, stream=None) -> None:
+        w = self.w
+        V.vx_centroid_update(self.pages, self.geom, w.k_pool, None, None, None, None,
+                             self.centroids, self.cent_bf16, stream)
+
+    def refresh_centroids(self, first_token=None, k_new=None, v_new=None, stream=None) -> None:
+        w = self.w
+        ft = self.newest if first_token is None else first_token
+        V.vx_centroid_update(self.pages, self.geom, w.k_pool, w.v_pool if v_new is not None else None,
+                             ft, k_new, v_new, self.centroids, self.cent_bf16, stream)
+
+    def score(self, stream=None) -> None:
+        cent = self.cent_bf16 if self.w.spec.mla else self.centroids
+        V.vx_page_scores(self.pages, self.geom, self.w.q, cent, self.score_scale, self.scores,
+                         stream)
+
+    def select(self, scores=None, stream=None) -> None:
+        V.vx_topk_pages(self.pages, self.w.spec.num_kv_heads,
+                        self.scores if scores is None else scores, self.k, self.n_sink,
+                        self.n_local, self.mode, self.w.d_rand_u32, self.sel, self.k_out,
+                        self.sel_count, stream)
+
+    def attend(self, sel=None, sel_count=None, stream=None) -> None:
+        w = self.w
+        V.vx_sparse_decode(self.pages, self.geom, w.q, w.k_pool, w.v_pool,
+                           self.sel if sel is None else sel, self.k_out,
+                           self.sel_count if sel_count is None else sel_count, self.sm_scale,
+                           self.out, self.lse, self.num_splits, self.workspace,
+                           self.workspace_bytes, stream)
+
+    def run(self, stream=None) -> None:
+        """The whole step: cache refresh, scoring, selection, attention."""
+        self.refresh_centroids(stream=stream)
+        self.score(stream)
+        self.select(stream=stream)
+        self.attend(stream=stream)

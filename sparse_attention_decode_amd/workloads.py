@@ -66,6 +66,7 @@ class Spec:
     head_dim_v: int
     page_size: int
     # ("fixed", L) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
+    # | ("list", (L_0, ..., L_{B-1}))
     lengths: tuple
     # ("fixed", pages) | ("factor", f)
     pool: tuple
@@ -224,6 +225,11 @@ class Workload:
 
 def _lengths(s: Spec, rng: np.random.Generator) -> np.ndarray:
     kind = s.lengths[0]
+    if kind == "list":
+        lens = np.asarray(s.lengths[1], dtype=np.int64)
+        if lens.shape != (s.batch,):
+            raise ValueError("length list does not match the batch")
+        return lens
     if kind == "fixed":
         return np.full(s.batch, s.lengths[1], dtype=np.int64)
     if kind == "uniform":

@@ -1,0 +1,147 @@
+"""Host-side checks of libvx.so: it loads, exports every symbol include/vx.h
+declares, rejects bad arguments before any HIP call, and plans launches.
+No GPU is needed: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_decode_amd import binding as V
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BAD = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "vx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = V.load()
+    names = header_functions()
+    assert set(V.ENTRY_POINTS) <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.vx_abi_version() == 1
+
+
+def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
+    p = BAD if ptrs else None
+    return V.make_pages(batch, page_size, pool, nnz, maxp, p, p, p)
+
+
+def geom(hq=16, hkv=8, dk=128, dv=128, mla=0, qd=V.VX_BF16, kvd=V.VX_BF16):
+    return V.make_geom(hq, hkv, dk, dv, mla, qd, kvd)
+
+
+def status_of(fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+    except V.VxError as e:
+        return e.status
+    return V.VX_OK
+
+
+def test_status_strings():
+    assert V.status_string(0) == "VX_OK"
+    assert V.status_string(3) == "VX_ERR_WORKSPACE"
+    assert V.status_string(99) == "VX_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=32), V.VX_ERR_UNSUPPORTED),
+    (dict(batch=-1), V.VX_ERR_INVALID_ARG),
+    (dict(maxp=9), V.VX_ERR_INVALID_ARG),
+    (dict(ptrs=False), V.VX_ERR_INVALID_ARG),
+    (dict(pool=0), V.VX_ERR_INVALID_ARG),
+])
+def test_bad_pages_rejected(kw, status):
+    assert status_of(V.vx_page_scores, pages(**kw), geom(), BAD, BAD, 1.0, BAD, stream=0) == status
+    assert status_of(V.vx_centroid_update, pages(**kw), geom(), BAD, None, None, None, None, BAD,
+                     None, stream=0) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=12, hkv=8), V.VX_ERR_INVALID_ARG),
+    (dict(dk=96, dv=96), V.VX_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), V.VX_ERR_UNSUPPORTED),
+    (dict(qd=V.VX_F32), V.VX_ERR_UNSUPPORTED),
+    (dict(hkv=2, mla=1, dk=576, dv=512, hq=32), V.VX_ERR_INVALID_ARG),
+    (dict(hkv=1, mla=1, dk=512, dv=512, hq=32), V.VX_ERR_UNSUPPORTED),
+    (dict(hkv=32, hq=32, dk=128, dv=128), V.VX_ERR_UNSUPPORTED),  # 32*128 > 2048
+])
+def test_bad_geometry_rejected(kw, status):
+    assert status_of(V.vx_page_scores, pages(), geom(**kw), BAD, BAD, 1.0, BAD, stream=0) == status
+
+
+def test_topk_argument_checks():
+    p = pages()
+    ok = dict(k=4, n_sink=1, n_local=1, mode=0, rand_u32=None, sel=BAD, sel_stride=6, sel_count=BAD)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return status_of(V.vx_topk_pages, p, 8, BAD, a["k"], a["n_sink"], a["n_local"], a["mode"],
+                         a["rand_u32"], a["sel"], a["sel_stride"], a["sel_count"], stream=0)
+
+    assert call(sel_stride=5) == V.VX_ERR_INVALID_ARG
+    assert call(k=-1) == V.VX_ERR_INVALID_ARG
+    assert call(mode=2) == V.VX_ERR_INVALID_ARG
+    assert call(mode=1) == V.VX_ERR_INVALID_ARG  # approx without random words
+    assert call(sel=None) == V.VX_ERR_INVALID_ARG
+    big = V.make_pages(1, 16, 20000, 17000, 17000, BAD, BAD, BAD)
+    assert status_of(V.vx_topk_pages, big, 1, BAD, 4, 0, 0, 0, None, BAD, 4, BAD,
+                     stream=0) == V.VX_ERR_UNSUPPORTED
+
+
+def test_centroid_argument_checks():
+    p, g = pages(), geom()
+    # k_new needs the append mode
+    assert status_of(V.vx_centroid_update, p, g, BAD, None, None, BAD, None, BAD, None,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    # v_new needs v_pool
+    assert status_of(V.vx_centroid_update, p, g, BAD, None, BAD, BAD, BAD, BAD, None,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_centroid_update, p, g, BAD, None, None, None, None, None, None,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+
+
+def test_decode_argument_checks():
+    p = pages()
+    # group of 3 query heads per KV head is not a supported attention geometry
+    assert status_of(V.vx_sparse_decode, p, geom(hq=24, hkv=8), BAD, BAD, BAD, BAD, 4, BAD, 1.0,
+                     BAD, None, 0, BAD, 1 << 20, stream=0) == V.VX_ERR_UNSUPPORTED
+    assert status_of(V.vx_sparse_decode, p, geom(), BAD, BAD, BAD, BAD, 0, BAD, 1.0,
+                     BAD, None, 0, BAD, 1 << 20, stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_sparse_decode, p, geom(), BAD, BAD, BAD, BAD, 4, BAD, float("nan"),
+                     BAD, None, 0, BAD, 1 << 20, stream=0) == V.VX_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    p = V.make_pages(0, 16, 0, 0, 0, None, None, None)
+    V.vx_page_scores(p, geom(), None, None, 1.0, None, stream=0)
+    V.vx_topk_pages(p, 8, None, 4, 1, 1, 0, None, None, 6, None, stream=0)
+    V.vx_centroid_update(p, geom(), None, None, None, None, None, BAD, None, stream=0)
+
+
+def test_planner_splits_and_workspace():
+    g = geom()
+    # 32 sequences x 8 KV heads, 18 selected pages, 256 CUs: 8 waves per CU
+    plan = V.vx_plan_decode(pages(batch=32, nnz=6144, pool=7680, maxp=256), g, 18, 0, 256)
+    S, pps = plan["num_splits"], plan["pages_per_split"]
+    assert pps == -(-18 // S) and S * pps >= 18 and (S - 1) * pps < 18
+    assert 32 * 8 * S >= 256 * 4
+    assert plan["workspace_bytes"] >= 32 * 16 * S * (128 + 2) * 4
+    # a batch that already fills the chip is not split
+    plan = V.vx_plan_decode(pages(batch=256, nnz=90000, pool=100000, maxp=1024, page_size=64),
+                            g.__class__(64, 8, 128, 128, 0, 1, 1), 64, 0, 256)
+    assert plan["num_splits"] == 1 and plan["workspace_bytes"] == 0
+    # an explicit split count is honoured up to the rounding of pages per split
+    plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 7, 256)
+    assert plan["pages_per_split"] == 3 and plan["num_splits"] == 6
+    # no split streams more than 64 pages
+    plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=200), g, 131, 1, 256)
+    assert plan["pages_per_split"] <= 64 and plan["num_splits"] == 3

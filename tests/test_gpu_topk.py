@@ -1,0 +1,104 @@
+"""GPU radix top-k against the oracle on identical fp32 scores (bit-exact).
+
+Scores are fed to the kernel directly, so both sides rank the same fp32
+values: the exact mode must return exactly the oracle's pages, and the
+approximate mode exactly the oracle's reading of it (same remap, same
+boundary bucket, same random window).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import vx_oracle as O
+from sparse_attention_decode_amd import binding as V
+
+pytestmark = pytest.mark.gpu
+
+P = 16
+
+
+def segments(seed, batch, hkv, max_n):
+    rng = np.random.default_rng(seed)
+    ns = rng.integers(1, max_n + 1, size=batch)
+    ns[0] = 1
+    if batch > 2:
+        ns[1] = max_n
+    scores = []
+    for b in range(batch):
+        for g in range(hkv):
+            kind = (b * hkv + g) % 5
+            n = ns[b]
+            if kind == 0:
+                s = rng.standard_normal(n)
+            elif kind == 1:
+                s = rng.integers(-3, 4, size=n).astype(np.float64)  # heavy ties
+            elif kind == 2:
+                s = np.zeros(n)
+                s[rng.random(n) < 0.5] = -0.0
+            elif kind == 3:
+                s = rng.standard_normal(n) * 1e-30  # tiny magnitudes, denormal-free
+            else:
+                s = np.round(rng.standard_normal(n), 2) * 1000.0
+            scores.append(s.astype(np.float32))
+    return ns, scores
+
+
+def run_topk(ns, scores, hkv, k, n_sink, n_local, mode, rnd):
+    batch = len(ns)
+    indptr = np.zeros(batch + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(ns)
+    nnz = int(indptr[-1])
+    sc = np.zeros((hkv, nnz), dtype=np.float32)
+    for b in range(batch):
+        for g in range(hkv):
+            sc[g, indptr[b]:indptr[b + 1]] = scores[b * hkv + g]
+    dev = torch.device("cuda")
+    d_indptr = torch.from_numpy(indptr).to(dev)
+    d_lens = torch.from_numpy((ns * P).astype(np.int32)).to(dev)
+    d_ids = torch.arange(nnz, dtype=torch.int32, device=dev)
+    pages = V.make_pages(batch, P, nnz, nnz, int(ns.max()), d_indptr, d_ids, d_lens)
+    stride = max(1, k + n_sink + n_local)
+    sel = torch.full((batch, hkv, stride), -7, dtype=torch.int32, device=dev)
+    cnt = torch.zeros((batch, hkv), dtype=torch.int32, device=dev)
+    d_sc = torch.from_numpy(sc).to(dev)
+    d_rnd = torch.from_numpy(rnd.view(np.int32)).to(dev)
+    V.vx_topk_pages(pages, hkv, d_sc, k, n_sink, n_local, mode, d_rnd, sel, stride, cnt)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("k,n_sink,n_local", [(16, 1, 1), (8, 0, 1), (128, 1, 2), (64, 0, 0),
+                                              (0, 1, 1), (1, 0, 0), (5, 3, 3)])
+@pytest.mark.parametrize("mode", [V.VX_TOPK_EXACT, V.VX_TOPK_APPROX])
+def test_topk_bit_exact(k, n_sink, n_local, mode):
+    hkv, batch = 3, 9
+    ns, scores = segments(1000 + k, batch, hkv, max_n=2100)
+    rnd = np.random.default_rng(k).integers(0, 2**32, size=(batch, hkv), dtype=np.uint64).astype(np.uint32)
+    sel, cnt = run_topk(ns, scores, hkv, k, n_sink, n_local, mode, rnd)
+    for b in range(batch):
+        for g in range(hkv):
+            s = scores[b * hkv + g]
+            if mode == V.VX_TOPK_EXACT:
+                want = O.topk_exact(s.astype(np.float64), k, n_sink, n_local)
+            else:
+                want = O.topk_approx(s, k, n_sink, n_local, int(rnd[b, g]))
+            stride = max(1, k + n_sink + n_local)
+            full = np.full(stride, -1)
+            full[:len(want)] = want
+            np.testing.assert_array_equal(sel[b, g], full, err_msg=f"b={b} g={g} n={ns[b]}")
+            assert cnt[b, g] == int((want >= 0).sum())
+
+
+def test_topk_large_segments_one_wave_per_block():
+    """Segments past the 4-waves-per-block LDS budget (max_pages > ~3800)."""
+    hkv, batch = 2, 3
+    rng = np.random.default_rng(5)
+    ns = np.array([5000, 3, 4100])
+    scores = [rng.standard_normal(ns[b]).astype(np.float32) for b in range(batch) for _ in range(hkv)]
+    rnd = np.zeros((batch, hkv), dtype=np.uint32)
+    sel, cnt = run_topk(ns, scores, hkv, 64, 1, 1, V.VX_TOPK_EXACT, rnd)
+    for b in range(batch):
+        for g in range(hkv):
+            want = O.topk_exact(scores[b * hkv + g].astype(np.float64), 64, 1, 1)
+            np.testing.assert_array_equal(sel[b, g][:len(want)], want)
