@@ -59,6 +59,8 @@ vx_status check_geom(const vx_geom* g) {
   VX_CHECK(g->kv_dtype == VX_F32 || g->kv_dtype == VX_BF16, VX_ERR_INVALID_ARG, "kv_dtype");
   if (g->mla) {
     VX_CHECK(g->num_kv_heads == 1, VX_ERR_INVALID_ARG, "MLA has one latent stream (num_kv_heads 1)");
+    VX_CHECK(g->num_q_heads == 16 || g->num_q_heads == 32, VX_ERR_UNSUPPORTED,
+             "MLA query heads %d (supported: 16, 32)", g->num_q_heads);
     VX_CHECK(g->head_dim_k == 576 && g->head_dim_v == 512, VX_ERR_UNSUPPORTED,
              "MLA geometry %dx%d (supported: 576 key, 512 value)", g->head_dim_k, g->head_dim_v);
     VX_CHECK(g->q_dtype == VX_BF16 && g->kv_dtype == VX_BF16, VX_ERR_UNSUPPORTED,
@@ -124,7 +126,8 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   } else {
     // Enough waves in flight to cover HBM latency: 8 per CU for 16-token
     // pages; large pages carry more bytes per wave, 4 per CU suffice.
-    const long target = (long)num_cus * (p->page_size >= 64 ? 4 : 8) * (g->mla ? 1 : 1);
+    // GQA items are single waves; MLA items are 4-wave blocks.
+    const long target = g->mla ? (long)num_cus * 2 : (long)num_cus * (p->page_size >= 64 ? 4 : 8);
     long s = items0 > 0 ? (target + items0 - 1) / items0 : 1;
     S = (int)(s < 1 ? 1 : s);
   }
@@ -217,7 +220,8 @@ vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom, const void*
   const vx::Meta m = meta_of(pages);
   hipError_t e;
   if (geom->mla)
-    e = vx::launch_scores_mla(m, *geom, q, (const uint16_t*)centroids, score_scale, scores, stream);
+    e = vx::launch_scores_mla_sized(m, *geom, q, (const uint16_t*)centroids, score_scale, scores,
+                                    pages->max_pages, stream);
   else
     e = vx::launch_scores_gqa(m, *geom, q, (const float*)centroids, score_scale, scores,
                               kScorePagesPerWave, stream);
@@ -267,9 +271,7 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const voi
     VX_CHECK(G == 1 || G == 2 || G == 4 || G == 8, VX_ERR_UNSUPPORTED,
              "GQA group %d (supported: 1, 2, 4, 8)", G);
   } else {
-    VX_CHECK(geom->num_q_heads == 32 || geom->num_q_heads == 16, VX_ERR_UNSUPPORTED,
-             "MLA query heads %d (supported: 16, 32)", geom->num_q_heads);
-    VX_CHECK(pages->page_size == 64, VX_ERR_UNSUPPORTED, "MLA needs page_size 64");
+    VX_CHECK(pages->page_size == 64, VX_ERR_UNSUPPORTED, "MLA attention needs page_size 64");
   }
   if (workspace) {
     VX_CHECK(pages->batch == 0 || (q && k_pool && sel && sel_count && out), VX_ERR_INVALID_ARG,

@@ -107,9 +107,9 @@ hipError_t launch_centroid_append(const Meta& m, const vx_geom& g, void* k_pool,
                                   hipStream_t s);
 hipError_t launch_scores_gqa(const Meta& m, const vx_geom& g, const void* q, const float* cent,
                              float scale, float* scores, int pages_per_wave, hipStream_t s);
-hipError_t launch_scores_mla(const Meta& m, const vx_geom& g, const void* q,
-                             const uint16_t* cent_bf16, float scale, float* scores,
-                             hipStream_t s);
+hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,
+                                   const uint16_t* cent_bf16, float scale, float* scores,
+                                   int max_pages, hipStream_t s);
 hipError_t launch_topk_sized(const Meta& m, int hkv, const float* scores, int k, int n_sink,
                              int n_local, int mode, const uint32_t* rand_u32, int32_t* sel,
                              int sel_stride, int32_t* sel_count, int max_pages,

@@ -25,7 +25,7 @@ def on_gpu(w: W.Workload) -> W.Workload:
 EDGE_LENS = (1, 16, 17, 33, 48, 160, 300, 1)
 
 
-@pytest.mark.parametrize("base", ["gqa_bf16", "tiny_fp32", "largebatch_bf16"])
+@pytest.mark.parametrize("base", ["gqa_bf16", "tiny_fp32", "largebatch_bf16", "mla_bf16"])
 def test_short_and_partial_sequences(base):
     """seq_len 1, exact page multiples, one token into a new page, fewer
     pages than k + forced (everything selected)."""
@@ -56,8 +56,10 @@ def test_zero_query_selects_lowest_indices():
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
-def test_split_count_invariance(splits):
-    sp = W.spec("longgen_bf16", batch=3, lengths=("uniform", 2500, 3000), headroom_tokens=0)
+@pytest.mark.parametrize("base", ["longgen_bf16", "mla_bf16"])
+def test_split_count_invariance(base, splits):
+    lens = ("uniform", 2500, 3000) if base == "longgen_bf16" else ("uniform", 4000, 5000)
+    sp = W.spec(base, batch=3, lengths=lens, headroom_tokens=0)
     w = on_gpu(W.make(sp, "cpu", seed=6))
     pipeline_check(w, range(3), DecodeStep(w, num_splits=splits))
 

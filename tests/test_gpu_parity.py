@@ -25,6 +25,7 @@ SMALL = {
                             headroom_tokens=40),
     "large_small": W.spec("largebatch_bf16", batch=6,
                           lengths=("lognormal", 4000, math.log(2.0), 1000, 16000)),
+    "mla_small": W.spec("mla_bf16", batch=4, lengths=("uniform", 2000, 6000)),
 }
 
 
@@ -77,6 +78,7 @@ def test_small_workloads_every_sequence(name):
     ("gqa_bf16", list(range(32))),
     ("longgen_bf16", [0, 17, 63]),
     ("largebatch_bf16", [0, 100, 255]),
+    ("mla_bf16", [0, 13, 31]),
 ])
 def test_full_size_workloads_sampled(name, sample):
     w = W.make(W.spec(name), "cuda", seed=0)
