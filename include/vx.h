@@ -7,6 +7,7 @@
  *   cache stage    per-page key centroid, query independent  -> vx_centroid_update
  *   indexer        query x centroid scores                    -> vx_page_scores
  *                  top-k pages per (sequence, KV head)        -> vx_topk_pages
+ *                  both, fused with the newest-page refresh   -> vx_index_pages
  *   attention      exact softmax over the selected pages      -> vx_sparse_decode
  * Section "System design > 2. vTensor" gives the paged layout (a tensor with
  * batch size, a pointer array and a page-index structure): vx_pages below.
@@ -25,10 +26,11 @@
  *     launched then. A failed launch returns VX_ERR_HIP. vx_last_error()
  *     returns a thread-local message for the last failure.
  *   - Device-side contract (not checked on the host, which never reads device
- *     memory): 1 <= seq_lens[b] <= (indptr[b+1]-indptr[b]) * page_size and
- *     0 <= page_ids[j] < num_pool_pages. Kernels clamp both so that no access
- *     leaves its buffer; results for a sequence that breaks them are
- *     unspecified.
+ *     memory): 0 <= seq_lens[b] <= (indptr[b+1]-indptr[b]) * page_size and
+ *     0 <= page_ids[j] < num_pool_pages. A sequence with seq_lens[b] = 0 is
+ *     an idle slot: no page scored, an empty selection, out = 0 and
+ *     lse = -inf. Kernels clamp both so that no access leaves its buffer;
+ *     results for a sequence that breaks them are unspecified.
  *   - Entry points are reentrant; the only library state is a per-device
  *     cache of the compute-unit count.
  *
@@ -173,6 +175,31 @@ vx_status vx_topk_pages(const vx_pages* pages, int32_t num_kv_heads,
                         int32_t n_local, int32_t mode, const uint32_t* rand_u32,
                         int32_t* sel, int32_t sel_stride, int32_t* sel_count,
                         hipStream_t stream);
+
+/* Indexer, fused (Vortex paper note, "System design > 3. Execution backend":
+ * sequence-local operators are fused). One call runs
+ *   1. refresh_newest = 1: the cache-stage refresh of the page holding each
+ *      sequence's newest token (exactly vx_centroid_update with
+ *      first_token[b] = -1 and no k_new: centroids, and cent_bf16 when given,
+ *      are rewritten for that page);
+ *   2. the scores of vx_page_scores (GQA reads `centroids`, MLA `cent_bf16`);
+ *   3. the selection of vx_topk_pages over those scores;
+ * and writes the same bits as those three calls in that order. For GQA it
+ * is one kernel with a block per (sequence, KV head): the block streams that
+ * head's slice of the sequence's centroid rows, keeps the scores as keys in
+ * LDS and selects from them, so no block waits for another. MLA runs the
+ * three steps as consecutive kernels.
+ * With refresh_newest = 1, no physical page that is some sequence's newest
+ * page may appear in another sequence's page table in the same call. */
+vx_status vx_index_pages(const vx_pages* pages, const vx_geom* geom,
+                         const void* q, const void* k_pool,
+                         float* centroids, void* cent_bf16,
+                         int32_t refresh_newest, float score_scale,
+                         float* scores, int32_t k, int32_t n_sink,
+                         int32_t n_local, int32_t mode,
+                         const uint32_t* rand_u32, int32_t* sel,
+                         int32_t sel_stride, int32_t* sel_count,
+                         hipStream_t stream);
 
 /* Sparse attention (Vortex paper note, "System design > 1. vFlow": exact
  * softmax attention on the selected blocks). For query head h of sequence b

@@ -16,16 +16,16 @@ import torch
 
 __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
-    "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_sparse_decode",
-    "vx_plan_decode", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
+    "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
+    "vx_sparse_decode", "vx_plan_decode", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
 
 VX_OK, VX_ERR_INVALID_ARG, VX_ERR_UNSUPPORTED, VX_ERR_WORKSPACE, VX_ERR_HIP = range(5)
 VX_F32, VX_BF16 = 0, 1
 VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
-ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_sparse_decode",
-                "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
+ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
+                "vx_sparse_decode", "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
 
@@ -77,12 +77,15 @@ def load() -> ctypes.CDLL:
     lib.vx_page_scores.argtypes = [P, G, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     lib.vx_topk_pages.argtypes = [P, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                   c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
+    lib.vx_index_pages.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                   c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                   c_void_p, c_int32, c_void_p, c_void_p]
     lib.vx_sparse_decode.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                      c_void_p, c_float, c_void_p, c_void_p, c_int32, c_void_p,
                                      POINTER(c_size_t), c_void_p]
     lib.vx_plan_decode.argtypes = [P, G, c_int32, c_int32, c_int32, POINTER(VxPlan)]
-    for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_sparse_decode",
-                 "vx_plan_decode"):
+    for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
+                 "vx_sparse_decode", "vx_plan_decode"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -155,13 +158,29 @@ def vx_topk_pages(pages: VxPages, num_kv_heads: int, scores, k: int, n_sink: int
                                 _ptr(sel_count), _stream(stream)))
 
 
+def _nbytes(workspace, workspace_bytes) -> c_size_t:
+    if workspace is not None and workspace_bytes is None:
+        return c_size_t(workspace.numel() * workspace.element_size())
+    return c_size_t(0 if workspace_bytes is None else workspace_bytes)
+
+
+def vx_index_pages(pages: VxPages, geom: VxGeom, q, k_pool, centroids, cent_bf16,
+                   refresh_newest: bool, score_scale: float, scores, k: int, n_sink: int,
+                   n_local: int, mode: int, rand_u32, sel, sel_stride: int, sel_count,
+                   stream=None) -> None:
+    """Newest-page refresh (optional) + scores + top-k."""
+    _check(load().vx_index_pages(ctypes.byref(pages), ctypes.byref(geom), _ptr(q), _ptr(k_pool),
+                                 _ptr(centroids), _ptr(cent_bf16), int(refresh_newest),
+                                 float(score_scale), _ptr(scores), k, n_sink, n_local, mode,
+                                 _ptr(rand_u32), _ptr(sel), sel_stride, _ptr(sel_count),
+                                 _stream(stream)))
+
+
 def vx_sparse_decode(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, sel, sel_stride: int,
                      sel_count, sm_scale: float, out, lse, num_splits: int = 0, workspace=None,
                      workspace_bytes: Optional[int] = None, stream=None) -> int:
     """Runs the attention; with workspace=None only returns the bytes needed."""
-    nbytes = c_size_t(0 if workspace_bytes is None else workspace_bytes)
-    if workspace is not None and workspace_bytes is None:
-        nbytes = c_size_t(workspace.numel() * workspace.element_size())
+    nbytes = _nbytes(workspace, workspace_bytes)
     _check(load().vx_sparse_decode(ctypes.byref(pages), ctypes.byref(geom), _ptr(q), _ptr(k_pool),
                                    _ptr(v_pool), _ptr(sel), sel_stride, _ptr(sel_count),
                                    float(sm_scale), _ptr(out), _ptr(lse), num_splits,

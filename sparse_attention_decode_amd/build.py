@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvx.so")
-SOURCES = ["vx_capi.hip", "centroid.hip", "scores.hip", "topk.hip", "attention.hip", "mla.hip"]
+SOURCES = ["vx_capi.hip", "centroid.hip", "scores.hip", "indexer.hip", "topk.hip", "attention.hip",
+           "mla.hip"]
 ARCH = "gfx950"
 
 

@@ -5,19 +5,20 @@
 // existing attention kernels ("System design > 3. Execution backend"); this
 // one is written for gfx950 instead: decode over a handful of pages per
 // (sequence, KV head) is a pure HBM stream (G flop per byte), so it runs on
-// the vector ALUs, one wave per work item, with no LDS round trip.
+// the vector ALUs with no LDS round trip for K/V.
 //
-// Work item = (sequence b, KV head g, split s); the split streams selected
-// pages [s*pps, min(count, (s+1)*pps)). Pages are walked as 16-token chunks.
-// A chunk is read with 16-byte loads, lane l covering bytes [16 l, 16 l + 16)
-// of every 1 KB of the chunk, so each load instruction is 1 KB contiguous.
-// That puts each token row across LPR = Dk / E lanes (E elements per 16 B) and
-// TPI = 64 / LPR tokens in one instruction. q.k is a per-lane partial dot
+// One block of 8 waves per (sequence b, KV head g, split s); the split holds
+// a balanced share of the selection (all of it when the batch fills the
+// GPU). Pages are walked as 16-token chunks, dealt round-robin to the waves;
+// each wave loads a batch of chunks, then consumes it. A chunk is read
+// with 16-byte loads, lane l covering bytes [16 l, 16 l + 16) of every 1 KB,
+// so each load instruction is 1 KB contiguous. That puts each token row
+// across LPR = Dk / E lanes (E elements per 16 B) and TPI = 64 / LPR tokens
+// in one instruction. q.k is a per-lane partial (v_dot2_f32_bf16 for bf16)
 // reduced over the LPR lanes with DPP; each group of LPR lanes ("row") keeps
 // its own online-softmax state (m, l, o) for the tokens it holds, so V needs
-// no cross-lane traffic. Rows are merged once at the end of the split.
-// Logits are kept in log2 units (q pre-scaled by sm_scale * log2 e).
-// The next chunk's loads are issued before the current chunk is consumed.
+// no cross-lane traffic. Rows merge inside the wave, waves merge in LDS, and
+// splits (if any) merge in merge_kernel. Logits are in log2 units.
 #include "vx_internal.h"
 
 namespace vx {
@@ -46,11 +47,26 @@ template <> struct KVTraits<uint16_t> {
   }
 };
 
+// Page range of split s among S: balanced over the selection actually used.
+__device__ __forceinline__ void split_range(int count, int S, int s, int& p0, int& np) {
+  p0 = (int)(((long)count * s) / S);
+  np = (int)(((long)count * (s + 1)) / S) - p0;
+}
+
+#ifndef VX_ATTN_WAVES
+#define VX_ATTN_WAVES 8
+#endif
+constexpr int kWaves = VX_ATTN_WAVES;  // waves per attention block
+#ifndef VX_ATTN_BATCH
+#define VX_ATTN_BATCH 1
+#endif
+constexpr int kBatch = VX_ATTN_BATCH;  // chunks in flight per wave (MFMA kernel)
+
 template <typename QT, typename KV, int G, int DK, int P>
-__global__ __launch_bounds__(256) void attn_gqa_kernel(
+__global__ __launch_bounds__(64 * kWaves) void attn_gqa_kernel(
     Meta m, int hkv, const QT* __restrict__ q, const KV* __restrict__ kp,
     const KV* __restrict__ vp, const int32_t* __restrict__ sel, int stride,
-    const int32_t* __restrict__ sel_count, float qscale, int S, int pps,
+    const int32_t* __restrict__ sel_count, float qscale, int S,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   using T = KVTraits<KV>;
@@ -58,37 +74,38 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(
   constexpr int LPR = DK / E;      // lanes per token row
   constexpr int TPI = 64 / LPR;    // tokens per load instruction
   constexpr int CT = 16;           // tokens per chunk
-  constexpr int CH = CT / TPI;     // load instructions per chunk
+  constexpr int CH = CT / TPI;     // load instructions per chunk (per K and per V)
   constexpr int CPP = P / CT;      // chunks per page
   constexpr bool kDot2 = sizeof(KV) == 2 && sizeof(QT) == 2;
   static_assert(64 % LPR == 0 && CT % TPI == 0 && P % CT == 0, "layout");
 
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  __shared__ int pg_phys[kMaxPagesPerSplit];
+  __shared__ int pg_nv[kMaxPagesPerSplit];
+  __shared__ float red_o[kWaves][G][DK];
+  __shared__ float red_ml[kWaves][G][2];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int hq = hkv * G;
-  if (item >= m.batch * hkv * S) return;
-  const int s = item % S;
-  const int bg = item / S;
+  const int item = blockIdx.x;
+  const int s = item % S, bg = item / S;
   const int b = bg / hkv, g = bg % hkv;
-  const int row = lane / LPR;          // which token of each load this lane holds
-  const int dofs = (lane % LPR) * E;   // first dim this lane holds
+  const int row = lane / LPR;
+  const int dofs = (lane % LPR) * E;
 
   const int L = seq_len_clamped(m, b);
   const int cap = m.indptr[b + 1] - m.indptr[b];
   const int count = cap > 0 ? min(sel_count[bg], stride) : 0;
-  const int p0 = s * pps;
-  const int np = max(0, min(count, p0 + pps) - p0);
-
-  // Page list of this split, one page per lane: physical id and valid tokens.
-  int my_phys = 0, my_nv = 0;
-  if (lane < np) {
-    int lp = sel[(size_t)bg * stride + p0 + lane];
+  int p0, np;
+  split_range(count, S, s, p0, np);
+  np = min(np, kMaxPagesPerSplit);
+  if (threadIdx.x < np) {
+    int lp = sel[(size_t)bg * stride + p0 + threadIdx.x];
     lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);
-    my_phys = phys_page(m, m.indptr[b] + lp);
-    my_nv = max(0, min(P, L - lp * P));
+    pg_phys[threadIdx.x] = phys_page(m, m.indptr[b] + lp);
+    pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
   }
 
-  // Query rows of the group, pre-scaled into log2 units.
+  // Query rows of the group (log2 units): packed bf16 pairs for v_dot2, or fp32.
   float qf[G][E];
   uint32_t qp[G][E / 2];
 #pragma unroll
@@ -114,20 +131,13 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) o[h][e] = 0.f;
   }
+  __syncthreads();  // page list ready
 
   const int nchunks = np * CPP;
-  const size_t head_stride = (size_t)P * DK;  // elements of one (page, head)
-
-  auto chunk_base = [&](int c, int& nv_chunk) -> size_t {
-    const int pi = c / CPP, sub = c % CPP;
-    const int phys = __builtin_amdgcn_readlane(my_phys, pi);
-    nv_chunk = __builtin_amdgcn_readlane(my_nv, pi) - sub * CT;
-    return ((size_t)phys * hkv + g) * head_stride + (size_t)sub * CT * DK;
-  };
+  const size_t head_stride = (size_t)P * DK;
+  auto chunk_nv = [&](int c) { return pg_nv[c / CPP] - (c % CPP) * CT; };
   auto load_chunk = [&](int c, u32x4* kr, u32x4* vr) {
-    int nvc;
-    const size_t base = chunk_base(c, nvc);
-    if (nvc <= 0) return;
+    const size_t base = ((size_t)pg_phys[c / CPP] * hkv + g) * head_stride + (size_t)(c % CPP) * CT * DK;
     const u32x4* kc = (const u32x4*)(kp + base);
     const u32x4* vc = (const u32x4*)(vp + base);
 #pragma unroll
@@ -136,10 +146,10 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(
       vr[i] = __builtin_nontemporal_load(vc + i * 64 + lane);
     }
   };
+  // No early exit: an empty chunk is consumed fully masked, so every slot's
+  // loads are waited on in one place and the prefetch ring stays pipelined.
   auto consume = [&](int c, const u32x4* kr, const u32x4* vr) {
-    int nvc;
-    (void)chunk_base(c, nvc);
-    if (nvc <= 0) return;
+    const int nvc = chunk_nv(c);
     const bool full = nvc >= CT;
     float z[CH][G];
 #pragma unroll
@@ -204,18 +214,20 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(
     }
   };
 
-  u32x4 kA[CH], vA[CH], kB[CH], vB[CH];
-  if (nchunks > 0) load_chunk(0, kA, vA);
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) load_chunk(c + 1, kB, vB);
-    consume(c, kA, vA);
-    if (c + 1 < nchunks) {
-      if (c + 2 < nchunks) load_chunk(c + 2, kA, vA);
-      consume(c + 1, kB, vB);
-    }
+  // Batches of NB chunks (see attn_gqa_mfma_kernel): loads first, then use.
+  constexpr int NB = CH >= 8 ? 1 : kBatch;
+  const int my_n = nchunks > w ? (nchunks - w + kWaves - 1) / kWaves : 0;
+  for (int j0 = 0; j0 < my_n; j0 += NB) {
+    u32x4 kr[NB][CH], vr[NB][CH];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      load_chunk(w + min(j0 + u, my_n - 1) * kWaves, kr[u], vr[u]);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (j0 + u < my_n) consume(w + (j0 + u) * kWaves, kr[u], vr[u]);
   }
 
-  // Merge the TPI rows (lanes l, l ^ LPR, l ^ 2 LPR, ...) of every head.
+  // Merge the TPI rows of each head inside the wave (lanes l ^ LPR, ...).
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -234,51 +246,274 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(
       mrow[h] = mnew;
     }
   }
-
   if (lane < LPR) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int head = g * G + h;
-      if (S == 1) {
-        const float inv = lrow[h] > 0.f ? 1.f / lrow[h] : 0.f;
-        float* dst = out + ((size_t)b * hq + head) * DK + dofs;
 #pragma unroll
-        for (int e = 0; e < E; ++e) dst[e] = o[h][e] * inv;
-        if (lse && lane == 0)
-          lse[(size_t)b * hq + head] =
-              lrow[h] > 0.f ? (mrow[h] + log2f(lrow[h])) * kLn2 : -INFINITY;
-      } else {
-        const size_t ps = ((size_t)b * hq + head) * S + s;
-        float* dst = part_o + ps * DK + dofs;
+      for (int e = 0; e < E; ++e) red_o[w][h][dofs + e] = o[h][e];
+      if (lane == 0) {
+        red_ml[w][h][0] = mrow[h];
+        red_ml[w][h][1] = lrow[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves: thread -> (head, 4 dims).
+  for (int t = threadIdx.x; t < G * DK / 4; t += blockDim.x) {
+    const int h = t / (DK / 4), d = (t % (DK / 4)) * 4;
+    float mmax = kNegBig;
 #pragma unroll
-        for (int e = 0; e < E; ++e) dst[e] = o[h][e];
-        if (lane == 0) {
-          part_ml[2 * ps] = mrow[h];
-          part_ml[2 * ps + 1] = lrow[h];
-        }
+    for (int v = 0; v < kWaves; ++v) mmax = fmaxf(mmax, red_ml[v][h][0]);
+    float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float wt = __builtin_amdgcn_exp2f(red_ml[v][h][0] - mmax);
+      lsum = fmaf(red_ml[v][h][1], wt, lsum);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(red_o[v][h][d + e], wt, acc[e]);
+    }
+    const int head = g * G + h;
+    if (S == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      float4* dst = (float4*)(out + ((size_t)b * hq + head) * DK + d);
+      *dst = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      if (lse && d == 0)
+        lse[(size_t)b * hq + head] = lsum > 0.f ? (mmax + log2f(lsum)) * kLn2 : -INFINITY;
+    } else {
+      const size_t ps = ((size_t)b * hq + head) * S + s;
+      *(float4*)(part_o + ps * DK + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if (d == 0) {
+        part_ml[2 * ps] = mmax;
+        part_ml[2 * ps + 1] = lsum;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, Dk = Dv = 128: the group's query heads (G <= 16, padded to 16 rows)
+// against each 16-token chunk on the matrix cores.
+//   q.k^T  v_mfma_f32_16x16x32_bf16: A = query rows (lane: head l%16, dims
+//          8 q4 + 32 ks..), B = key rows straight from HBM (lane: token l%16,
+//          the same dims) -> S[head 4 q4 + i][token l%16].
+//   P.V    v_mfma_f32_16x16x16_bf16: lane (q4, c) loads tokens 4 q4 .. 4 q4+3,
+//          dims 8 c .. 8 c+7 (four 16-byte loads, whole 256-byte rows per
+//          instruction). Taking N-tile e's columns as dims {8 c + e}, the B
+//          fragment is element e of the lane's four rows; P reaches the A
+//          layout (head l%16, tokens 4 q4..) through a 16x16 LDS tile.
+//   -> O[head 4 q4 + i][dim 8 c + e] in accumulator e.
+// Vector work per chunk is the online softmax only.
+constexpr int kPRow = 20;  // padded row of a wave's P tile (bf16)
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t elem16(const u32x4& v, int e) {
+  const uint32_t wv = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return (e & 1) ? (wv >> 16) : (wv & 0xffffu);
+}
+
+template <int G, int P>
+__global__ __launch_bounds__(64 * kWaves) void attn_gqa_mfma_kernel(
+    Meta m, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
+    const uint16_t* __restrict__ vp, const int32_t* __restrict__ sel, int stride,
+    const int32_t* __restrict__ sel_count, float qscale, int S, float* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int DK = 128;
+  constexpr int CT = 16;
+  constexpr int CPP = P / CT;
+  static_assert(G >= 1 && G <= 16, "group");
+
+  __shared__ int pg_phys[kMaxPagesPerSplit];
+  __shared__ int pg_nv[kMaxPagesPerSplit];
+  __shared__ float red_o[kWaves][G][DK];
+  __shared__ float red_ml[kWaves][G][2];
+  __shared__ __attribute__((aligned(16))) uint16_t ptile[kWaves][16 * kPRow];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, q4 = lane >> 4;
+  const int hq = hkv * G;
+  const int item = blockIdx.x;
+  const int s = item % S, bg = item / S;
+  const int b = bg / hkv, g = bg % hkv;
+
+  const int L = seq_len_clamped(m, b);
+  const int cap = m.indptr[b + 1] - m.indptr[b];
+  const int count = cap > 0 ? min(sel_count[bg], stride) : 0;
+  int p0, np;
+  split_range(count, S, s, p0, np);
+  np = min(np, kMaxPagesPerSplit);
+  if (threadIdx.x < np) {
+    int lp = sel[(size_t)bg * stride + p0 + threadIdx.x];
+    lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);
+    pg_phys[threadIdx.x] = phys_page(m, m.indptr[b] + lp);
+    pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
+  }
+
+  // A operand of q.k^T: head row `col` (zero past the group), dims 32 ks + 8 q4.
+  u32x4 qa[DK / 32];
+  {
+    const bool real = col < G;
+    const uint16_t* qh = q + ((size_t)b * hq + g * G + (real ? col : 0)) * DK + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+      qa[ks] = real ? *(const u32x4*)(qh + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { mrow[i] = kNegBig; lrow[i] = 0.f; }
+  uint16_t* pw = ptile[w];
+  __syncthreads();  // page list ready
+
+  const int nchunks = np * CPP;
+  const size_t head_stride = (size_t)P * DK;
+  auto chunk_nv = [&](int c) { return pg_nv[c / CPP] - (c % CPP) * CT; };
+  auto load_chunk = [&](int c, u32x4* kr, u32x4* vr) {
+    const size_t base = ((size_t)pg_phys[c / CPP] * hkv + g) * head_stride + (size_t)(c % CPP) * CT * DK;
+    const uint16_t* kc = kp + base + (size_t)col * DK + 8 * q4;
+    const uint16_t* vc = vp + base + (size_t)(4 * q4) * DK + 8 * col;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) kr[ks] = __builtin_nontemporal_load((const u32x4*)(kc + 32 * ks));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vr[r] = __builtin_nontemporal_load((const u32x4*)(vc + r * DK));
+  };
+  auto consume = [&](int c, const u32x4* kr, const u32x4* vr) {
+    const int nvc = chunk_nv(c);
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[ks]),
+                                                     __builtin_bit_cast(bf16x8_t, kr[ks]), sacc,
+                                                     0, 0, 0);
+    const bool tok_ok = col < nvc;
+    float alpha[4];
+    bool grow = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float z = tok_ok ? sacc[i] * qscale : -INFINITY;
+      const float mnew = fmaxf(mrow[i], group_max<16>(z));
+      alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mnew);
+      grow = grow || (mnew > mrow[i]);
+      const float pv = __builtin_amdgcn_exp2f(z - mnew);
+      lrow[i] = fmaf(lrow[i], alpha[i], group_sum<16>(pv));
+      mrow[i] = mnew;
+      pw[(4 * q4 + i) * kPRow + col] = f32_to_bf16(pv);
+    }
+    if (__ballot(grow)) {  // rescale only when some row's maximum moved
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[e][i] *= alpha[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint2 pa = *(const uint2*)(pw + col * kPRow + 4 * q4);
+    u32x4 v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (4 * q4 + r < nvc) ? vr[r] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b01 = elem16(v[0], e) | (elem16(v[1], e) << 16);
+      const uint32_t b23 = elem16(v[2], e) | (elem16(v[3], e) << 16);
+      o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(bf16x4_t, pa), __builtin_bit_cast(bf16x4_t, uint2{b01, b23}), o[e],
+          0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();  // P tile reads done before the next chunk writes it
+  };
+
+  // Batches of kBatch chunks: all loads of a batch are issued, then the
+  // batch is consumed. No load register lives across iterations, so nothing
+  // forces the compiler to copy (and wait on) in-flight registers.
+  const int my_n = nchunks > w ? (nchunks - w + kWaves - 1) / kWaves : 0;
+  for (int j0 = 0; j0 < my_n; j0 += kBatch) {
+    u32x4 kr[kBatch][DK / 32], vr[kBatch][4];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)  // unconditional: a short last batch re-reads a chunk
+      load_chunk(w + min(j0 + u, my_n - 1) * kWaves, kr[u], vr[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (j0 + u < my_n) consume(w + (j0 + u) * kWaves, kr[u], vr[u]);
+  }
+
+  // Per-wave results of the group's heads to LDS, then merge the waves.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * q4 + i;
+    if (h < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[w][h][8 * col + e] = o[e][i];
+      if (col == 0) {
+        red_ml[w][h][0] = mrow[i];
+        red_ml[w][h][1] = lrow[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * DK / 4; t += blockDim.x) {
+    const int h = t / (DK / 4), d = (t % (DK / 4)) * 4;
+    float mmax = kNegBig;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) mmax = fmaxf(mmax, red_ml[v][h][0]);
+    float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float wt = __builtin_amdgcn_exp2f(red_ml[v][h][0] - mmax);
+      lsum = fmaf(red_ml[v][h][1], wt, lsum);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(red_o[v][h][d + e], wt, acc[e]);
+    }
+    const int head = g * G + h;
+    if (S == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      *(float4*)(out + ((size_t)b * hq + head) * DK + d) =
+          make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      if (lse && d == 0)
+        lse[(size_t)b * hq + head] = lsum > 0.f ? (mmax + log2f(lsum)) * kLn2 : -INFINITY;
+    } else {
+      const size_t ps = ((size_t)b * hq + head) * S + s;
+      *(float4*)(part_o + ps * DK + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if (d == 0) {
+        part_ml[2 * ps] = mmax;
+        part_ml[2 * ps + 1] = lsum;
       }
     }
   }
 }
 
 // out[b][h] = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m).
-__global__ __launch_bounds__(64) void merge_kernel(int S, int dv, const float* __restrict__ part_o,
-                                                   const float* __restrict__ part_ml,
-                                                   float* __restrict__ out,
-                                                   float* __restrict__ lse) {
+// One block per (sequence, head), one thread per 4 value columns.
+__global__ __launch_bounds__(128) void merge_kernel(int S, int dv, const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    float* __restrict__ out,
+                                                    float* __restrict__ lse) {
   const int bh = blockIdx.x;
   const float* ml = part_ml + (size_t)bh * S * 2;
   float mmax = kNegBig;
   for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+  const int d = 4 * threadIdx.x;
   float wsum = 0.f;
-  for (int s = 0; s < S; ++s) wsum += ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int d = threadIdx.x; d < dv; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s)
-      acc = fmaf(__builtin_amdgcn_exp2f(ml[2 * s] - mmax), part_o[((size_t)bh * S + s) * dv + d], acc);
-    out[(size_t)bh * dv + d] = acc * inv;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* po = part_o + (size_t)bh * S * dv + d;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
+    wsum = fmaf(ml[2 * s + 1], wt, wsum);
+    if (d < dv) {
+      const float4 x = *(const float4*)(po + (size_t)s * dv);
+      acc.x = fmaf(x.x, wt, acc.x); acc.y = fmaf(x.y, wt, acc.y);
+      acc.z = fmaf(x.z, wt, acc.z); acc.w = fmaf(x.w, wt, acc.w);
+    }
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (d < dv)
+    *(float4*)(out + (size_t)bh * dv + d) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   if (lse && threadIdx.x == 0)
     lse[bh] = wsum > 0.f ? (mmax + log2f(wsum)) * kLn2 : -INFINITY;
 }
@@ -290,13 +525,13 @@ hipError_t launch_g(const Meta& m, const vx_geom& geo, const void* q, const void
                     hipStream_t st) {
   const int hkv = geo.num_kv_heads;
   const int items = m.batch * hkv * S;
-  dim3 block(256), grid((items + 3) / 4);
+  dim3 block(64 * kWaves), grid(items);
   const int G = geo.num_q_heads / hkv;
 #define VX_ATTN_CASE(GG)                                                                       \
   case GG:                                                                                     \
     hipLaunchKernelGGL((attn_gqa_kernel<QT, KV, GG, DK, P>), grid, block, 0, st, m, hkv,      \
                        (const QT*)q, (const KV*)k_pool, (const KV*)v_pool, sel, stride, cnt,   \
-                       qscale, S, pps, out, lse, po, pml);                                     \
+                       qscale, S, out, lse, po, pml);                                          \
     break;
   switch (G) {
     VX_ATTN_CASE(1)
@@ -307,6 +542,32 @@ hipError_t launch_g(const Meta& m, const vx_geom& geo, const void* q, const void
       return hipErrorInvalidValue;
   }
 #undef VX_ATTN_CASE
+  return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_mfma(const Meta& m, const vx_geom& geo, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* sel, int stride, const int32_t* cnt,
+                       float qscale, int S, float* out, float* lse, float* po, float* pml,
+                       hipStream_t st) {
+  const int hkv = geo.num_kv_heads;
+  dim3 block(64 * kWaves), grid(m.batch * hkv * S);
+  const int G = geo.num_q_heads / hkv;
+#define VX_MFMA_CASE(GG)                                                                        \
+  case GG:                                                                                      \
+    hipLaunchKernelGGL((attn_gqa_mfma_kernel<GG, P>), grid, block, 0, st, m, hkv,              \
+                       (const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,   \
+                       sel, stride, cnt, qscale, S, out, lse, po, pml);                        \
+    break;
+  switch (G) {
+    VX_MFMA_CASE(1)
+    VX_MFMA_CASE(2)
+    VX_MFMA_CASE(4)
+    VX_MFMA_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef VX_MFMA_CASE
   return hipGetLastError();
 }
 
@@ -322,6 +583,16 @@ hipError_t launch_t(const Meta& m, const vx_geom& geo, const void* q, const void
   if (dk == 64 && P == 64)
     return launch_g<QT, KV, 64, 64>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, pps,
                                     out, lse, po, pml, st);
+#ifndef VX_GQA_FORCE_VALU
+  if constexpr (sizeof(KV) == 2) {
+    if (dk == 128 && P == 16)
+      return launch_mfma<16>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out, lse,
+                             po, pml, st);
+    if (dk == 128 && P == 64)
+      return launch_mfma<64>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out, lse,
+                             po, pml, st);
+  }
+#endif
   if (dk == 128 && P == 16)
     return launch_g<QT, KV, 128, 16>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, pps,
                                      out, lse, po, pml, st);
@@ -350,8 +621,8 @@ hipError_t launch_attention_gqa(const Meta& m, const vx_geom& g, const void* q,
 hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* part_o,
                         const float* part_ml, float* out, float* lse, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(64), 0, s, num_splits, dv, part_o,
-                     part_ml, out, lse);
+  hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3((dv / 4 + 63) / 64 * 64), 0, s,
+                     num_splits, dv, part_o, part_ml, out, lse);
   return hipGetLastError();
 }
 

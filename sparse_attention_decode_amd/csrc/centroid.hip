@@ -43,11 +43,24 @@ __device__ __forceinline__ void refresh_pair(const KV* __restrict__ kp, int P, i
   const int g = pair / (dk / 2);
   const int d = 2 * (pair % (dk / 2));
   const KV* base = kp + ((size_t)pid * hkv + g) * (size_t)P * dk + d;
+  // Loads of 16 tokens are issued together; the sums still run in token order.
   float s0 = 0.f, s1 = 0.f;
-  for (int t = 0; t < nv; ++t) {
-    float2 x = (t == slot) ? fresh : Pair<KV>::get(base + (size_t)t * dk);
-    s0 += x.x;
-    s1 += x.y;
+  for (int t0 = 0; t0 < nv; t0 += 16) {
+    float2 x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = t0 + u;
+      x[u] = t < nv ? Pair<KV>::get(base + (size_t)t * dk) : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = t0 + u;
+      if (t < nv) {
+        const float2 v = (t == slot) ? fresh : x[u];
+        s0 += v.x;
+        s1 += v.y;
+      }
+    }
   }
   float2 c = make_float2(0.f, 0.f);
   if (nv > 0) {
@@ -102,7 +115,7 @@ __global__ void centroid_append_kernel(Meta m, int hkv, int dk, int dv, KV* __re
     }
   }
 
-  int ft = first_token[b];
+  int ft = first_token ? first_token[b] : -1;  // NULL: the newest token's page only
   if (ft < 0) ft += L;  // negative: counted from the end (-1 = newest token)
   ft = ft < 0 ? 0 : (ft > last ? last : ft);
   for (int p = ft / P; p <= last_page; ++p) {

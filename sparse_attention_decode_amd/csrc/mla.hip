@@ -89,52 +89,65 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 }
 
 // ---------------------------------------------------------------- attention
-// One block (4 waves) per (sequence b, split s). Pages are processed as
-// 32-token chunks staged in LDS; the next chunk is prefetched into registers
-// while the current one is consumed. Wave w owns query-head tile
-// mt = w % MT and value columns [part * DV / NP, +DV / NP), NP = 4 / MT; it
-// computes its heads' logits for the whole chunk itself, so its online
-// softmax state needs no exchange with other waves.
-constexpr int CHT = 32;                        // tokens per chunk
-constexpr int CHUNK_VEC = CHT * DK / 8;        // 16-byte vectors per chunk (2304)
-constexpr int VEC_PER_THREAD = CHUNK_VEC / 256;  // 9
-constexpr int PROW = CHT + 8;                  // padded P row (bf16)
+// One block (4 waves) per (sequence b, split s); the split holds a balanced
+// share of the selected pages. Pages are consumed as 32-token chunks. Each
+// chunk is staged in LDS twice: row-major (the B operand of q.k^T reads a
+// token's 8 consecutive columns) and value columns transposed (the B operand
+// of P.V reads 8 consecutive tokens of one column); the transpose is done in
+// registers on 8x8 bf16 blocks, so both operands are single 16-byte LDS
+// reads. The next chunk is prefetched into registers while the current one
+// is consumed. Logits: wave w computes the 16x16 tile (head tile w % MT,
+// token half w / MT); row maxima and sums are exchanged through LDS. P.V:
+// wave w owns head tile w % MT and value columns [part * 512 / NP, +512 / NP).
+constexpr int CHT = 32;                 // tokens per chunk
+constexpr int VT_ROW = CHT + 8;         // padded transposed-V row (bf16), 80 B
+constexpr int PROW = CHT + 8;           // padded P row (bf16)
+
+__device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
+  const uint32_t wv = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return (e & 1) ? (wv >> 16) : (wv & 0xffffu);
+}
 
 template <int MT>
 __global__ __launch_bounds__(256) void attn_mla_kernel(
     Meta m, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const int32_t* __restrict__ sel, int stride, const int32_t* __restrict__ sel_count,
-    float qscale, int S, int pps, float* __restrict__ out, float* __restrict__ lse,
+    float qscale, int S, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int HQ = 16 * MT;
   constexpr int NP = 4 / MT;          // value-column parts
   constexpr int NT2 = DV / NP / 16;   // 16-column tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t kc[CHT * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[4][16 * PROW];
+  __shared__ __attribute__((aligned(16))) uint16_t krow[CHT * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[DV * VT_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t pl[MT][16 * PROW];
+  __shared__ float rmax[MT][2][16];
+  __shared__ float rsum[MT][2][16];
   __shared__ int pg_phys[kMaxPagesPerSplit];
   __shared__ int pg_nv[kMaxPagesPerSplit];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
   const int col = lane & 15, q4 = lane >> 4;
   const int mt = w % MT, part = w / MT;
+  const bool qk_wave = w < 2 * MT;
+  const int nt = w / MT;  // token half of the logit tile (qk waves)
   const int item = blockIdx.x;
   const int s = item % S, b = item / S;
   const int row0 = m.indptr[b];
   const int cap = m.indptr[b + 1] - row0;
   const int L = seq_len_clamped(m, b);
   const int count = cap > 0 ? min(sel_count[b], stride) : 0;
-  const int p0 = s * pps;
-  const int np = max(0, min(count, p0 + pps) - p0);
+  const int p0 = (int)(((long)count * s) / S);
+  const int np = min((int)(((long)count * (s + 1)) / S) - p0, kMaxPagesPerSplit);
   const int P = m.page_size;
 
-  if (threadIdx.x < np) {
-    int lp = sel[(size_t)b * stride + p0 + threadIdx.x];
+  if (t < np) {
+    int lp = sel[(size_t)b * stride + p0 + t];
     lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);
-    pg_phys[threadIdx.x] = phys_page(m, row0 + lp);
-    pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
+    pg_phys[t] = phys_page(m, row0 + lp);
+    pg_nv[t] = max(0, min(P, L - lp * P));
   }
 
-  // Query fragments of this wave's head tile (A operand of q.k), kept in VGPRs.
   u32x4 qf[KSTEPS];
   {
     const uint16_t* qrow = q + ((size_t)b * HQ + 16 * mt + col) * DK + 8 * q4;
@@ -143,100 +156,112 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
   }
   f32x4 o[NT2];
 #pragma unroll
-  for (int t = 0; t < NT2; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < NT2; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[4], lrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { mrow[i] = kNegBig; lrow[i] = 0.f; }
   __syncthreads();  // page list ready
 
-  const int cpp = P / CHT;  // chunks per page
+  const int cpp = P / CHT;
   const int nchunks = np * cpp;
   auto chunk_valid = [&](int c) { return min(CHT, pg_nv[c / cpp] - (c % cpp) * CHT); };
-  auto chunk_src = [&](int c) {
-    return kp + ((size_t)pg_phys[c / cpp] * P + (size_t)(c % cpp) * CHT) * DK;
-  };
-
-  u32x4 pre[VEC_PER_THREAD];
-  auto prefetch = [&](int c) {
-    const u32x4* src = (const u32x4*)chunk_src(c);
-#pragma unroll
-    for (int r = 0; r < VEC_PER_THREAD; ++r)
-      pre[r] = __builtin_nontemporal_load(src + r * 256 + threadIdx.x);
-  };
   auto next_valid = [&](int c) {
     while (c < nchunks && chunk_valid(c) <= 0) ++c;
     return c;
   };
+  // staging roles: an 8x8 (token x column) block of value columns + one rope vector
+  const int dg = t & 63, tg = t >> 6;      // columns 8 dg.., tokens 8 tg..
+  const int rr = t >> 3, rg = t & 7;       // rope: token rr, columns 512 + 8 rg..
+  u32x4 vb[8], rp;
+  auto prefetch = [&](int c) {
+    const uint16_t* src = kp + ((size_t)pg_phys[c / cpp] * P + (size_t)(c % cpp) * CHT) * DK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vb[i] = __builtin_nontemporal_load((const u32x4*)(src + (8 * tg + i) * DK + 8 * dg));
+    rp = __builtin_nontemporal_load((const u32x4*)(src + rr * DK + DV + 8 * rg));
+  };
 
   const int dcol0 = part * (DV / NP);
-  uint16_t* pw = pl[w];
   int c = next_valid(0);
   if (c < nchunks) prefetch(c);
   while (c < nchunks) {
     const int nv = chunk_valid(c);
-    __syncthreads();  // previous chunk fully consumed
+    __syncthreads();  // (A) previous chunk fully consumed
+    {
+      u32x4 x[8];
 #pragma unroll
-    for (int r = 0; r < VEC_PER_THREAD; ++r) {
-      const int v = r * 256 + threadIdx.x;
-      const int tok = v / (DK / 8), k8 = v % (DK / 8);
-      u32x4 x = pre[r];
-      if (tok >= nv) x = u32x4{0u, 0u, 0u, 0u};  // rows past the sequence end
-      *(u32x4*)(kc + tok * ROW + 8 * k8) = x;
+      for (int i = 0; i < 8; ++i) {
+        x[i] = (8 * tg + i < nv) ? vb[i] : u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)(krow + (8 * tg + i) * ROW + 8 * dg) = x[i];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u32x4 y;
+        y.x = half_of(x[0], e) | (half_of(x[1], e) << 16);
+        y.y = half_of(x[2], e) | (half_of(x[3], e) << 16);
+        y.z = half_of(x[4], e) | (half_of(x[5], e) << 16);
+        y.w = half_of(x[6], e) | (half_of(x[7], e) << 16);
+        *(u32x4*)(vt + (8 * dg + e) * VT_ROW + 8 * tg) = y;
+      }
+      *(u32x4*)(krow + rr * ROW + DV + 8 * rg) = (rr < nv) ? rp : u32x4{0u, 0u, 0u, 0u};
     }
     const int cn = next_valid(c + 1);
     if (cn < nchunks) prefetch(cn);
-    __syncthreads();  // chunk c staged
+    __syncthreads();  // (B) chunk c staged
 
-    // logits S[16 heads][32 tokens] of this wave's head tile
-    f32x4 sacc[2];
+    float z[4];
+    if (qk_wave) {
+      f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
+      const uint16_t* kr = krow + (16 * nt + col) * ROW + 8 * q4;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = kc + (16 * nt + col) * ROW + 8 * q4;
+      for (int ks = 0; ks < KSTEPS; ks += 2) {
+        a0 = mfma(qf[ks], *(const u32x4*)(kr + 32 * ks), a0);
+        a1 = mfma(qf[ks + 1], *(const u32x4*)(kr + 32 * (ks + 1)), a1);
+      }
+      const bool ok = 16 * nt + col < nv;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) sacc[nt] = mfma(qf[ks], *(const u32x4*)(krow + 32 * ks), sacc[nt]);
+      for (int i = 0; i < 4; ++i) {
+        z[i] = ok ? (a0[i] + a1[i]) * qscale : -INFINITY;
+        const float mx = group_max<16>(z[i]);
+        if (col == 0) rmax[mt][nt][4 * q4 + i] = mx;
+      }
     }
-    // online softmax on rows 4*q4 + i; tokens 16 nt + col
-    float alpha[4];
+    __syncthreads();  // (C) row maxima of both token halves
+    float mnew[4], alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float z0 = sacc[0][i] * qscale, z1 = sacc[1][i] * qscale;
-      if (col >= nv) z0 = -INFINITY;
-      if (16 + col >= nv) z1 = -INFINITY;
-      const float mx = group_max<16>(fmaxf(z0, z1));
-      const float mnew = fmaxf(mrow[i], mx);
-      alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mnew);
-      const float e0 = __builtin_amdgcn_exp2f(z0 - mnew), e1 = __builtin_amdgcn_exp2f(z1 - mnew);
-      lrow[i] = lrow[i] * alpha[i] + group_sum<16>(e0 + e1);
-      mrow[i] = mnew;
-      pw[(4 * q4 + i) * PROW + col] = f32_to_bf16(e0);
-      pw[(4 * q4 + i) * PROW + 16 + col] = f32_to_bf16(e1);
+      const int r = 4 * q4 + i;
+      mnew[i] = fmaxf(mrow[i], fmaxf(rmax[mt][0][r], rmax[mt][1][r]));
+      alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mnew[i]);
     }
+    if (qk_wave) {
 #pragma unroll
-    for (int t = 0; t < NT2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] *= alpha[i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O += P . V over the chunk's 32 tokens
-    const u32x4 pa = *(const u32x4*)(pw + col * PROW + 8 * q4);
-#pragma unroll
-    for (int t = 0; t < NT2; ++t) {
-      const int dc = dcol0 + 16 * t + col;
-      uint32_t vb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = kc[(8 * q4 + 2 * e) * ROW + dc];
-        const uint32_t hi = kc[(8 * q4 + 2 * e + 1) * ROW + dc];
-        vb[e] = lo | (hi << 16);
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(z[i] - mnew[i]);
+        const float sum = group_sum<16>(e);
+        if (col == 0) rsum[mt][nt][4 * q4 + i] = sum;
+        pl[mt][(4 * q4 + i) * PROW + 16 * nt + col] = f32_to_bf16(e);
       }
-      o[t] = mfma(pa, u32x4{vb[0], vb[1], vb[2], vb[3]}, o[t]);
     }
+    __syncthreads();  // (D) P and row sums ready
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q4 + i;
+      lrow[i] = lrow[i] * alpha[i] + (rsum[mt][0][r] + rsum[mt][1][r]);
+      mrow[i] = mnew[i];
+    }
+#pragma unroll
+    for (int x = 0; x < NT2; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[x][i] *= alpha[i];
+    const u32x4 pa = *(const u32x4*)(pl[mt] + col * PROW + 8 * q4);
+#pragma unroll
+    for (int x = 0; x < NT2; ++x)
+      o[x] = mfma(pa, *(const u32x4*)(vt + (dcol0 + 16 * x + col) * VT_ROW + 8 * q4), o[x]);
     c = cn;
   }
 
-  // results: rows 4*q4 + i of head tile mt, columns dcol0 + 16 t + col
+  // results: rows 4*q4 + i of head tile mt, columns dcol0 + 16 x + col
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int head = 16 * mt + 4 * q4 + i;
@@ -244,14 +269,14 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
       const float inv = lrow[i] > 0.f ? 1.f / lrow[i] : 0.f;
       float* dst = out + ((size_t)b * HQ + head) * DV + dcol0 + col;
 #pragma unroll
-      for (int t = 0; t < NT2; ++t) dst[16 * t] = o[t][i] * inv;
+      for (int x = 0; x < NT2; ++x) dst[16 * x] = o[x][i] * inv;
       if (lse && part == 0 && col == 0)
         lse[(size_t)b * HQ + head] = lrow[i] > 0.f ? (mrow[i] + log2f(lrow[i])) * kLn2 : -INFINITY;
     } else {
       const size_t ps = ((size_t)b * HQ + head) * S + s;
       float* dst = part_o + ps * DV + dcol0 + col;
 #pragma unroll
-      for (int t = 0; t < NT2; ++t) dst[16 * t] = o[t][i];
+      for (int x = 0; x < NT2; ++x) dst[16 * x] = o[x][i];
       if (part == 0 && col == 0) {
         part_ml[2 * ps] = mrow[i];
         part_ml[2 * ps + 1] = lrow[i];
@@ -289,11 +314,11 @@ hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
   if (g.num_q_heads == 32)
     hipLaunchKernelGGL(attn_mla_kernel<2>, grid, block, 0, s, m, (const uint16_t*)q,
                        (const uint16_t*)k_pool, sel, sel_stride, sel_count, qscale, num_splits,
-                       pages_per_split, out, lse, part_o, part_ml);
+                       out, lse, part_o, part_ml);
   else if (g.num_q_heads == 16)
     hipLaunchKernelGGL(attn_mla_kernel<1>, grid, block, 0, s, m, (const uint16_t*)q,
                        (const uint16_t*)k_pool, sel, sel_stride, sel_count, qscale, num_splits,
-                       pages_per_split, out, lse, part_o, part_ml);
+                       out, lse, part_o, part_ml);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -1,0 +1,244 @@
+// Wave-level radix top-k over one (sequence, KV head) segment of page scores.
+//
+// Vortex paper note, "System design > 1. vFlow": keep the top-k blocks by
+// score; "System design > 3. Execution backend": top-k is the indexer's
+// bottleneck, served by a radix top-k with an approximate mode (stochastic
+// early termination and remapping) when recall can be traded for time.
+//
+// One wave per segment. Scores become order-preserving 32-bit keys in LDS
+// (forced pages get key 0 and never compete). Exact mode runs up to four
+// 8-bit digit passes, most significant first: an LDS histogram of the digit
+// among keys that still match the chosen prefix, a suffix scan across the
+// wave to find the digit where the count from the top reaches the remaining
+// need r, and an early exit when that bucket holds exactly r keys. The
+// survivors are then compacted in index order with ballot + mbcnt prefix
+// sums, which yields ascending page ids and the lower-index tie-break.
+// Approximate mode maps candidate scores affinely onto 256 buckets, runs one
+// pass and fills the r remaining places from the boundary bucket cyclically
+// from a random offset.
+#pragma once
+
+#include "vx_internal.h"
+
+namespace vx {
+namespace topk_detail {
+
+constexpr int kU = 8;  // segment elements per lane handled per loop trip
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Order-preserving key: larger score -> larger key; -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = (s == 0.f) ? 0u : __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t rank_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Suffix scan over lanes: lane l gets sum_{l' >= l} x(l').
+__device__ __forceinline__ uint32_t suffix_scan(uint32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t y = __shfl_down(x, off);
+    if (lane + off < 64) x += y;
+  }
+  return x;
+}
+
+struct Digit {
+  uint32_t d;      // chosen bucket
+  uint32_t above;  // keys strictly above it (among those matching the prefix)
+  uint32_t count;  // keys inside it
+};
+
+// Find the bucket where the count from the top first reaches r (1 <= r <= total).
+__device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t r, int lane) {
+  const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+  const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const uint32_t incl = suffix_scan(h0 + h1 + h2 + h3, lane);  // S(4 lane)
+  const uint32_t s0 = incl, s1 = incl - h0, s2 = s1 - h1, s3 = s2 - h2;  // S(4 lane + i)
+  int hit = -1;
+  uint32_t hab = 0, hcnt = 0;
+  if (s3 >= r && s3 - h3 < r) { hit = 3; hab = s3 - h3; hcnt = h3; }
+  else if (s2 >= r && s2 - h2 < r) { hit = 2; hab = s2 - h2; hcnt = h2; }
+  else if (s1 >= r && s1 - h1 < r) { hit = 1; hab = s1 - h1; hcnt = h1; }
+  else if (s0 >= r && s0 - h0 < r) { hit = 0; hab = s0 - h0; hcnt = h0; }
+  const unsigned long long found = __ballot(hit >= 0);
+  const int src = __ffsll((long long)found) - 1;
+  Digit out;
+  out.d = (uint32_t)__shfl(4 * lane + hit, src);
+  out.above = (uint32_t)__shfl((int)hab, src);
+  out.count = (uint32_t)__shfl((int)hcnt, src);
+  return out;
+}
+
+}  // namespace topk_detail
+
+// Select for one segment whose n keys are already in this wave's LDS
+// (keys[i] = 0 for a forced page, else score_key of its score); `hist` is
+// 256 words of LDS. Writes out[0..stride) and *count_out.
+__device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
+                                                 uint32_t* __restrict__ hist, int n, int k,
+                                                 int n_sink, int n_local, int mode,
+                                                 uint32_t rnd_word, int32_t* __restrict__ out,
+                                                 int stride, int32_t* __restrict__ count_out,
+                                                 int lane) {
+  using namespace topk_detail;
+  const int nf = min(n, n_sink + n_local);  // forced: a prefix and a suffix of [0, n)
+  const int nc = n - nf;
+  const int kk = min(k, nc);
+
+  // Survivors: candidates with (key & mask) > prefix, plus `r` of those with
+  // (key & mask) == prefix taken in index order from offset `off` (cyclic
+  // over the `members` of that tie group).
+  uint32_t prefix = 0, mask = 0, r = (uint32_t)kk, off = 0, members = (uint32_t)nc;
+  if (kk > 0 && kk < nc) {
+    if (mode == VX_TOPK_APPROX) {
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
+      for (int base = 0; base < n; base += 64 * kU) {
+        uint32_t kv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = base + 64 * u + lane;
+          kv[u] = i < n ? keys[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (kv[u]) { kmin = min(kmin, kv[u]); kmax = max(kmax, kv[u]); }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      }
+      const float mn = key_score(kmin), mx = key_score(kmax);
+      const float wdt = __fsub_rn(mx, mn);
+      const bool spread = wdt > 0.f;
+      const float inv = spread ? __fdiv_rn(256.f, wdt) : 0.f;
+      for (int i = lane; i < 256; i += 64) hist[i] = 0;
+      wave_sync();
+      for (int base = 0; base < n; base += 64 * kU) {
+        uint32_t kv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = base + 64 * u + lane;
+          kv[u] = i < n ? keys[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = base + 64 * u + lane;
+          if (kv[u]) {
+            uint32_t bk = 0;
+            if (spread) {
+              const float t = floorf(__fmul_rn(__fsub_rn(key_score(kv[u]), mn), inv));
+              bk = t >= 255.f ? 255u : (uint32_t)t;
+            }
+            keys[i] = (bk << 24) | 1u;  // nonzero; digit 3 is the bucket
+            atomicAdd(&hist[bk], 1u);
+          }
+        }
+      }
+      wave_sync();
+      const Digit dg = find_digit(hist, r, lane);
+      prefix = dg.d << 24;
+      mask = 0xff000000u;
+      r -= dg.above;
+      members = dg.count;
+      off = members ? rnd_word % members : 0u;
+    } else {
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = lane; i < 256; i += 64) hist[i] = 0;
+        wave_sync();
+        for (int base = 0; base < n; base += 64 * kU) {
+          uint32_t kv[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int i = base + 64 * u + lane;
+            kv[u] = i < n ? keys[i] : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            if (kv[u] && (kv[u] & mask) == prefix) atomicAdd(&hist[(kv[u] >> shift) & 255u], 1u);
+        }
+        wave_sync();
+        const Digit dg = find_digit(hist, r, lane);
+        prefix |= dg.d << shift;
+        mask |= 255u << shift;
+        r -= dg.above;
+        members = dg.count;
+        wave_sync();
+        if (dg.count == r) break;  // the whole bucket is needed: exact already
+      }
+    }
+  }
+
+  // Ordered compaction (ascending page index).
+  uint32_t written = 0, tie_seen = 0;
+  for (int base0 = 0; base0 < n; base0 += 64 * kU) {
+    uint32_t kvs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base0 + 64 * u + lane;
+      kvs[u] = i < n ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+    const int i = base0 + 64 * u + lane;
+    const bool in = i < n;
+    const uint32_t kv = kvs[u];
+    const bool forced = in && (i < n_sink || i >= n - n_local);
+    const bool cand = kv != 0u;
+    const bool above = cand && (kv & mask) > prefix;
+    const bool tie = cand && (kv & mask) == prefix;
+    const unsigned long long tmask = __ballot(tie);
+    const uint32_t trank = tie_seen + rank_below(tmask);
+    tie_seen += (uint32_t)__popcll(tmask);
+    bool take = forced || above;
+    if (tie && members) take = take || ((trank + members - off) % members) < r;
+    const unsigned long long smask = __ballot(take);
+    if (take) out[written + rank_below(smask)] = i;
+    written += (uint32_t)__popcll(smask);
+    }
+  }
+  for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
+  if (lane == 0) *count_out = (int32_t)written;
+}
+
+// Select for one segment: `sc` points at its n scores, `keys` / `hist` at
+// this wave's LDS (cap_keys + 256 words). Writes out[0..stride) and *count_out.
+__device__ __forceinline__ void wave_select(uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
+                                            int cap_keys, const float* __restrict__ sc, int n, int k,
+                                            int n_sink, int n_local, int mode, uint32_t rnd_word,
+                                            int32_t* __restrict__ out, int stride,
+                                            int32_t* __restrict__ count_out, int lane) {
+  using namespace topk_detail;
+  n = n > cap_keys ? cap_keys : n;  // a wrong host max_pages must not overrun LDS
+  // Load the segment 8 elements per lane at a time (all loads in flight).
+  for (int base = 0; base < n; base += 64 * kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + 64 * u + lane;
+      v[u] = i < n ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + 64 * u + lane;
+      if (i < n) keys[i] = (i < n_sink || i >= n - n_local) ? 0u : score_key(v[u]);
+    }
+  }
+  wave_sync();
+  wave_select_keys(keys, hist, n, k, n_sink, n_local, mode, rnd_word, out, stride, count_out, lane);
+}
+
+}  // namespace vx

@@ -76,6 +76,29 @@ vx_status check_geom(const vx_geom* g) {
   return VX_OK;
 }
 
+vx_status check_topk(const vx_pages* p, int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
+                     const uint32_t* rand_u32, const int32_t* sel, int32_t sel_stride,
+                     const int32_t* sel_count) {
+  VX_CHECK(k >= 0 && n_sink >= 0 && n_local >= 0, VX_ERR_INVALID_ARG,
+           "k, n_sink, n_local must be >= 0");
+  VX_CHECK((long)k + n_sink + n_local <= sel_stride && sel_stride >= 1, VX_ERR_INVALID_ARG,
+           "sel_stride %d < max(1, k + n_sink + n_local)", sel_stride);
+  VX_CHECK(mode == VX_TOPK_EXACT || mode == VX_TOPK_APPROX, VX_ERR_INVALID_ARG, "mode %d", mode);
+  VX_CHECK(mode != VX_TOPK_APPROX || rand_u32, VX_ERR_INVALID_ARG, "approx mode needs rand_u32");
+  VX_CHECK(p->max_pages <= vx::kMaxTopkPages, VX_ERR_UNSUPPORTED,
+           "max_pages %d > %d", p->max_pages, vx::kMaxTopkPages);
+  VX_CHECK(p->batch == 0 || (sel && sel_count), VX_ERR_INVALID_ARG, "sel or sel_count is NULL");
+  return VX_OK;
+}
+
+// Waves per block of the stand-alone top-k kernel: as many LDS-resident
+// segments as fit 64 KB, at most 4.
+int topk_waves(int max_pages) {
+  const int cap_keys = (max_pages + 63) / 64 * 64;
+  const int wpb = (int)(65536 / ((size_t)(cap_keys + 256) * 4));
+  return wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
+}
+
 vx::Meta meta_of(const vx_pages* p) {
   vx::Meta m;
   m.batch = p->batch;
@@ -108,12 +131,14 @@ vx_status device_cus(int* out) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr int kScorePagesPerWave = 4;
+constexpr int kScorePagesPerWave = 8;
 
-// The planner. Attention work items are (sequence, KV head, split) for GQA
-// and (sequence, split) for MLA. Splits are sized so the launch holds about
-// kWavesPerCU waves per compute unit when the batch alone cannot fill the
-// chip, never more than kMaxPagesPerSplit pages per split.
+// The planner. An attention block serves one (sequence, KV head) for GQA or
+// one sequence for MLA, with its waves splitting that selection's chunks;
+// when the batch alone gives fewer blocks than compute units, each selection
+// is cut into S balanced splits (merged afterwards by log-sum-exp) so that
+// about one block runs per compute unit. No split holds more than
+// kMaxPagesPerSplit pages.
 vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num_splits,
                     int num_cus, vx_plan* out) {
   *out = vx_plan{};
@@ -124,24 +149,18 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   if (num_splits > 0) {
     S = num_splits;
   } else {
-    // Enough waves in flight to cover HBM latency: 8 per CU for 16-token
-    // pages; large pages carry more bytes per wave, 4 per CU suffice.
-    // GQA items are single waves; MLA items are 4-wave blocks.
-    const long target = g->mla ? (long)num_cus * 2 : (long)num_cus * (p->page_size >= 64 ? 4 : 8);
-    long s = items0 > 0 ? (target + items0 - 1) / items0 : 1;
+    long s = items0 > 0 ? (num_cus + items0 - 1) / items0 : 1;
     S = (int)(s < 1 ? 1 : s);
   }
   if (S > stride) S = stride;
-  int pps = (stride + S - 1) / S;
-  if (pps > vx::kMaxPagesPerSplit) pps = vx::kMaxPagesPerSplit;
-  S = (stride + pps - 1) / pps;
+  const int min_splits = (stride + vx::kMaxPagesPerSplit - 1) / vx::kMaxPagesPerSplit;
+  if (S < min_splits) S = min_splits;
+  const int pps = (stride + S - 1) / S;  // largest split
   out->num_splits = S;
   out->pages_per_split = pps;
   out->score_pages_per_block = 4 * kScorePagesPerWave;
   out->score_blocks = (p->total_pages + out->score_pages_per_block - 1) / out->score_pages_per_block;
-  const int cap_keys = (p->max_pages + 63) / 64 * 64;
-  int wpb = (int)(65536 / ((size_t)(cap_keys + 256) * 4));
-  out->topk_threads = 64 * (wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb));
+  out->topk_threads = 64 * topk_waves(p->max_pages);
   const int hq = g->num_q_heads, dv = g->head_dim_v;
   size_t ws = 0;
   if (S > 1) {
@@ -223,8 +242,8 @@ vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom, const void*
     e = vx::launch_scores_mla_sized(m, *geom, q, (const uint16_t*)centroids, score_scale, scores,
                                     pages->max_pages, stream);
   else
-    e = vx::launch_scores_gqa(m, *geom, q, (const float*)centroids, score_scale, scores,
-                              kScorePagesPerWave, stream);
+    e = vx::launch_scores_gqa(m, *geom, q, nullptr, const_cast<float*>((const float*)centroids),
+                              nullptr, 0, score_scale, scores, stream);
   return hip_status(e, "score kernel launch");
 }
 
@@ -235,23 +254,63 @@ vx_status vx_topk_pages(const vx_pages* pages, int32_t num_kv_heads, const float
   vx_status st;
   if ((st = check_pages(pages)) != VX_OK) return st;
   VX_CHECK(num_kv_heads >= 1, VX_ERR_INVALID_ARG, "num_kv_heads < 1");
-  VX_CHECK(k >= 0 && n_sink >= 0 && n_local >= 0, VX_ERR_INVALID_ARG,
-           "k, n_sink, n_local must be >= 0");
-  VX_CHECK((long)k + n_sink + n_local <= sel_stride && sel_stride >= 1, VX_ERR_INVALID_ARG,
-           "sel_stride %d < max(1, k + n_sink + n_local)", sel_stride);
-  VX_CHECK(mode == VX_TOPK_EXACT || mode == VX_TOPK_APPROX, VX_ERR_INVALID_ARG, "mode %d", mode);
-  VX_CHECK(mode != VX_TOPK_APPROX || rand_u32, VX_ERR_INVALID_ARG, "approx mode needs rand_u32");
-  VX_CHECK(pages->max_pages <= vx::kMaxTopkPages, VX_ERR_UNSUPPORTED,
-           "max_pages %d > %d", pages->max_pages, vx::kMaxTopkPages);
-  VX_CHECK(pages->batch == 0 || (sel && sel_count), VX_ERR_INVALID_ARG, "sel or sel_count is NULL");
+  if ((st = check_topk(pages, k, n_sink, n_local, mode, rand_u32, sel, sel_stride, sel_count)) !=
+      VX_OK)
+    return st;
   VX_CHECK(pages->total_pages == 0 || scores, VX_ERR_INVALID_ARG, "scores is NULL");
   if (pages->batch == 0) return VX_OK;
   const vx::Meta m = meta_of(pages);
-  const int cap_keys = (pages->max_pages + 63) / 64 * 64;
-  int wpb = (int)(65536 / ((size_t)(cap_keys + 256) * 4));
-  wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
   hipError_t e = vx::launch_topk_sized(m, num_kv_heads, scores, k, n_sink, n_local, mode, rand_u32,
-                                       sel, sel_stride, sel_count, pages->max_pages, wpb, stream);
+                                       sel, sel_stride, sel_count, pages->max_pages,
+                                       topk_waves(pages->max_pages), stream);
+  return hip_status(e, "top-k kernel launch");
+}
+
+vx_status vx_index_pages(const vx_pages* pages, const vx_geom* geom, const void* q,
+                         const void* k_pool, float* centroids, void* cent_bf16,
+                         int32_t refresh_newest, float score_scale, float* scores, int32_t k,
+                         int32_t n_sink, int32_t n_local, int32_t mode, const uint32_t* rand_u32,
+                         int32_t* sel, int32_t sel_stride, int32_t* sel_count,
+                         hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(refresh_newest == 0 || refresh_newest == 1, VX_ERR_INVALID_ARG,
+           "refresh_newest must be 0 or 1");
+  VX_CHECK(std::isfinite(score_scale), VX_ERR_INVALID_ARG, "score_scale not finite");
+  if ((st = check_topk(pages, k, n_sink, n_local, mode, rand_u32, sel, sel_stride, sel_count)) !=
+      VX_OK)
+    return st;
+  VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
+  VX_CHECK(pages->total_pages == 0 || scores, VX_ERR_INVALID_ARG, "scores is NULL");
+  VX_CHECK(pages->total_pages == 0 || centroids, VX_ERR_INVALID_ARG, "centroids is NULL");
+  VX_CHECK(!geom->mla || pages->total_pages == 0 || cent_bf16, VX_ERR_INVALID_ARG,
+           "MLA scores the bf16 centroids: cent_bf16 is NULL");
+  VX_CHECK(!refresh_newest || pages->total_pages == 0 || k_pool, VX_ERR_INVALID_ARG,
+           "refresh_newest needs k_pool");
+  if (pages->batch == 0) return VX_OK;
+  const vx::Meta m = meta_of(pages);
+  hipError_t e = hipSuccess;
+  if (pages->total_pages > 0) {
+    if (geom->mla) {
+      if (refresh_newest) {
+        e = vx::launch_centroid_append(m, *geom, const_cast<void*>(k_pool), nullptr, nullptr,
+                                       nullptr, nullptr, centroids, (uint16_t*)cent_bf16, stream);
+        if (e != hipSuccess) return hip_status(e, "centroid kernel launch");
+      }
+      e = vx::launch_scores_mla_sized(m, *geom, q, (const uint16_t*)cent_bf16, score_scale, scores,
+                                      pages->max_pages, stream);
+    } else {
+      e = vx::launch_index_gqa(m, *geom, q, k_pool, centroids, (uint16_t*)cent_bf16,
+                               refresh_newest, score_scale, scores, k, n_sink, n_local, mode,
+                               rand_u32, sel, sel_stride, sel_count, pages->max_pages, stream);
+      return hip_status(e, "indexer kernel launch");
+    }
+    if (e != hipSuccess) return hip_status(e, "score kernel launch");
+  }
+  e = vx::launch_topk_sized(m, geom->num_kv_heads, scores, k, n_sink, n_local, mode, rand_u32, sel,
+                            sel_stride, sel_count, pages->max_pages, topk_waves(pages->max_pages),
+                            stream);
   return hip_status(e, "top-k kernel launch");
 }
 

@@ -49,6 +49,34 @@ VX_DEV int find_seq(const int32_t* __restrict__ indptr, int batch, int j) {
   return lo;
 }
 
+// Sequence owning page-table entry j, computed by a whole wave: the number of
+// sequences e in [1, batch) with indptr[e] <= j (indptr is non-decreasing, so
+// that predicate holds on a prefix of e). A 256-ary search: each round every
+// lane samples 4 evenly spaced entries of the remaining range and a ballot
+// narrows it 256-fold, so batch <= 257 takes one round and <= 65537 two.
+// Every lane returns the same value.
+VX_DEV int wave_find_seq(const int32_t* __restrict__ indptr, int batch, int j, int lane) {
+  int lo = 1, n = batch - 1;  // candidates e in [lo, lo + n); all e < lo hold
+  while (n > 0) {
+    const int step = (n + 255) / 256;
+    int v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 64 * k + lane;
+      v[k] = i * step < n ? indptr[lo + i * step] : 0x7fffffff;
+    }
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c += __popcll(__ballot(v[k] <= j));
+    if (c == 0) break;
+    if (step == 1) return lo - 1 + c;
+    const int nlo = lo + (c - 1) * step + 1;  // sample c-1 holds, sample c does not
+    n = min(step - 1, lo + n - nlo);
+    lo = nlo;
+  }
+  return lo - 1;
+}
+
 // Valid tokens of sequence b, clamped to its page-table capacity.
 VX_DEV int seq_len_clamped(const Meta& m, int b) {
   int cap = (m.indptr[b + 1] - m.indptr[b]) * m.page_size;
@@ -95,6 +123,22 @@ VX_DEV float group_max(float x) {
   return x;
 }
 
+// Four consecutive elements: raw load, then widening to fp32 (kept apart so
+// that many loads can be in flight in raw form).
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+  using raw = float4;
+  static VX_DEV float4 load(const float* p) { return *(const float4*)p; }
+  static VX_DEV float4 widen(float4 r) { return r; }
+};
+template <> struct Quad<uint16_t> {
+  using raw = uint2;
+  static VX_DEV uint2 load(const uint16_t* p) { return *(const uint2*)p; }
+  static VX_DEV float4 widen(uint2 w) {
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+  }
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. Shapes are validated by the
 // caller (vx_capi.hip) before these run.
@@ -105,8 +149,18 @@ hipError_t launch_centroid_append(const Meta& m, const vx_geom& g, void* k_pool,
                                   const int32_t* first_token, const void* k_new,
                                   const void* v_new, float* cent, uint16_t* cent_bf16,
                                   hipStream_t s);
-hipError_t launch_scores_gqa(const Meta& m, const vx_geom& g, const void* q, const float* cent,
-                             float scale, float* scores, int pages_per_wave, hipStream_t s);
+// GQA scores; refresh != 0 first recomputes the centroid (and its bf16 copy
+// when cent_bf16 is given) of each sequence's newest page, reading k_pool.
+hipError_t launch_scores_gqa(const Meta& m, const vx_geom& g, const void* q, const void* k_pool,
+                             float* cent, uint16_t* cent_bf16, int refresh, float scale,
+                             float* scores, hipStream_t s);
+// Fused GQA indexer, one block per (sequence, KV head): newest-page refresh
+// (optional), scores and the top-k selection.
+hipError_t launch_index_gqa(const Meta& m, const vx_geom& g, const void* q, const void* k_pool,
+                            float* cent, uint16_t* cent_bf16, int refresh, float scale,
+                            float* scores, int k, int n_sink, int n_local, int mode,
+                            const uint32_t* rnd, int32_t* sel, int stride, int32_t* sel_count,
+                            int max_pages, hipStream_t s);
 hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,
                                    const uint16_t* cent_bf16, float scale, float* scores,
                                    int max_pages, hipStream_t s);
@@ -131,5 +185,6 @@ hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* 
 constexpr int kMaxPagesPerSplit = 64;
 // Largest per-sequence page count the top-k supports (LDS resident keys).
 constexpr int kMaxTopkPages = 16000;
+
 
 }  // namespace vx

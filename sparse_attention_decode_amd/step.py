@@ -21,11 +21,12 @@ __all__ = ["DecodeStep"]
 class DecodeStep:
     def __init__(self, w: Workload, mode: int = V.VX_TOPK_EXACT, num_splits: int = 0,
                  k: Optional[int] = None, n_sink: Optional[int] = None,
-                 n_local: Optional[int] = None, with_lse: bool = True):
+                 n_local: Optional[int] = None, with_lse: bool = True, fused: bool = True):
         s = w.spec
         dev = w.device
         self.w = w
         self.mode = mode
+        self.fused = fused
         self.num_splits = num_splits
         self.k = s.topk if k is None else k
         self.n_sink = s.n_sink if n_sink is None else n_sink
@@ -78,6 +79,14 @@ class DecodeStep:
                         self.n_local, self.mode, self.w.d_rand_u32, self.sel, self.k_out,
                         self.sel_count, stream)
 
+    def index(self, refresh: bool = True, stream=None) -> None:
+        """Fused indexer: newest-page refresh (optional), scores, selection."""
+        w = self.w
+        V.vx_index_pages(self.pages, self.geom, w.q, w.k_pool, self.centroids, self.cent_bf16,
+                         refresh, self.score_scale, self.scores, self.k, self.n_sink,
+                         self.n_local, self.mode, w.d_rand_u32, self.sel, self.k_out,
+                         self.sel_count, stream)
+
     def attend(self, sel=None, sel_count=None, stream=None) -> None:
         w = self.w
         V.vx_sparse_decode(self.pages, self.geom, w.q, w.k_pool, w.v_pool,
@@ -88,7 +97,10 @@ class DecodeStep:
 
     def run(self, stream=None) -> None:
         """The whole step: cache refresh, scoring, selection, attention."""
-        self.refresh_centroids(stream=stream)
-        self.score(stream)
-        self.select(stream=stream)
+        if self.fused:
+            self.index(stream=stream)
+        else:
+            self.refresh_centroids(stream=stream)
+            self.score(stream)
+            self.select(stream=stream)
         self.attend(stream=stream)

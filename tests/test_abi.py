@@ -129,19 +129,59 @@ def test_empty_batch_is_a_no_op():
 
 def test_planner_splits_and_workspace():
     g = geom()
-    # 32 sequences x 8 KV heads, 18 selected pages, 256 CUs: 8 waves per CU
+    # 32 sequences x 8 KV heads already give one block per compute unit: no split
     plan = V.vx_plan_decode(pages(batch=32, nnz=6144, pool=7680, maxp=256), g, 18, 0, 256)
-    S, pps = plan["num_splits"], plan["pages_per_split"]
-    assert pps == -(-18 // S) and S * pps >= 18 and (S - 1) * pps < 18
-    assert 32 * 8 * S >= 256 * 4
-    assert plan["workspace_bytes"] >= 32 * 16 * S * (128 + 2) * 4
-    # a batch that already fills the chip is not split
-    plan = V.vx_plan_decode(pages(batch=256, nnz=90000, pool=100000, maxp=1024, page_size=64),
-                            g.__class__(64, 8, 128, 128, 0, 1, 1), 64, 0, 256)
     assert plan["num_splits"] == 1 and plan["workspace_bytes"] == 0
-    # an explicit split count is honoured up to the rounding of pages per split
+    # a small batch is split so that about one block runs per compute unit
+    plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 0, 256)
+    S, pps = plan["num_splits"], plan["pages_per_split"]
+    assert S == 16 and pps == 2
+    assert plan["workspace_bytes"] >= 2 * 16 * S * (128 + 2) * 4
+    # an explicit split count is honoured (balanced splits, largest one reported)
     plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 7, 256)
-    assert plan["pages_per_split"] == 3 and plan["num_splits"] == 6
-    # no split streams more than 64 pages
+    assert plan["num_splits"] == 7 and plan["pages_per_split"] == 3
+    # never more splits than selected pages, never more than 64 pages per split
+    plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64), g.__class__(2, 1, 64, 64, 0, 0, 0), 9, 0, 256)
+    assert plan["num_splits"] == 9
     plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=200), g, 131, 1, 256)
     assert plan["pages_per_split"] <= 64 and plan["num_splits"] == 3
+    # MLA: one block per sequence and split
+    mla = V.make_geom(32, 1, 576, 512, 1, V.VX_BF16, V.VX_BF16)
+    plan = V.vx_plan_decode(pages(batch=32, nnz=20480, pool=25600, maxp=1024, page_size=64), mla, 34, 0, 256)
+    assert plan["num_splits"] == 8
+
+
+def test_index_pages_argument_checks():
+    p, g = pages(), geom()
+    ok = dict(q=BAD, k_pool=BAD, centroids=BAD, cent_bf16=None, refresh=1, scale=1.0, scores=BAD,
+              k=4, n_sink=1, n_local=1, mode=0, rand_u32=None, sel=BAD, stride=6, count=BAD,
+              pages=p, geom=g)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return status_of(V.vx_index_pages, a["pages"], a["geom"], a["q"], a["k_pool"],
+                         a["centroids"], a["cent_bf16"], a["refresh"], a["scale"], a["scores"],
+                         a["k"], a["n_sink"], a["n_local"], a["mode"], a["rand_u32"], a["sel"],
+                         a["stride"], a["count"], stream=0)
+
+    assert call(refresh=2) == V.VX_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == V.VX_ERR_INVALID_ARG
+    assert call(stride=5) == V.VX_ERR_INVALID_ARG
+    assert call(k=-1) == V.VX_ERR_INVALID_ARG
+    assert call(mode=1) == V.VX_ERR_INVALID_ARG  # approx without random words
+    assert call(k_pool=None) == V.VX_ERR_INVALID_ARG  # refresh reads the keys
+    assert call(centroids=None) == V.VX_ERR_INVALID_ARG
+    assert call(q=None) == V.VX_ERR_INVALID_ARG
+    assert call(sel=None) == V.VX_ERR_INVALID_ARG
+    assert call(scores=None) == V.VX_ERR_INVALID_ARG
+    mla = V.make_geom(32, 1, 576, 512, 1, V.VX_BF16, V.VX_BF16)
+    mp = pages(page_size=64)
+    assert call(geom=mla, pages=mp) == V.VX_ERR_INVALID_ARG  # MLA scores cent_bf16
+    assert call(geom=geom(dk=96, dv=96)) == V.VX_ERR_UNSUPPORTED
+    assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
+    big = V.make_pages(1, 16, 20000, 17000, 17000, BAD, BAD, BAD)
+    assert call(pages=big) == V.VX_ERR_UNSUPPORTED
+    # an empty batch launches nothing
+    e = V.make_pages(0, 16, 0, 0, 0, None, None, None)
+    assert call(pages=e, q=None, k_pool=None, centroids=None, scores=None, sel=None,
+                count=None) == V.VX_OK

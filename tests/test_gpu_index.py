@@ -1,0 +1,150 @@
+"""The fused indexer (vx_index_pages) against the separate calls it stands
+for: newest-page refresh (vx_centroid_update, first token -1), scores
+(vx_page_scores) and selection (vx_topk_pages) must give the same bits, in
+both top-k modes, for every geometry; and the whole step through it must
+match the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import vx_testlib as T
+from sparse_attention_decode_amd import binding as V
+from sparse_attention_decode_amd import workloads as W
+from sparse_attention_decode_amd.step import DecodeStep
+from test_gpu_edges import on_gpu
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def used_pages(w):
+    return torch.from_numpy(w.page_ids.astype(np.int64)).to(w.device)
+
+
+def valid_entries(w):
+    """Page-table entries holding at least one token."""
+    m = np.zeros(w.nnz, dtype=bool)
+    for b in range(w.batch):
+        lo = int(w.indptr[b])
+        m[lo:lo + w.n_pages(b)] = True
+    return torch.from_numpy(m).to(w.device)
+
+
+def fused_vs_separate(w, mode=V.VX_TOPK_EXACT, appends=1, **kw):
+    """Grow every sequence by `appends` tokens; after each, run the separate
+    calls on one set of buffers and the fused call on another; compare."""
+    sep = DecodeStep(w, mode=mode, fused=False, **kw)
+    fus = DecodeStep(w, mode=mode, fused=True, **kw)
+    sep.rebuild_centroids()
+    fus.rebuild_centroids()
+    used, valid = used_pages(w), valid_entries(w)
+    for _ in range(appends):
+        if appends > 1 or w.spec.headroom_tokens > 0:
+            w.append_token()
+            valid = valid_entries(w)
+        sep.refresh_centroids()
+        sep.score()
+        sep.select()
+        fus.index()
+        T.sync()
+        assert torch.equal(sep.centroids[used], fus.centroids[used])
+        if w.spec.mla:
+            assert torch.equal(sep.cent_bf16[used], fus.cent_bf16[used])
+        assert torch.equal(sep.scores[:, valid], fus.scores[:, valid])
+        assert torch.equal(sep.sel_count, fus.sel_count)
+        assert torch.equal(sep.sel, fus.sel)
+    return sep, fus
+
+
+@pytest.mark.parametrize("mode", [V.VX_TOPK_EXACT, V.VX_TOPK_APPROX])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_fused_equals_separate(name, mode):
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=11))
+    fused_vs_separate(w, mode=mode, appends=3)
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "longgen_bf16", "largebatch_bf16", "mla_bf16"])
+def test_full_size_fused_equals_separate(name):
+    w = W.make(W.spec(name, headroom_tokens=max(64, W.spec(name).headroom_tokens)), "cuda", seed=1)
+    fused_vs_separate(w, appends=2)
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_large_capacity():
+    """Page capacities in the thousands (one sequence of 30000 tokens among
+    short ones): same bits as the separate calls, and the oracle."""
+    sp = W.spec("gqa_bf16", batch=3, num_q_heads=4, num_kv_heads=2,
+                lengths=("list", (3000, 30000, 70)), headroom_tokens=16000)
+    w = W.make(sp, "cuda", seed=12)
+    assert w.max_pages > 2500
+    fused_vs_separate(w, appends=2)
+    step = DecodeStep(w)
+    step.rebuild_centroids()
+    step.run()
+    T.sync()
+    check_step_against_oracle(w, step, range(3))
+
+
+def check_step_against_oracle(w, step, sample):
+    out = step.out.cpu().double().numpy()
+    lse = step.lse.cpu().double().numpy()
+    G = w.spec.num_q_heads // w.spec.num_kv_heads
+    differing = 0
+    for b in sample:
+        r = T.oracle_seq(w, step, b)
+        T.check_centroids(w, step, b, r)
+        T.check_scores(w, step, b, r)
+        for g, ok in enumerate(T.check_selection(w, step, b, r)):
+            if ok:
+                T.check_attention(w, out[b], lse[b], r["out"], r["lse"],
+                                  heads=range(g * G, (g + 1) * G), tag=f"b={b} g={g}")
+            else:
+                differing += 1
+    return differing
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_step_matches_oracle(name):
+    """run(): fused indexer then attention, after appends, against the oracle."""
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=20), "cpu", seed=13))
+    step = DecodeStep(w)
+    step.rebuild_centroids()
+    for _ in range(5):
+        w.append_token()
+        step.run()
+    T.sync()
+    differing = check_step_against_oracle(w, step, range(w.batch))
+    assert differing <= max(1, w.batch * w.spec.num_kv_heads // 20)
+
+
+@pytest.mark.parametrize("headroom", [0, 16])
+@pytest.mark.parametrize("base", ["gqa_bf16", "mla_bf16", "tiny_fp32"])
+def test_idle_slots(base, headroom):
+    """seq_lens 0 (with and without page capacity): empty selection, zero
+    output, lse -inf; the other sequences are unaffected."""
+    lens = (0, 40, 0, 0, 333, 0) if base != "tiny_fp32" else (0, 0, 500)
+    sp = W.spec(base, batch=len(lens), lengths=("list", lens), headroom_tokens=headroom,
+                pool=("factor", 1.5))
+    w = on_gpu(W.make(sp, "cpu", seed=14))
+    for fused in (False, True):
+        step = DecodeStep(w, fused=fused)
+        step.sel.fill_(7)
+        step.sel_count.fill_(7)
+        step.out.fill_(1.0)
+        step.rebuild_centroids()
+        if fused:
+            step.index(refresh=False)
+        else:
+            step.score()
+            step.select()
+        step.attend()
+        T.sync()
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert (step.sel_count[b] == 0).all()
+                assert (step.sel[b] == -1).all()
+                assert (step.out[b] == 0).all()
+                assert torch.isneginf(step.lse[b]).all()
+        assert check_step_against_oracle(w, step, [b for b, L in enumerate(lens) if L]) == 0
