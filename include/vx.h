@@ -8,6 +8,7 @@
  *   indexer        query x centroid scores                    -> vx_page_scores
  *                  top-k pages per (sequence, KV head)        -> vx_topk_pages
  *                  both, fused with the newest-page refresh   -> vx_index_pages
+ *   whole step     indexer + attention, fused where possible  -> vx_decode_step
  *   attention      exact softmax over the selected pages      -> vx_sparse_decode
  * Section "System design > 2. vTensor" gives the paged layout (a tensor with
  * batch size, a pointer array and a page-index structure): vx_pages below.
@@ -113,6 +114,7 @@ typedef struct vx_plan {
   int32_t score_blocks;
   int32_t topk_threads;      /* threads per (sequence, KV head) segment */
   int32_t num_cus;
+  int32_t fused_step;        /* 1: vx_decode_step runs as one kernel */
   size_t workspace_bytes;    /* what vx_sparse_decode needs for this plan */
 } vx_plan;
 
@@ -220,6 +222,30 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom,
                            float sm_scale, float* out, float* lse,
                            int32_t num_splits, void* workspace,
                            size_t* workspace_bytes, hipStream_t stream);
+
+/* The whole decode step (Vortex paper note, "System design > 1. vFlow":
+ * cache stage, indexer, sparse attention; "System design > 3. Execution
+ * backend": sequence-local fusion). Writes the same bits as vx_index_pages
+ * followed by vx_sparse_decode with the same arguments (the latter's sel /
+ * sel_count being the former's outputs). When the plan has one split per
+ * (sequence, KV head) and the geometry is GQA, bf16, Dk = 128 with
+ * sel_stride <= 128 and max_pages <= 4096, it is one kernel with a block per
+ * (sequence, KV head) that indexes and then attends over its own selection;
+ * otherwise the two calls' kernels run in turn.
+ * workspace == NULL: writes the bytes needed to *workspace_bytes (those of
+ * vx_sparse_decode) and returns VX_OK; otherwise *workspace_bytes must be at
+ * least that. */
+vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom,
+                         const void* q, const void* k_pool,
+                         const void* v_pool, float* centroids,
+                         void* cent_bf16, int32_t refresh_newest,
+                         float score_scale, float sm_scale, int32_t k,
+                         int32_t n_sink, int32_t n_local, int32_t mode,
+                         const uint32_t* rand_u32, float* scores,
+                         int32_t* sel, int32_t sel_stride,
+                         int32_t* sel_count, float* out, float* lse,
+                         int32_t num_splits, void* workspace,
+                         size_t* workspace_bytes, hipStream_t stream);
 
 /* Workload planner (Vortex paper note, "System design > 3. Execution
  * backend": plan by batch size, sequence length, layout and operator).

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
     "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-    "vx_sparse_decode", "vx_plan_decode", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
+    "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
 
@@ -25,7 +25,7 @@ VX_OK, VX_ERR_INVALID_ARG, VX_ERR_UNSUPPORTED, VX_ERR_WORKSPACE, VX_ERR_HIP = ra
 VX_F32, VX_BF16 = 0, 1
 VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
 ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-                "vx_sparse_decode", "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
+                "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
 
@@ -51,7 +51,8 @@ class VxGeom(ctypes.Structure):
 class VxPlan(ctypes.Structure):
     _fields_ = [("num_splits", c_int32), ("pages_per_split", c_int32),
                 ("score_pages_per_block", c_int32), ("score_blocks", c_int32),
-                ("topk_threads", c_int32), ("num_cus", c_int32), ("workspace_bytes", c_size_t)]
+                ("topk_threads", c_int32), ("num_cus", c_int32), ("fused_step", c_int32),
+                ("workspace_bytes", c_size_t)]
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -83,9 +84,13 @@ def load() -> ctypes.CDLL:
     lib.vx_sparse_decode.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                      c_void_p, c_float, c_void_p, c_void_p, c_int32, c_void_p,
                                      POINTER(c_size_t), c_void_p]
+    lib.vx_decode_step.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                   c_float, c_float, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                   c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                   c_int32, c_void_p, POINTER(c_size_t), c_void_p]
     lib.vx_plan_decode.argtypes = [P, G, c_int32, c_int32, c_int32, POINTER(VxPlan)]
     for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-                 "vx_sparse_decode", "vx_plan_decode"):
+                 "vx_sparse_decode", "vx_decode_step", "vx_plan_decode"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -185,6 +190,22 @@ def vx_sparse_decode(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, sel, sel_s
                                    _ptr(v_pool), _ptr(sel), sel_stride, _ptr(sel_count),
                                    float(sm_scale), _ptr(out), _ptr(lse), num_splits,
                                    _ptr(workspace), ctypes.byref(nbytes), _stream(stream)))
+    return nbytes.value
+
+
+def vx_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, centroids, cent_bf16,
+                   refresh_newest: bool, score_scale: float, sm_scale: float, k: int, n_sink: int,
+                   n_local: int, mode: int, rand_u32, scores, sel, sel_stride: int, sel_count, out,
+                   lse, num_splits: int = 0, workspace=None, workspace_bytes: Optional[int] = None,
+                   stream=None) -> int:
+    """Indexer + attention; with workspace=None only returns the bytes needed."""
+    nbytes = _nbytes(workspace, workspace_bytes)
+    _check(load().vx_decode_step(ctypes.byref(pages), ctypes.byref(geom), _ptr(q), _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(centroids), _ptr(cent_bf16),
+                                 int(refresh_newest), float(score_scale), float(sm_scale), k,
+                                 n_sink, n_local, mode, _ptr(rand_u32), _ptr(scores), _ptr(sel),
+                                 sel_stride, _ptr(sel_count), _ptr(out), _ptr(lse), num_splits,
+                                 _ptr(workspace), ctypes.byref(nbytes), _stream(stream)))
     return nbytes.value
 
 

@@ -19,17 +19,13 @@
 // its own online-softmax state (m, l, o) for the tokens it holds, so V needs
 // no cross-lane traffic. Rows merge inside the wave, waves merge in LDS, and
 // splits (if any) merge in merge_kernel. Logits are in log2 units.
-#include "vx_internal.h"
+#include "attn_mfma.h"
 
 namespace vx {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename KV> struct KVTraits;
 template <> struct KVTraits<float> {
@@ -60,7 +56,7 @@ constexpr int kWaves = VX_ATTN_WAVES;  // waves per attention block
 #ifndef VX_ATTN_BATCH
 #define VX_ATTN_BATCH 1
 #endif
-constexpr int kBatch = VX_ATTN_BATCH;  // chunks in flight per wave (MFMA kernel)
+constexpr int kBatch = VX_ATTN_BATCH;  // chunks in flight per wave (vector kernel, short rows)
 
 template <typename QT, typename KV, int G, int DK, int P>
 __global__ __launch_bounds__(64 * kWaves) void attn_gqa_kernel(
@@ -79,6 +75,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_gqa_kernel(
   constexpr bool kDot2 = sizeof(KV) == 2 && sizeof(QT) == 2;
   static_assert(64 % LPR == 0 && CT % TPI == 0 && P % CT == 0, "layout");
 
+  static_assert(kMaxPagesPerSplit <= 64 * kWaves, "one page-list entry per thread");
   __shared__ int pg_phys[kMaxPagesPerSplit];
   __shared__ int pg_nv[kMaxPagesPerSplit];
   __shared__ float red_o[kWaves][G][DK];
@@ -291,54 +288,21 @@ __global__ __launch_bounds__(64 * kWaves) void attn_gqa_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16, Dk = Dv = 128: the group's query heads (G <= 16, padded to 16 rows)
-// against each 16-token chunk on the matrix cores.
-//   q.k^T  v_mfma_f32_16x16x32_bf16: A = query rows (lane: head l%16, dims
-//          8 q4 + 32 ks..), B = key rows straight from HBM (lane: token l%16,
-//          the same dims) -> S[head 4 q4 + i][token l%16].
-//   P.V    v_mfma_f32_16x16x16_bf16: lane (q4, c) loads tokens 4 q4 .. 4 q4+3,
-//          dims 8 c .. 8 c+7 (four 16-byte loads, whole 256-byte rows per
-//          instruction). Taking N-tile e's columns as dims {8 c + e}, the B
-//          fragment is element e of the lane's four rows; P reaches the A
-//          layout (head l%16, tokens 4 q4..) through a 16x16 LDS tile.
-//   -> O[head 4 q4 + i][dim 8 c + e] in accumulator e.
-// Vector work per chunk is the online softmax only.
-constexpr int kPRow = 20;  // padded row of a wave's P tile (bf16)
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ uint32_t elem16(const u32x4& v, int e) {
-  const uint32_t wv = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (wv >> 16) : (wv & 0xffffu);
-}
-
+// The bf16, Dk = Dv = 128 path on the matrix cores: mfma_attend in attn_mfma.h.
 template <int G, int P>
 __global__ __launch_bounds__(64 * kWaves) void attn_gqa_mfma_kernel(
     Meta m, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ sel, int stride,
     const int32_t* __restrict__ sel_count, float qscale, int S, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int DK = 128;
-  constexpr int CT = 16;
-  constexpr int CPP = P / CT;
-  static_assert(G >= 1 && G <= 16, "group");
-
+  static_assert(kMaxPagesPerSplit <= 64 * kWaves, "one page-list entry per thread");
   __shared__ int pg_phys[kMaxPagesPerSplit];
   __shared__ int pg_nv[kMaxPagesPerSplit];
-  __shared__ float red_o[kWaves][G][DK];
-  __shared__ float red_ml[kWaves][G][2];
-  __shared__ __attribute__((aligned(16))) uint16_t ptile[kWaves][16 * kPRow];
+  __shared__ MfmaShared<G, kWaves> sm;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 15, q4 = lane >> 4;
-  const int hq = hkv * G;
   const int item = blockIdx.x;
   const int s = item % S, bg = item / S;
   const int b = bg / hkv, g = bg % hkv;
-
   const int L = seq_len_clamped(m, b);
   const int cap = m.indptr[b + 1] - m.indptr[b];
   const int count = cap > 0 ? min(sel_count[bg], stride) : 0;
@@ -351,140 +315,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_gqa_mfma_kernel(
     pg_phys[threadIdx.x] = phys_page(m, m.indptr[b] + lp);
     pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
   }
-
-  // A operand of q.k^T: head row `col` (zero past the group), dims 32 ks + 8 q4.
-  u32x4 qa[DK / 32];
-  {
-    const bool real = col < G;
-    const uint16_t* qh = q + ((size_t)b * hq + g * G + (real ? col : 0)) * DK + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks)
-      qa[ks] = real ? *(const u32x4*)(qh + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-  }
-  f32x4 o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { mrow[i] = kNegBig; lrow[i] = 0.f; }
-  uint16_t* pw = ptile[w];
+  u32x4 qa[4];
+  mfma_load_q<G>(q, b, g, hkv, qa);
   __syncthreads();  // page list ready
-
-  const int nchunks = np * CPP;
-  const size_t head_stride = (size_t)P * DK;
-  auto chunk_nv = [&](int c) { return pg_nv[c / CPP] - (c % CPP) * CT; };
-  auto load_chunk = [&](int c, u32x4* kr, u32x4* vr) {
-    const size_t base = ((size_t)pg_phys[c / CPP] * hkv + g) * head_stride + (size_t)(c % CPP) * CT * DK;
-    const uint16_t* kc = kp + base + (size_t)col * DK + 8 * q4;
-    const uint16_t* vc = vp + base + (size_t)(4 * q4) * DK + 8 * col;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) kr[ks] = __builtin_nontemporal_load((const u32x4*)(kc + 32 * ks));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = __builtin_nontemporal_load((const u32x4*)(vc + r * DK));
-  };
-  auto consume = [&](int c, const u32x4* kr, const u32x4* vr) {
-    const int nvc = chunk_nv(c);
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[ks]),
-                                                     __builtin_bit_cast(bf16x8_t, kr[ks]), sacc,
-                                                     0, 0, 0);
-    const bool tok_ok = col < nvc;
-    float alpha[4];
-    bool grow = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float z = tok_ok ? sacc[i] * qscale : -INFINITY;
-      const float mnew = fmaxf(mrow[i], group_max<16>(z));
-      alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mnew);
-      grow = grow || (mnew > mrow[i]);
-      const float pv = __builtin_amdgcn_exp2f(z - mnew);
-      lrow[i] = fmaf(lrow[i], alpha[i], group_sum<16>(pv));
-      mrow[i] = mnew;
-      pw[(4 * q4 + i) * kPRow + col] = f32_to_bf16(pv);
-    }
-    if (__ballot(grow)) {  // rescale only when some row's maximum moved
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[e][i] *= alpha[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint2 pa = *(const uint2*)(pw + col * kPRow + 4 * q4);
-    u32x4 v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = (4 * q4 + r < nvc) ? vr[r] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t b01 = elem16(v[0], e) | (elem16(v[1], e) << 16);
-      const uint32_t b23 = elem16(v[2], e) | (elem16(v[3], e) << 16);
-      o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(bf16x4_t, pa), __builtin_bit_cast(bf16x4_t, uint2{b01, b23}), o[e],
-          0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();  // P tile reads done before the next chunk writes it
-  };
-
-  // Batches of kBatch chunks: all loads of a batch are issued, then the
-  // batch is consumed. No load register lives across iterations, so nothing
-  // forces the compiler to copy (and wait on) in-flight registers.
-  const int my_n = nchunks > w ? (nchunks - w + kWaves - 1) / kWaves : 0;
-  for (int j0 = 0; j0 < my_n; j0 += kBatch) {
-    u32x4 kr[kBatch][DK / 32], vr[kBatch][4];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)  // unconditional: a short last batch re-reads a chunk
-      load_chunk(w + min(j0 + u, my_n - 1) * kWaves, kr[u], vr[u]);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (j0 + u < my_n) consume(w + (j0 + u) * kWaves, kr[u], vr[u]);
-  }
-
-  // Per-wave results of the group's heads to LDS, then merge the waves.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * q4 + i;
-    if (h < G) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_o[w][h][8 * col + e] = o[e][i];
-      if (col == 0) {
-        red_ml[w][h][0] = mrow[i];
-        red_ml[w][h][1] = lrow[i];
-      }
-    }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < G * DK / 4; t += blockDim.x) {
-    const int h = t / (DK / 4), d = (t % (DK / 4)) * 4;
-    float mmax = kNegBig;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) mmax = fmaxf(mmax, red_ml[v][h][0]);
-    float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float wt = __builtin_amdgcn_exp2f(red_ml[v][h][0] - mmax);
-      lsum = fmaf(red_ml[v][h][1], wt, lsum);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(red_o[v][h][d + e], wt, acc[e]);
-    }
-    const int head = g * G + h;
-    if (S == 1) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      *(float4*)(out + ((size_t)b * hq + head) * DK + d) =
-          make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-      if (lse && d == 0)
-        lse[(size_t)b * hq + head] = lsum > 0.f ? (mmax + log2f(lsum)) * kLn2 : -INFINITY;
-    } else {
-      const size_t ps = ((size_t)b * hq + head) * S + s;
-      *(float4*)(part_o + ps * DK + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      if (d == 0) {
-        part_ml[2 * ps] = mmax;
-        part_ml[2 * ps + 1] = lsum;
-      }
-    }
-  }
+  mfma_attend<G, P, kWaves>(sm, pg_phys, pg_nv, np, b, g, hkv, qa, kp, vp, qscale, S, s, out, lse,
+                            part_o, part_ml);
 }
 
 // out[b][h] = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m).

@@ -1,0 +1,121 @@
+// The whole decode step for one (sequence, KV head) segment in one block:
+// indexer (newest-page refresh, scores, top-k) then exact attention over the
+// chosen pages. GQA, bf16, Dk = Dv = 128, one split per segment.
+//
+// Vortex paper note, "System design > 1. vFlow": cache stage, indexer and
+// sparse attention form the step; "System design > 3. Execution backend":
+// sequence-local operators are fused greedily. The selection of a segment
+// feeds only that segment's attention, so a block that has just selected
+// can attend at once: the chosen ids and the physical page of every entry
+// are already in its LDS (no kernel boundary, no reload of the selection or
+// of the page table).
+#include "attn_mfma.h"
+#include "index_seg.h"
+
+namespace vx {
+namespace {
+
+constexpr int kStepWaves = 8;
+
+template <int G, int P>
+__global__ __launch_bounds__(64 * kStepWaves) void decode_seg_kernel(SegArgs a,
+                                                                     const uint16_t* __restrict__ vp,
+                                                                     float qscale,
+                                                                     float* __restrict__ out,
+                                                                     float* __restrict__ lse) {
+  // keys [cap_keys + 256], then the physical page of every entry [cap_keys]
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  __shared__ int32_t sel_l[kMaxPagesPerSplit];
+  __shared__ int32_t cnt_l;
+  __shared__ int pg_phys[kMaxPagesPerSplit];
+  __shared__ int pg_nv[kMaxPagesPerSplit];
+  __shared__ MfmaShared<G, kStepWaves> sm;
+  static_assert(kMaxPagesPerSplit <= 64 * kStepWaves, "one page-list entry per thread");
+
+  const int seg = blockIdx.x;
+  int* pid_l = (int*)(dyn + a.cap_keys + 256);
+  index_segment<uint16_t, uint16_t, 128, G, kStepWaves>(a, seg, dyn, pid_l, sel_l, &cnt_l);
+
+  const Meta& m = a.m;
+  const int b = seg / a.hkv, g = seg % a.hkv;
+  u32x4 qa[4];
+  mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
+  __syncthreads();  // selection and page ids visible to the block
+  const int count = min(cnt_l, kMaxPagesPerSplit);
+  const int L = seq_len_clamped(m, b);
+  if ((int)threadIdx.x < count) {
+    const int lp = sel_l[threadIdx.x];
+    pg_phys[threadIdx.x] = pid_l[lp];
+    pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
+  }
+  __syncthreads();  // page list ready
+  mfma_attend<G, P, kStepWaves>(sm, pg_phys, pg_nv, count, b, g, a.hkv, qa,
+                                (const uint16_t*)a.kp, vp, qscale, 1, 0, out, lse, nullptr,
+                                nullptr);
+}
+
+template <int P>
+hipError_t launch_p(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
+                    hipStream_t s) {
+  dim3 grid(a.m.batch * a.hkv), block(64 * kStepWaves);
+  const size_t lds = (size_t)(2 * a.cap_keys + 256) * sizeof(uint32_t);
+#define VX_STEP(GG)                                                                             \
+  case GG:                                                                                      \
+    hipLaunchKernelGGL((decode_seg_kernel<GG, P>), grid, block, lds, s, a,                     \
+                       (const uint16_t*)v_pool, qscale, out, lse);                              \
+    break;
+  switch (a.hq / a.hkv) {
+    VX_STEP(1)
+    VX_STEP(2)
+    VX_STEP(4)
+    VX_STEP(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef VX_STEP
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_step_fusable(const vx_geom& g, int page_size, int max_pages, int sel_stride) {
+  const int G = g.num_q_heads / g.num_kv_heads;
+  return !g.mla && g.kv_dtype == VX_BF16 && g.q_dtype == VX_BF16 && g.head_dim_k == 128 &&
+         (G == 1 || G == 2 || G == 4 || G == 8) && (page_size == 16 || page_size == 64) &&
+         max_pages <= kMaxFusedStepPages && sel_stride <= kMaxPagesPerSplit;
+}
+
+hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q,
+                                  const void* k_pool, const void* v_pool, float* cent,
+                                  uint16_t* cent_bf16, int refresh, float score_scale,
+                                  float sm_scale, float* scores, int k, int n_sink, int n_local,
+                                  int mode, const uint32_t* rnd, int32_t* sel, int stride,
+                                  int32_t* sel_count, float* out, float* lse, int max_pages,
+                                  hipStream_t s) {
+  if (m.batch == 0) return hipSuccess;
+  SegArgs a{};
+  a.m = m;
+  a.hq = g.num_q_heads;
+  a.hkv = g.num_kv_heads;
+  a.q = q;
+  a.kp = k_pool;
+  a.cent = cent;
+  a.cent_bf16 = cent_bf16;
+  a.refresh = refresh;
+  a.scale = score_scale;
+  a.scores = scores;
+  a.k = k;
+  a.n_sink = n_sink;
+  a.n_local = n_local;
+  a.mode = mode;
+  a.rnd = rnd;
+  a.sel = sel;
+  a.stride = stride;
+  a.sel_count = sel_count;
+  a.cap_keys = (max_pages + 63) / 64 * 64;
+  const float qscale = sm_scale * kLog2e;
+  if (m.page_size == 16) return launch_p<16>(a, v_pool, qscale, out, lse, s);
+  return launch_p<64>(a, v_pool, qscale, out, lse, s);
+}
+
+}  // namespace vx

@@ -1,165 +1,19 @@
-// Indexer, GQA geometry, fused per (sequence, KV head): cache refresh of the
-// newest page, page scores and the top-k selection in one kernel.
-//
-// Vortex paper note, "System design > 1. vFlow": the indexer multiplies the
-// query with the cached centroids and keeps the top-k blocks; "System design
-// > 3. Execution backend": sequence-local operators are fused greedily, and
-// the radix top-k serves the selection.
-//
-// One block per segment (sequence b, KV head g). Everything the selection
-// needs is local to the segment, so no block waits for another: the block
-// streams the 4*Dk-byte slice of head g from every centroid row of b, keeps
-// the scores as radix keys in LDS, and its first wave selects from them.
-//   - Rows: the waves split b's pages into contiguous ranges; per chunk of
-//     16 load instructions a wave loads the chunk's page ids (one per lane),
-//     then all the chunk's row slices (64/W pages per instruction, W = Dk/4
-//     lanes per slice, 16 bytes per lane), so every load is in flight at once.
-//   - Scores: the same arithmetic as the flat scorer (group-summed query,
-//     4 products per lane, then a W-lane DPP sum), so the bits are equal.
-//   - Refresh (optional): the last wave recomputes the newest page's slice
-//     from its keys (fp32, token order, one IEEE divide: the cache stage's
-//     arithmetic) with up to 32 tokens in flight per lane, writes it back and
-//     scores it.
-#include "topk_wave.h"
+// Indexer kernel, GQA geometry: one block per (sequence, KV head) segment
+// runs index_segment (index_seg.h): newest-page refresh, scores, top-k.
+#include "index_seg.h"
 
 namespace vx {
 namespace {
 
-constexpr int kSegWaves = 8;    // waves per block
-constexpr int kChunkInstr = 16; // row loads in flight per lane
-
-struct SegArgs {
-  Meta m;
-  int hq, hkv;
-  const void* q;
-  const void* kp;
-  float* cent;
-  uint16_t* cent_bf16;
-  int refresh;
-  float scale;
-  float* scores;
-  int k, n_sink, n_local, mode;
-  const uint32_t* rnd;
-  int32_t* sel;
-  int stride;
-  int32_t* sel_count;
-  int cap_keys;
-};
+#ifndef VX_SEG_WAVES
+#define VX_SEG_WAVES 8
+#endif
+constexpr int kSegWaves = VX_SEG_WAVES;  // waves per block
 
 template <typename QT, typename KV, int DK, int GG>
 __global__ __launch_bounds__(64 * kSegWaves) void index_seg_kernel(SegArgs a) {
-  constexpr int W = DK / 4;    // lanes per row slice
-  constexpr int PPI = 64 / W;  // pages per load instruction
-  constexpr int kChunk = kChunkInstr * PPI;
-  extern __shared__ uint32_t keys[];  // [cap_keys] keys, then 256 histogram words
-
-  const Meta& m = a.m;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int seg = blockIdx.x;
-  const int b = seg / a.hkv, g = seg % a.hkv;
-  const int P = m.page_size;
-  const int row0 = m.indptr[b];
-  const int cap = m.indptr[b + 1] - row0;
-  const int L = min(max(m.seq_lens[b], 0), cap * P);
-  const int n = min(min((L + P - 1) / P, cap), a.cap_keys);
-  const int G = GG > 0 ? GG : a.hq / a.hkv;
-  const int sub = lane / W, dl = lane % W;
-
-  // Scaled group sum of the query for this lane's 4 dims of head g.
-  float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
-  {
-    const QT* qb = (const QT*)a.q + ((size_t)b * a.hq + (size_t)g * G) * DK + 4 * dl;
-    if constexpr (GG > 0) {
-      typename Quad<QT>::raw x[GG];
-#pragma unroll
-      for (int h = 0; h < GG; ++h) x[h] = Quad<QT>::load(qb + (size_t)h * DK);
-#pragma unroll
-      for (int h = 0; h < GG; ++h) {
-        const float4 v = Quad<QT>::widen(x[h]);
-        qs.x += v.x; qs.y += v.y; qs.z += v.z; qs.w += v.w;
-      }
-    } else {
-      for (int h = 0; h < G; ++h) {
-        const float4 v = Quad<QT>::widen(Quad<QT>::load(qb + (size_t)h * DK));
-        qs.x += v.x; qs.y += v.y; qs.z += v.z; qs.w += v.w;
-      }
-    }
-    qs = make_float4(qs.x * a.scale, qs.y * a.scale, qs.z * a.scale, qs.w * a.scale);
-  }
-  const bool refresh = a.refresh && n > 0;
-  const int nrow = refresh ? n - 1 : n;  // pages scored from their stored rows
-  const int rw = refresh ? kSegWaves - 1 : kSegWaves;
-  float* scores = a.scores + (size_t)g * m.nnz + row0;
-
-  auto emit = [&](int p, float4 r, bool ok) {
-    float sc = qs.x * r.x;
-    sc = fmaf(qs.y, r.y, sc);
-    sc = fmaf(qs.z, r.z, sc);
-    sc = fmaf(qs.w, r.w, sc);
-    sc = group_sum<W>(sc);
-    if (ok && dl == 0) {
-      scores[p] = sc;
-      keys[p] = (p < a.n_sink || p >= n - a.n_local) ? 0u : topk_detail::score_key(sc);
-    }
-  };
-
-  if (w < rw) {
-    const int pw0 = (int)(((long)nrow * w) / rw), pw1 = (int)(((long)nrow * (w + 1)) / rw);
-    for (int cb = pw0; cb < pw1; cb += kChunk) {
-      const int my_pid = cb + lane < pw1 && lane < kChunk ? phys_page(m, row0 + cb + lane) : 0;
-      float4 r[kChunkInstr];
-#pragma unroll
-      for (int t = 0; t < kChunkInstr; ++t) {
-        const int p = cb + t * PPI + sub;
-        const int pid = __shfl(my_pid, t * PPI + sub);
-        r[t] = p < pw1 ? *(const float4*)(a.cent + ((size_t)pid * a.hkv + g) * DK + 4 * dl)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int t = 0; t < kChunkInstr; ++t) {
-        const int p = cb + t * PPI + sub;
-        emit(p, r[t], p < pw1);
-      }
-    }
-  } else if (refresh) {
-    // Newest page n-1: lanes 0..W-1 own 4 dims each and sum its tokens in order.
-    const int p = n - 1;
-    const int nv = min(P, L - p * P);
-    const int pid = phys_page(m, row0 + p);
-    const bool own = sub == 0;
-    const KV* col = (const KV*)a.kp + ((size_t)pid * a.hkv + g) * P * DK + 4 * dl;
-    constexpr int kTok = sizeof(KV) == 2 ? 32 : 16;
-    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t0 = 0; t0 < nv; t0 += kTok) {
-      typename Quad<KV>::raw x[kTok];
-#pragma unroll
-      for (int t = 0; t < kTok; ++t)
-        if (own && t0 + t < nv) x[t] = Quad<KV>::load(col + (size_t)(t0 + t) * DK);
-#pragma unroll
-      for (int t = 0; t < kTok; ++t)
-        if (own && t0 + t < nv) {
-          const float4 v = Quad<KV>::widen(x[t]);
-          s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
-        }
-    }
-    const float fn = (float)nv;
-    const float4 c4 = make_float4(s4.x / fn, s4.y / fn, s4.z / fn, s4.w / fn);
-    if (own) {
-      const size_t o = ((size_t)pid * a.hkv + g) * DK + 4 * dl;
-      *(float4*)(a.cent + o) = c4;
-      if (a.cent_bf16) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(c4.x) | ((uint32_t)f32_to_bf16(c4.y) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(c4.z) | ((uint32_t)f32_to_bf16(c4.w) << 16);
-        *(uint2*)(a.cent_bf16 + o) = make_uint2(lo, hi);
-      }
-    }
-    emit(p, c4, own);
-  }
-  __syncthreads();  // every key of the segment is in LDS
-  if (w == 0)
-    wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode,
-                     a.mode == VX_TOPK_APPROX ? a.rnd[seg] : 0u, a.sel + (size_t)seg * a.stride,
-                     a.stride, a.sel_count + seg, lane);
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // cap_keys + 256 words
+  index_segment<QT, KV, DK, GG, kSegWaves>(a, blockIdx.x, keys, nullptr, nullptr, nullptr);
 }
 
 template <typename QT, typename KV, int DK>

@@ -22,13 +22,9 @@ constexpr int DK = 576;
 constexpr int DV = 512;
 constexpr int KSTEPS = DK / 32;   // 18
 constexpr int ROW = DK + 8;       // padded LDS row (bf16), 1168 B: 16-B aligned
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegBig = -1.0e30f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -141,6 +137,7 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
   const int np = min((int)(((long)count * (s + 1)) / S) - p0, kMaxPagesPerSplit);
   const int P = m.page_size;
 
+  static_assert(kMaxPagesPerSplit <= 256, "one page-list entry per thread");
   if (t < np) {
     int lp = sel[(size_t)b * stride + p0 + t];
     lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);

@@ -12,7 +12,7 @@ __global__ __launch_bounds__(256) void topk_kernel(Meta m, int hkv, const float*
                                                    const uint32_t* __restrict__ rnd,
                                                    int32_t* __restrict__ sel, int stride,
                                                    int32_t* __restrict__ sel_count, int cap_keys) {
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int seg = blockIdx.x * (blockDim.x >> 6) + w;

@@ -6,11 +6,12 @@
 // early termination and remapping) when recall can be traded for time.
 //
 // One wave per segment. Scores become order-preserving 32-bit keys in LDS
-// (forced pages get key 0 and never compete). Exact mode runs up to four
-// 8-bit digit passes, most significant first: an LDS histogram of the digit
-// among keys that still match the chosen prefix, a suffix scan across the
-// wave to find the digit where the count from the top reaches the remaining
-// need r, and an early exit when that bucket holds exactly r keys. The
+// (forced pages get key 0 and never compete). Exact mode runs 8-bit digit
+// passes, most significant first, starting at the first byte where the
+// smallest and largest candidate keys differ: an LDS histogram of the digit
+// among keys that still match the chosen prefix, a DPP scan across the wave
+// to find the digit where the count from the top reaches the remaining need
+// r, and an early exit when that bucket holds exactly r keys. The
 // survivors are then compacted in index order with ballot + mbcnt prefix
 // sums, which yields ascending page ids and the lower-index tie-break.
 // Approximate mode maps candidate scores affinely onto 256 buckets, runs one
@@ -45,14 +46,35 @@ __device__ __forceinline__ uint32_t rank_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Suffix scan over lanes: lane l gets sum_{l' >= l} x(l').
-__device__ __forceinline__ uint32_t suffix_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t y = __shfl_down(x, off);
-    if (lane + off < 64) x += y;
-  }
+// DPP move of a 32-bit value; a lane without a source (or outside ROW_MASK)
+// reads 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp0(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, true);
+}
+
+// Inclusive prefix sum over the wave (lane l: sum over lanes <= l): shifts by
+// 1, 2, 4 and 8 inside rows of 16 lanes, then each row total broadcast to the
+// rows above it (row_bcast:15 into rows 1 and 3, row_bcast:31 into 2 and 3).
+__device__ __forceinline__ uint32_t prefix_sum(uint32_t x) {
+  x += dpp0<0x111, 0xf>(x);
+  x += dpp0<0x112, 0xf>(x);
+  x += dpp0<0x114, 0xf>(x);
+  x += dpp0<0x118, 0xf>(x);
+  x += dpp0<0x142, 0xa>(x);
+  x += dpp0<0x143, 0xc>(x);
   return x;
+}
+
+// Maximum over the wave (0 is the identity), same lane pattern.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp0<0x111, 0xf>(x));
+  x = max(x, dpp0<0x112, 0xf>(x));
+  x = max(x, dpp0<0x114, 0xf>(x));
+  x = max(x, dpp0<0x118, 0xf>(x));
+  x = max(x, dpp0<0x142, 0xa>(x));
+  x = max(x, dpp0<0x143, 0xc>(x));
+  return __builtin_amdgcn_readlane(x, 63);
 }
 
 struct Digit {
@@ -62,23 +84,26 @@ struct Digit {
 };
 
 // Find the bucket where the count from the top first reaches r (1 <= r <= total).
+// Lane l holds buckets 4l .. 4l+3; the count of keys in buckets >= 4l is the
+// wave total minus the exclusive prefix sum.
 __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t r, int lane) {
-  const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-  const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-  const uint32_t incl = suffix_scan(h0 + h1 + h2 + h3, lane);  // S(4 lane)
-  const uint32_t s0 = incl, s1 = incl - h0, s2 = s1 - h1, s3 = s2 - h2;  // S(4 lane + i)
+  const uint4 h = *(const uint4*)(hist + 4 * lane);
+  const uint32_t t = h.x + h.y + h.z + h.w;
+  const uint32_t pre = prefix_sum(t);
+  const uint32_t total = __builtin_amdgcn_readlane(pre, 63);
+  const uint32_t s0 = total - pre + t, s1 = s0 - h.x, s2 = s1 - h.y, s3 = s2 - h.z;
   int hit = -1;
   uint32_t hab = 0, hcnt = 0;
-  if (s3 >= r && s3 - h3 < r) { hit = 3; hab = s3 - h3; hcnt = h3; }
-  else if (s2 >= r && s2 - h2 < r) { hit = 2; hab = s2 - h2; hcnt = h2; }
-  else if (s1 >= r && s1 - h1 < r) { hit = 1; hab = s1 - h1; hcnt = h1; }
-  else if (s0 >= r && s0 - h0 < r) { hit = 0; hab = s0 - h0; hcnt = h0; }
+  if (s3 >= r && s3 - h.w < r) { hit = 3; hab = s3 - h.w; hcnt = h.w; }
+  else if (s2 >= r && s2 - h.z < r) { hit = 2; hab = s2 - h.z; hcnt = h.z; }
+  else if (s1 >= r && s1 - h.y < r) { hit = 1; hab = s1 - h.y; hcnt = h.y; }
+  else if (s0 >= r && s0 - h.x < r) { hit = 0; hab = s0 - h.x; hcnt = h.x; }
   const unsigned long long found = __ballot(hit >= 0);
-  const int src = __ffsll((long long)found) - 1;
+  const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)found) - 1);
   Digit out;
-  out.d = (uint32_t)__shfl(4 * lane + hit, src);
-  out.above = (uint32_t)__shfl((int)hab, src);
-  out.count = (uint32_t)__shfl((int)hcnt, src);
+  out.d = (uint32_t)__builtin_amdgcn_readlane(4 * lane + hit, src);
+  out.above = (uint32_t)__builtin_amdgcn_readlane((int)hab, src);
+  out.count = (uint32_t)__builtin_amdgcn_readlane((int)hcnt, src);
   return out;
 }
 
@@ -86,13 +111,15 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t r, in
 
 // Select for one segment whose n keys are already in this wave's LDS
 // (keys[i] = 0 for a forced page, else score_key of its score); `hist` is
-// 256 words of LDS. Writes out[0..stride) and *count_out.
+// 256 words of LDS. Writes out[0..stride) and *count_out, and, when given,
+// the chosen ids to out_lds[0..count) and the count to *count_lds.
 __device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
                                                  uint32_t* __restrict__ hist, int n, int k,
                                                  int n_sink, int n_local, int mode,
                                                  uint32_t rnd_word, int32_t* __restrict__ out,
                                                  int stride, int32_t* __restrict__ count_out,
-                                                 int lane) {
+                                                 int lane, int32_t* __restrict__ out_lds = nullptr,
+                                                 int32_t* __restrict__ count_lds = nullptr) {
   using namespace topk_detail;
   const int nf = min(n, n_sink + n_local);  // forced: a prefix and a suffix of [0, n)
   const int nc = n - nf;
@@ -103,29 +130,27 @@ __device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
   // over the `members` of that tie group).
   uint32_t prefix = 0, mask = 0, r = (uint32_t)kk, off = 0, members = (uint32_t)nc;
   if (kk > 0 && kk < nc) {
+    // smallest and largest candidate key (forced pages hold 0 and are skipped)
+    uint32_t kmax = 0u, kminc = 0u;  // kminc: max of ~key, so min = ~kminc
+    for (int base = 0; base < n; base += 64 * kU) {
+      uint32_t kv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + 64 * u + lane;
+        kv[u] = i < n ? keys[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (kv[u]) { kmax = max(kmax, kv[u]); kminc = max(kminc, ~kv[u]); }
+    }
+    kmax = wave_max(kmax);
+    const uint32_t kmin = ~wave_max(kminc);
     if (mode == VX_TOPK_APPROX) {
-      uint32_t kmin = 0xffffffffu, kmax = 0u;
-      for (int base = 0; base < n; base += 64 * kU) {
-        uint32_t kv[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int i = base + 64 * u + lane;
-          kv[u] = i < n ? keys[i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (kv[u]) { kmin = min(kmin, kv[u]); kmax = max(kmax, kv[u]); }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-      }
       const float mn = key_score(kmin), mx = key_score(kmax);
       const float wdt = __fsub_rn(mx, mn);
       const bool spread = wdt > 0.f;
       const float inv = spread ? __fdiv_rn(256.f, wdt) : 0.f;
-      for (int i = lane; i < 256; i += 64) hist[i] = 0;
+      *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
       wave_sync();
       for (int base = 0; base < n; base += 64 * kU) {
         uint32_t kv[kU];
@@ -155,9 +180,17 @@ __device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
       r -= dg.above;
       members = dg.count;
       off = members ? rnd_word % members : 0u;
+    } else if (kmin == kmax) {
+      prefix = kmin;  // every candidate ties: index order decides
+      mask = 0xffffffffu;
     } else {
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = lane; i < 256; i += 64) hist[i] = 0;
+      // Bytes every candidate shares need no pass: start at the first byte
+      // where the smallest and largest keys differ.
+      const int top = __clz(kmin ^ kmax) / 8;
+      mask = top ? 0xffffffffu << (32 - 8 * top) : 0u;
+      prefix = kmin & mask;
+      for (int shift = 24 - 8 * top; shift >= 0; shift -= 8) {
+        *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
         wave_sync();
         for (int base = 0; base < n; base += 64 * kU) {
           uint32_t kv[kU];
@@ -206,12 +239,18 @@ __device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
     bool take = forced || above;
     if (tie && members) take = take || ((trank + members - off) % members) < r;
     const unsigned long long smask = __ballot(take);
-    if (take) out[written + rank_below(smask)] = i;
+    if (take) {
+      out[written + rank_below(smask)] = i;
+      if (out_lds) out_lds[written + rank_below(smask)] = i;
+    }
     written += (uint32_t)__popcll(smask);
     }
   }
   for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
-  if (lane == 0) *count_out = (int32_t)written;
+  if (lane == 0) {
+    *count_out = (int32_t)written;
+    if (count_lds) *count_lds = (int32_t)written;
+  }
 }
 
 // Select for one segment: `sc` points at its n scores, `keys` / `hist` at

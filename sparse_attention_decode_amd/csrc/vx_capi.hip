@@ -99,6 +99,54 @@ int topk_waves(int max_pages) {
   return wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
 }
 
+vx_status check_index_args(const vx_pages* pages, const vx_geom* geom, const void* q,
+                           const void* k_pool, const float* centroids, const void* cent_bf16,
+                           int32_t refresh_newest, float score_scale, const float* scores,
+                           int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
+                           const uint32_t* rand_u32, const int32_t* sel, int32_t sel_stride,
+                           const int32_t* sel_count) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(refresh_newest == 0 || refresh_newest == 1, VX_ERR_INVALID_ARG,
+           "refresh_newest must be 0 or 1");
+  VX_CHECK(std::isfinite(score_scale), VX_ERR_INVALID_ARG, "score_scale not finite");
+  if ((st = check_topk(pages, k, n_sink, n_local, mode, rand_u32, sel, sel_stride, sel_count)) !=
+      VX_OK)
+    return st;
+  VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
+  VX_CHECK(pages->total_pages == 0 || scores, VX_ERR_INVALID_ARG, "scores is NULL");
+  VX_CHECK(pages->total_pages == 0 || centroids, VX_ERR_INVALID_ARG, "centroids is NULL");
+  VX_CHECK(!geom->mla || pages->total_pages == 0 || cent_bf16, VX_ERR_INVALID_ARG,
+           "MLA scores the bf16 centroids: cent_bf16 is NULL");
+  VX_CHECK(!refresh_newest || pages->total_pages == 0 || k_pool, VX_ERR_INVALID_ARG,
+           "refresh_newest needs k_pool");
+  return VX_OK;
+}
+
+// Checks of vx_sparse_decode's own arguments (pages and geometry already
+// checked); `launching` adds the pointers a launch needs.
+vx_status check_decode_args(const vx_pages* pages, const vx_geom* geom, const void* q,
+                            const void* k_pool, const void* v_pool, const int32_t* sel,
+                            int32_t sel_stride, const int32_t* sel_count, float sm_scale,
+                            const float* out, bool launching) {
+  VX_CHECK(sel_stride >= 1, VX_ERR_INVALID_ARG, "sel_stride < 1");
+  VX_CHECK(std::isfinite(sm_scale), VX_ERR_INVALID_ARG, "sm_scale not finite");
+  if (!geom->mla) {
+    const int G = geom->num_q_heads / geom->num_kv_heads;
+    VX_CHECK(G == 1 || G == 2 || G == 4 || G == 8, VX_ERR_UNSUPPORTED,
+             "GQA group %d (supported: 1, 2, 4, 8)", G);
+  } else {
+    VX_CHECK(pages->page_size == 64, VX_ERR_UNSUPPORTED, "MLA attention needs page_size 64");
+  }
+  if (launching) {
+    VX_CHECK(pages->batch == 0 || (q && k_pool && sel && sel_count && out), VX_ERR_INVALID_ARG,
+             "q, k_pool, sel, sel_count or out is NULL");
+    VX_CHECK(geom->mla || pages->batch == 0 || v_pool, VX_ERR_INVALID_ARG, "v_pool is NULL");
+  }
+  return VX_OK;
+}
+
 vx::Meta meta_of(const vx_pages* p) {
   vx::Meta m;
   m.batch = p->batch;
@@ -168,6 +216,8 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
     ws += align_up((size_t)p->batch * hq * S * 2 * sizeof(float), 256);
   }
   out->workspace_bytes = ws;
+  out->fused_step = S == 1 && p->total_pages > 0 &&
+                    vx::decode_step_fusable(*g, p->page_size, p->max_pages, sel_stride);
   return VX_OK;
 }
 
@@ -273,21 +323,10 @@ vx_status vx_index_pages(const vx_pages* pages, const vx_geom* geom, const void*
                          int32_t* sel, int32_t sel_stride, int32_t* sel_count,
                          hipStream_t stream) {
   vx_status st;
-  if ((st = check_pages(pages)) != VX_OK) return st;
-  if ((st = check_geom(geom)) != VX_OK) return st;
-  VX_CHECK(refresh_newest == 0 || refresh_newest == 1, VX_ERR_INVALID_ARG,
-           "refresh_newest must be 0 or 1");
-  VX_CHECK(std::isfinite(score_scale), VX_ERR_INVALID_ARG, "score_scale not finite");
-  if ((st = check_topk(pages, k, n_sink, n_local, mode, rand_u32, sel, sel_stride, sel_count)) !=
-      VX_OK)
+  if ((st = check_index_args(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
+                             score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,
+                             sel_stride, sel_count)) != VX_OK)
     return st;
-  VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
-  VX_CHECK(pages->total_pages == 0 || scores, VX_ERR_INVALID_ARG, "scores is NULL");
-  VX_CHECK(pages->total_pages == 0 || centroids, VX_ERR_INVALID_ARG, "centroids is NULL");
-  VX_CHECK(!geom->mla || pages->total_pages == 0 || cent_bf16, VX_ERR_INVALID_ARG,
-           "MLA scores the bf16 centroids: cent_bf16 is NULL");
-  VX_CHECK(!refresh_newest || pages->total_pages == 0 || k_pool, VX_ERR_INVALID_ARG,
-           "refresh_newest needs k_pool");
   if (pages->batch == 0) return VX_OK;
   const vx::Meta m = meta_of(pages);
   hipError_t e = hipSuccess;
@@ -323,20 +362,9 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const voi
   if ((st = check_pages(pages)) != VX_OK) return st;
   if ((st = check_geom(geom)) != VX_OK) return st;
   VX_CHECK(workspace_bytes, VX_ERR_INVALID_ARG, "workspace_bytes is NULL");
-  VX_CHECK(sel_stride >= 1, VX_ERR_INVALID_ARG, "sel_stride < 1");
-  VX_CHECK(std::isfinite(sm_scale), VX_ERR_INVALID_ARG, "sm_scale not finite");
-  if (!geom->mla) {
-    const int G = geom->num_q_heads / geom->num_kv_heads;
-    VX_CHECK(G == 1 || G == 2 || G == 4 || G == 8, VX_ERR_UNSUPPORTED,
-             "GQA group %d (supported: 1, 2, 4, 8)", G);
-  } else {
-    VX_CHECK(pages->page_size == 64, VX_ERR_UNSUPPORTED, "MLA attention needs page_size 64");
-  }
-  if (workspace) {
-    VX_CHECK(pages->batch == 0 || (q && k_pool && sel && sel_count && out), VX_ERR_INVALID_ARG,
-             "q, k_pool, sel, sel_count or out is NULL");
-    VX_CHECK(geom->mla || pages->batch == 0 || v_pool, VX_ERR_INVALID_ARG, "v_pool is NULL");
-  }
+  if ((st = check_decode_args(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                              out, workspace != nullptr)) != VX_OK)
+    return st;
   int cus = 0;
   if ((st = device_cus(&cus)) != VX_OK) return st;
   vx_plan plan;
@@ -374,6 +402,53 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const voi
     if (e != hipSuccess) return hip_status(e, "merge kernel launch");
   }
   return VX_OK;
+}
+
+vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void* q,
+                         const void* k_pool, const void* v_pool, float* centroids,
+                         void* cent_bf16, int32_t refresh_newest, float score_scale,
+                         float sm_scale, int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
+                         const uint32_t* rand_u32, float* scores, int32_t* sel,
+                         int32_t sel_stride, int32_t* sel_count, float* out, float* lse,
+                         int32_t num_splits, void* workspace, size_t* workspace_bytes,
+                         hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(workspace_bytes, VX_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  if ((st = check_decode_args(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                              out, workspace != nullptr)) != VX_OK)
+    return st;
+  if (workspace &&
+      (st = check_index_args(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
+                             score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,
+                             sel_stride, sel_count)) != VX_OK)
+    return st;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != VX_OK) return st;
+  vx_plan plan;
+  if ((st = make_plan(pages, geom, sel_stride, num_splits, cus, &plan)) != VX_OK) return st;
+  if (!workspace) {
+    *workspace_bytes = plan.workspace_bytes;
+    return VX_OK;
+  }
+  VX_CHECK(*workspace_bytes >= plan.workspace_bytes, VX_ERR_WORKSPACE,
+           "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
+  if (pages->batch == 0) return VX_OK;
+  if (plan.num_splits == 1 && pages->total_pages > 0 &&
+      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride)) {
+    const hipError_t e = vx::launch_decode_step_gqa(
+        meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, refresh_newest,
+        score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
+        sel_count, out, lse, pages->max_pages, stream);
+    return hip_status(e, "decode step kernel launch");
+  }
+  if ((st = vx_index_pages(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
+                           score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,
+                           sel_stride, sel_count, stream)) != VX_OK)
+    return st;
+  return vx_sparse_decode(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                          out, lse, num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

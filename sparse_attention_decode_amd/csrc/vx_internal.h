@@ -123,6 +123,13 @@ VX_DEV float group_max(float x) {
   return x;
 }
 
+// Softmax constants: logits are kept in log2 units (exp2 on the ALUs).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Four consecutive elements: raw load, then widening to fp32 (kept apart so
 // that many loads can be in flight in raw form).
 template <typename T> struct Quad;
@@ -161,6 +168,16 @@ hipError_t launch_index_gqa(const Meta& m, const vx_geom& g, const void* q, cons
                             float* scores, int k, int n_sink, int n_local, int mode,
                             const uint32_t* rnd, int32_t* sel, int stride, int32_t* sel_count,
                             int max_pages, hipStream_t s);
+// Whole step per (sequence, KV head) in one kernel (GQA, bf16, Dk = 128, one
+// split): index_segment then mfma_attend.
+bool decode_step_fusable(const vx_geom& g, int page_size, int max_pages, int sel_stride);
+hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q,
+                                  const void* k_pool, const void* v_pool, float* cent,
+                                  uint16_t* cent_bf16, int refresh, float score_scale,
+                                  float sm_scale, float* scores, int k, int n_sink, int n_local,
+                                  int mode, const uint32_t* rnd, int32_t* sel, int stride,
+                                  int32_t* sel_count, float* out, float* lse, int max_pages,
+                                  hipStream_t s);
 hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,
                                    const uint16_t* cent_bf16, float scale, float* scores,
                                    int max_pages, hipStream_t s);
@@ -181,8 +198,12 @@ hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
 hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* part_o,
                         const float* part_ml, float* out, float* lse, hipStream_t s);
 
-// Largest selection one split may stream (lane-distributed page list).
-constexpr int kMaxPagesPerSplit = 64;
+// Largest selection one attention split streams: its page list sits in LDS,
+// one entry per thread of the block that fills it (blocks have >= 256).
+constexpr int kMaxPagesPerSplit = 128;
+// Largest page capacity for which the whole-step kernel keeps every entry's
+// key and physical page in LDS.
+constexpr int kMaxFusedStepPages = 4096;
 // Largest per-sequence page count the top-k supports (LDS resident keys).
 constexpr int kMaxTopkPages = 16000;
 

@@ -95,12 +95,24 @@ class DecodeStep:
                            self.out, self.lse, self.num_splits, self.workspace,
                            self.workspace_bytes, stream)
 
+    def step(self, refresh: bool = True, stream=None) -> None:
+        """vx_decode_step: the indexer and the attention in one call."""
+        w = self.w
+        V.vx_decode_step(self.pages, self.geom, w.q, w.k_pool, w.v_pool, self.centroids,
+                         self.cent_bf16, refresh, self.score_scale, self.sm_scale, self.k,
+                         self.n_sink, self.n_local, self.mode, w.d_rand_u32, self.scores,
+                         self.sel, self.k_out, self.sel_count, self.out, self.lse,
+                         self.num_splits, self.workspace, self.workspace_bytes, stream)
+
+    def plan(self) -> dict:
+        return V.vx_plan_decode(self.pages, self.geom, self.k_out, self.num_splits)
+
     def run(self, stream=None) -> None:
         """The whole step: cache refresh, scoring, selection, attention."""
         if self.fused:
-            self.index(stream=stream)
+            self.step(stream=stream)
         else:
             self.refresh_centroids(stream=stream)
             self.score(stream)
             self.select(stream=stream)
-        self.attend(stream=stream)
+            self.attend(stream=stream)

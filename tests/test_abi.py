@@ -140,11 +140,13 @@ def test_planner_splits_and_workspace():
     # an explicit split count is honoured (balanced splits, largest one reported)
     plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 7, 256)
     assert plan["num_splits"] == 7 and plan["pages_per_split"] == 3
-    # never more splits than selected pages, never more than 64 pages per split
+    # never more splits than selected pages, never more than 128 pages per split
     plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64), g.__class__(2, 1, 64, 64, 0, 0, 0), 9, 0, 256)
     assert plan["num_splits"] == 9
     plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=200), g, 131, 1, 256)
-    assert plan["pages_per_split"] <= 64 and plan["num_splits"] == 3
+    assert plan["pages_per_split"] <= 128 and plan["num_splits"] == 2
+    plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=300), g, 260, 1, 256)
+    assert plan["pages_per_split"] <= 128 and plan["num_splits"] == 3
     # MLA: one block per sequence and split
     mla = V.make_geom(32, 1, 576, 512, 1, V.VX_BF16, V.VX_BF16)
     plan = V.vx_plan_decode(pages(batch=32, nnz=20480, pool=25600, maxp=1024, page_size=64), mla, 34, 0, 256)
@@ -185,3 +187,45 @@ def test_index_pages_argument_checks():
     e = V.make_pages(0, 16, 0, 0, 0, None, None, None)
     assert call(pages=e, q=None, k_pool=None, centroids=None, scores=None, sel=None,
                 count=None) == V.VX_OK
+
+
+def test_decode_step_argument_checks():
+    p, g = pages(), geom()
+    ok = dict(q=BAD, k_pool=BAD, v_pool=BAD, centroids=BAD, cent_bf16=None, refresh=1, sscale=1.0,
+              smscale=1.0, k=4, n_sink=1, n_local=1, mode=0, rand_u32=None, scores=BAD, sel=BAD,
+              stride=6, count=BAD, out=BAD, lse=None, splits=0, ws=BAD, ws_bytes=1 << 30,
+              pages=p, geom=g)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return status_of(V.vx_decode_step, a["pages"], a["geom"], a["q"], a["k_pool"], a["v_pool"],
+                         a["centroids"], a["cent_bf16"], a["refresh"], a["sscale"], a["smscale"],
+                         a["k"], a["n_sink"], a["n_local"], a["mode"], a["rand_u32"], a["scores"],
+                         a["sel"], a["stride"], a["count"], a["out"], a["lse"], a["splits"],
+                         a["ws"], a["ws_bytes"], stream=0)
+
+    assert call(refresh=2) == V.VX_ERR_INVALID_ARG
+    assert call(sscale=float("nan")) == V.VX_ERR_INVALID_ARG
+    assert call(smscale=float("inf")) == V.VX_ERR_INVALID_ARG
+    assert call(stride=5) == V.VX_ERR_INVALID_ARG
+    assert call(mode=1) == V.VX_ERR_INVALID_ARG
+    assert call(v_pool=None) == V.VX_ERR_INVALID_ARG
+    assert call(out=None) == V.VX_ERR_INVALID_ARG
+    assert call(scores=None) == V.VX_ERR_INVALID_ARG
+    assert call(centroids=None) == V.VX_ERR_INVALID_ARG
+    assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
+    assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
+
+
+def test_plan_reports_the_whole_step_kernel():
+    g = geom()
+    big = pages(batch=32, nnz=6144, pool=7680, maxp=256)
+    assert V.vx_plan_decode(big, g, 18, 0, 256)["fused_step"] == 1
+    assert V.vx_plan_decode(big, g, 18, 2, 256)["fused_step"] == 0  # two splits
+    assert V.vx_plan_decode(big, g, 131, 0, 256)["fused_step"] == 0  # selection > 128 pages
+    assert V.vx_plan_decode(big, geom(qd=V.VX_F32, kvd=V.VX_F32), 18, 0, 256)["fused_step"] == 0
+    huge = pages(batch=32, nnz=200000, pool=200000, maxp=5000)
+    assert V.vx_plan_decode(huge, g, 18, 0, 256)["fused_step"] == 0  # capacity > 4096 pages
+    small = pages(batch=2, nnz=40, pool=40, maxp=20)
+    assert V.vx_plan_decode(small, g, 18, 0, 256)["fused_step"] == 0  # planner splits
+    assert V.vx_plan_decode(small, g, 18, 1, 256)["fused_step"] == 1

@@ -148,3 +148,67 @@ def test_idle_slots(base, headroom):
                 assert (step.out[b] == 0).all()
                 assert torch.isneginf(step.lse[b]).all()
         assert check_step_against_oracle(w, step, [b for b, L in enumerate(lens) if L]) == 0
+
+
+# ---- vx_decode_step: the whole step in one call ---------------------------
+
+def step_vs_calls(w, num_splits=0, mode=V.VX_TOPK_EXACT, appends=2):
+    """vx_decode_step against vx_centroid_update + vx_page_scores +
+    vx_topk_pages + vx_sparse_decode on separate buffers: same bits."""
+    sep = DecodeStep(w, mode=mode, fused=False, num_splits=num_splits)
+    one = DecodeStep(w, mode=mode, fused=True, num_splits=num_splits)
+    sep.rebuild_centroids()
+    one.rebuild_centroids()
+    used = used_pages(w)
+    for _ in range(appends):
+        if w.spec.headroom_tokens > 0:
+            w.append_token()
+        valid = valid_entries(w)
+        sep.run()
+        one.run()
+        T.sync()
+        assert torch.equal(sep.centroids[used], one.centroids[used])
+        assert torch.equal(sep.scores[:, valid], one.scores[:, valid])
+        assert torch.equal(sep.sel_count, one.sel_count)
+        assert torch.equal(sep.sel, one.sel)
+        assert torch.equal(sep.out, one.out)
+        assert torch.equal(sep.lse, one.lse)
+    return one
+
+
+@pytest.mark.parametrize("num_splits", [0, 1])
+@pytest.mark.parametrize("mode", [V.VX_TOPK_EXACT, V.VX_TOPK_APPROX])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_decode_step_equals_calls(name, mode, num_splits):
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=15))
+    one = step_vs_calls(w, num_splits=num_splits, mode=mode)
+    spec = w.spec
+    fused = (num_splits == 1 and not spec.mla and spec.kv_dtype == "bf16"
+             and spec.head_dim_k == 128 and one.k_out <= 128)
+    assert one.plan()["fused_step"] == int(fused)
+
+
+@pytest.mark.parametrize("name,fused", [("gqa_bf16", 1), ("largebatch_bf16", 1),
+                                        ("longgen_bf16", 0), ("mla_bf16", 0)])
+def test_full_size_decode_step_equals_calls(name, fused):
+    sp = W.spec(name, headroom_tokens=max(64, W.spec(name).headroom_tokens))
+    w = W.make(sp, "cuda", seed=2)
+    one = step_vs_calls(w)
+    assert one.plan()["fused_step"] == fused
+    del w, one
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["gqa_small", "large_small", "longgen_small"])
+def test_fused_decode_step_matches_oracle(name):
+    """One split per segment (the whole-step kernel where the shape allows),
+    after appends, against the oracle for every sequence."""
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=20), "cpu", seed=16))
+    step = DecodeStep(w, num_splits=1)
+    step.rebuild_centroids()
+    for _ in range(3):
+        w.append_token()
+        step.run()
+    T.sync()
+    differing = check_step_against_oracle(w, step, range(w.batch))
+    assert differing <= max(1, w.batch * w.spec.num_kv_heads // 20)
