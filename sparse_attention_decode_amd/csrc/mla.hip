@@ -85,18 +85,28 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 }
 
 // ---------------------------------------------------------------- attention
-// One block (4 waves) per (sequence b, split s); the split holds a balanced
-// share of the selected pages. Pages are consumed as 32-token chunks. Each
+// One block (8 waves) per (sequence b, split s); the split holds a balanced
+// share of the selected pages. Pages are consumed as 64-token chunks. Each
 // chunk is staged in LDS twice: row-major (the B operand of q.k^T reads a
 // token's 8 consecutive columns) and value columns transposed (the B operand
 // of P.V reads 8 consecutive tokens of one column); the transpose is done in
 // registers on 8x8 bf16 blocks, so both operands are single 16-byte LDS
-// reads. The next chunk is prefetched into registers while the current one
-// is consumed. Logits: wave w computes the 16x16 tile (head tile w % MT,
-// token half w / MT); row maxima and sums are exchanged through LDS. P.V:
-// wave w owns head tile w % MT and value columns [part * 512 / NP, +512 / NP).
-constexpr int CHT = 32;                 // tokens per chunk
-constexpr int VT_ROW = CHT + 8;         // padded transposed-V row (bf16), 80 B
+// reads; in the transposed copy, the 8-token groups of column r sit at
+// group index ^ ((r / 8) % 8), which spreads a wave's stores over the LDS
+// banks. The next kRing chunks are in flight in registers while one is
+// consumed. Logits: wave w < 4 MT computes the 16x16 tile (head tile w % MT,
+// token tile w / MT); row maxima and sums are exchanged through LDS. P.V:
+// wave w owns head tile w % MT and value columns [part * 512 / NP, +512 / NP)
+// with NP = 8 / MT, so its accumulators stay small enough for two waves per
+// SIMD.
+constexpr int kMlaWaves = 8;
+constexpr int CHT = 64;                 // tokens per chunk
+constexpr int NTT = CHT / 16;           // token tiles per chunk
+#ifndef VX_MLA_RING
+#define VX_MLA_RING 1
+#endif
+constexpr int kRing = VX_MLA_RING;      // chunks in flight per block
+constexpr int VT_ROW = CHT + 8;         // padded transposed-V row (bf16), 144 B
 constexpr int PROW = CHT + 8;           // padded P row (bf16)
 
 __device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
@@ -105,19 +115,21 @@ __device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
 }
 
 template <int MT>
-__global__ __launch_bounds__(256) void attn_mla_kernel(
+__global__ __launch_bounds__(64 * kMlaWaves) void attn_mla_kernel(
     Meta m, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const int32_t* __restrict__ sel, int stride, const int32_t* __restrict__ sel_count,
     float qscale, int S, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int HQ = 16 * MT;
-  constexpr int NP = 4 / MT;          // value-column parts
+  constexpr int NP = kMlaWaves / MT;  // value-column parts
   constexpr int NT2 = DV / NP / 16;   // 16-column tiles per wave
+  static_assert(DV / 8 * (CHT / 8) == 64 * kMlaWaves, "one 8x8 staging block per thread");
+  static_assert(CHT * 8 == 64 * kMlaWaves, "one rope vector per thread");
   __shared__ __attribute__((aligned(16))) uint16_t krow[CHT * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t vt[DV * VT_ROW];
   __shared__ __attribute__((aligned(16))) uint16_t pl[MT][16 * PROW];
-  __shared__ float rmax[MT][2][16];
-  __shared__ float rsum[MT][2][16];
+  __shared__ float rmax[MT][NTT][16];
+  __shared__ float rsum[MT][NTT][16];
   __shared__ int pg_phys[kMaxPagesPerSplit];
   __shared__ int pg_nv[kMaxPagesPerSplit];
 
@@ -125,8 +137,8 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
   const int lane = t & 63, w = t >> 6;
   const int col = lane & 15, q4 = lane >> 4;
   const int mt = w % MT, part = w / MT;
-  const bool qk_wave = w < 2 * MT;
-  const int nt = w / MT;  // token half of the logit tile (qk waves)
+  const bool qk_wave = w < NTT * MT;
+  const int nt = w / MT;  // token tile of the logit tile (qk waves)
   const int item = blockIdx.x;
   const int s = item % S, b = item / S;
   const int row0 = m.indptr[b];
@@ -135,9 +147,9 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
   const int count = cap > 0 ? min(sel_count[b], stride) : 0;
   const int p0 = (int)(((long)count * s) / S);
   const int np = min((int)(((long)count * (s + 1)) / S) - p0, kMaxPagesPerSplit);
-  const int P = m.page_size;
+  const int P = m.page_size;  // 64 (checked on the host): one chunk per page
 
-  static_assert(kMaxPagesPerSplit <= 256, "one page-list entry per thread");
+  static_assert(kMaxPagesPerSplit <= 64 * kMlaWaves, "one page-list entry per thread");
   if (t < np) {
     int lp = sel[(size_t)b * stride + p0 + t];
     lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);
@@ -161,34 +173,41 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
 
   const int cpp = P / CHT;
   const int nchunks = np * cpp;
-  auto chunk_valid = [&](int c) { return min(CHT, pg_nv[c / cpp] - (c % cpp) * CHT); };
-  auto next_valid = [&](int c) {
-    while (c < nchunks && chunk_valid(c) <= 0) ++c;
-    return c;
+  // Valid tokens of chunk c; chunks past the end (the ring's tail) are empty
+  // and contribute exactly nothing (p = 0, alpha = 1).
+  auto chunk_valid = [&](int c) {
+    return c < nchunks ? min(CHT, pg_nv[c / cpp] - (c % cpp) * CHT) : 0;
   };
   // staging roles: an 8x8 (token x column) block of value columns + one rope vector
   const int dg = t & 63, tg = t >> 6;      // columns 8 dg.., tokens 8 tg..
   const int rr = t >> 3, rg = t & 7;       // rope: token rr, columns 512 + 8 rg..
-  u32x4 vb[8], rp;
-  auto prefetch = [&](int c) {
+  // Ring of kRing chunks in flight; a load past the end re-reads the last chunk.
+  u32x4 vb[kRing][8], rp[kRing];
+  auto prefetch = [&](int c, u32x4* v, u32x4& r) {
+    c = min(c, nchunks - 1);
     const uint16_t* src = kp + ((size_t)pg_phys[c / cpp] * P + (size_t)(c % cpp) * CHT) * DK;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      vb[i] = __builtin_nontemporal_load((const u32x4*)(src + (8 * tg + i) * DK + 8 * dg));
-    rp = __builtin_nontemporal_load((const u32x4*)(src + rr * DK + DV + 8 * rg));
+      v[i] = __builtin_nontemporal_load((const u32x4*)(src + (8 * tg + i) * DK + 8 * dg));
+    r = __builtin_nontemporal_load((const u32x4*)(src + rr * DK + DV + 8 * rg));
   };
 
   const int dcol0 = part * (DV / NP);
-  int c = next_valid(0);
-  if (c < nchunks) prefetch(c);
-  while (c < nchunks) {
+  if (nchunks > 0) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) prefetch(d, vb[d], rp[d]);
+  }
+  for (int c0 = 0; c0 < nchunks; c0 += kRing) {
+#pragma unroll
+  for (int d = 0; d < kRing; ++d) {
+    const int c = c0 + d;
     const int nv = chunk_valid(c);
     __syncthreads();  // (A) previous chunk fully consumed
     {
       u32x4 x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        x[i] = (8 * tg + i < nv) ? vb[i] : u32x4{0u, 0u, 0u, 0u};
+        x[i] = (8 * tg + i < nv) ? vb[d][i] : u32x4{0u, 0u, 0u, 0u};
         *(u32x4*)(krow + (8 * tg + i) * ROW + 8 * dg) = x[i];
       }
 #pragma unroll
@@ -198,12 +217,11 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
         y.y = half_of(x[2], e) | (half_of(x[3], e) << 16);
         y.z = half_of(x[4], e) | (half_of(x[5], e) << 16);
         y.w = half_of(x[6], e) | (half_of(x[7], e) << 16);
-        *(u32x4*)(vt + (8 * dg + e) * VT_ROW + 8 * tg) = y;
+        *(u32x4*)(vt + (8 * dg + e) * VT_ROW + 8 * (tg ^ (dg & 7))) = y;
       }
-      *(u32x4*)(krow + rr * ROW + DV + 8 * rg) = (rr < nv) ? rp : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(krow + rr * ROW + DV + 8 * rg) = (rr < nv) ? rp[d] : u32x4{0u, 0u, 0u, 0u};
     }
-    const int cn = next_valid(c + 1);
-    if (cn < nchunks) prefetch(cn);
+    prefetch(c + kRing, vb[d], rp[d]);
     __syncthreads();  // (B) chunk c staged
 
     float z[4];
@@ -223,12 +241,15 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
         if (col == 0) rmax[mt][nt][4 * q4 + i] = mx;
       }
     }
-    __syncthreads();  // (C) row maxima of both token halves
+    __syncthreads();  // (C) row maxima of every token tile
     float mnew[4], alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * q4 + i;
-      mnew[i] = fmaxf(mrow[i], fmaxf(rmax[mt][0][r], rmax[mt][1][r]));
+      float mx = rmax[mt][0][r];
+#pragma unroll
+      for (int u = 1; u < NTT; ++u) mx = fmaxf(mx, rmax[mt][u][r]);
+      mnew[i] = fmaxf(mrow[i], mx);
       alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mnew[i]);
     }
     if (qk_wave) {
@@ -244,18 +265,28 @@ __global__ __launch_bounds__(256) void attn_mla_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * q4 + i;
-      lrow[i] = lrow[i] * alpha[i] + (rsum[mt][0][r] + rsum[mt][1][r]);
+      float sum = rsum[mt][0][r];
+#pragma unroll
+      for (int u = 1; u < NTT; ++u) sum += rsum[mt][u][r];
+      lrow[i] = lrow[i] * alpha[i] + sum;
       mrow[i] = mnew[i];
     }
 #pragma unroll
     for (int x = 0; x < NT2; ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[x][i] *= alpha[i];
-    const u32x4 pa = *(const u32x4*)(pl[mt] + col * PROW + 8 * q4);
 #pragma unroll
-    for (int x = 0; x < NT2; ++x)
-      o[x] = mfma(pa, *(const u32x4*)(vt + (dcol0 + 16 * x + col) * VT_ROW + 8 * q4), o[x]);
-    c = cn;
+    for (int k2 = 0; k2 < CHT / 32; ++k2) {
+      const u32x4 pa = *(const u32x4*)(pl[mt] + col * PROW + 32 * k2 + 8 * q4);
+#pragma unroll
+      for (int x = 0; x < NT2; ++x)
+      {
+        const int r = dcol0 + 16 * x + col;  // value column; its token groups are swizzled
+        o[x] = mfma(pa, *(const u32x4*)(vt + r * VT_ROW + 8 * ((4 * k2 + q4) ^ ((r >> 3) & 7))),
+                    o[x]);
+      }
+    }
+  }
   }
 
   // results: rows 4*q4 + i of head tile mt, columns dcol0 + 16 x + col
@@ -307,7 +338,7 @@ hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
                                 float* part_ml, hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   const float qscale = sm_scale * kLog2e;
-  dim3 grid(m.batch * num_splits), block(256);
+  dim3 grid(m.batch * num_splits), block(64 * kMlaWaves);
   if (g.num_q_heads == 32)
     hipLaunchKernelGGL(attn_mla_kernel<2>, grid, block, 0, s, m, (const uint16_t*)q,
                        (const uint16_t*)k_pool, sel, sel_stride, sel_count, qscale, num_splits,
