@@ -289,16 +289,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_gqa_kernel(
 }
 
 // The bf16, Dk = Dv = 128 path on the matrix cores: mfma_attend in attn_mfma.h.
-template <int G, int P>
-__global__ __launch_bounds__(64 * kWaves) void attn_gqa_mfma_kernel(
+template <int G, int P, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_gqa_mfma_kernel(
     Meta m, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ sel, int stride,
     const int32_t* __restrict__ sel_count, float qscale, int S, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  static_assert(kMaxPagesPerSplit <= 64 * kWaves, "one page-list entry per thread");
+  static_assert(kMaxPagesPerSplit <= 64 * NW, "one page-list entry per thread");
   __shared__ int pg_phys[kMaxPagesPerSplit];
   __shared__ int pg_nv[kMaxPagesPerSplit];
-  __shared__ MfmaShared<G, kWaves> sm;
+  __shared__ MfmaShared<G, NW> sm;
 
   const int item = blockIdx.x;
   const int s = item % S, bg = item / S;
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_gqa_mfma_kernel(
   u32x4 qa[4];
   mfma_load_q<G>(q, b, g, hkv, qa);
   __syncthreads();  // page list ready
-  mfma_attend<G, P, kWaves>(sm, pg_phys, pg_nv, np, b, g, hkv, qa, kp, vp, qscale, S, s, out, lse,
+  mfma_attend<G, P, NW>(sm, pg_phys, pg_nv, np, b, g, hkv, qa, kp, vp, qscale, S, s, out, lse,
                             part_o, part_ml);
 }
 
@@ -380,37 +380,50 @@ hipError_t launch_g(const Meta& m, const vx_geom& geo, const void* q, const void
   return hipGetLastError();
 }
 
+template <int G, int P>
+hipError_t launch_mfma_g(const Meta& m, int hkv, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* sel, int stride, const int32_t* cnt,
+                         float qscale, int S, float* out, float* lse, float* po, float* pml,
+                         int max_pages, hipStream_t st) {
+  dim3 grid(m.batch * hkv * S);
+  if constexpr (G <= 4) {
+    if (gqa_attn_waves(G, max_pages) == 16) {
+      hipLaunchKernelGGL((attn_gqa_mfma_kernel<G, P, 16>), grid, dim3(1024), 0, st, m, hkv,
+                         (const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool, sel,
+                         stride, cnt, qscale, S, out, lse, po, pml);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_gqa_mfma_kernel<G, P, 8>), grid, dim3(512), 0, st, m, hkv,
+                     (const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool, sel,
+                     stride, cnt, qscale, S, out, lse, po, pml);
+  return hipGetLastError();
+}
+
 template <int P>
 hipError_t launch_mfma(const Meta& m, const vx_geom& geo, const void* q, const void* k_pool,
                        const void* v_pool, const int32_t* sel, int stride, const int32_t* cnt,
                        float qscale, int S, float* out, float* lse, float* po, float* pml,
-                       hipStream_t st) {
+                       int max_pages, hipStream_t st) {
   const int hkv = geo.num_kv_heads;
-  dim3 block(64 * kWaves), grid(m.batch * hkv * S);
-  const int G = geo.num_q_heads / hkv;
-#define VX_MFMA_CASE(GG)                                                                        \
-  case GG:                                                                                      \
-    hipLaunchKernelGGL((attn_gqa_mfma_kernel<GG, P>), grid, block, 0, st, m, hkv,              \
-                       (const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,   \
-                       sel, stride, cnt, qscale, S, out, lse, po, pml);                        \
-    break;
-  switch (G) {
-    VX_MFMA_CASE(1)
-    VX_MFMA_CASE(2)
-    VX_MFMA_CASE(4)
-    VX_MFMA_CASE(8)
-    default:
-      return hipErrorInvalidValue;
+  switch (geo.num_q_heads / hkv) {
+    case 1: return launch_mfma_g<1, P>(m, hkv, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out,
+                                       lse, po, pml, max_pages, st);
+    case 2: return launch_mfma_g<2, P>(m, hkv, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out,
+                                       lse, po, pml, max_pages, st);
+    case 4: return launch_mfma_g<4, P>(m, hkv, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out,
+                                       lse, po, pml, max_pages, st);
+    case 8: return launch_mfma_g<8, P>(m, hkv, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out,
+                                       lse, po, pml, max_pages, st);
+    default: return hipErrorInvalidValue;
   }
-#undef VX_MFMA_CASE
-  return hipGetLastError();
 }
 
 template <typename QT, typename KV>
 hipError_t launch_t(const Meta& m, const vx_geom& geo, const void* q, const void* k_pool,
                     const void* v_pool, const int32_t* sel, int stride, const int32_t* cnt,
                     float qscale, int S, int pps, float* out, float* lse, float* po, float* pml,
-                    hipStream_t st) {
+                    int max_pages, hipStream_t st) {
   const int dk = geo.head_dim_k, P = m.page_size;
   if (dk == 64 && P == 16)
     return launch_g<QT, KV, 64, 16>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, pps,
@@ -422,10 +435,10 @@ hipError_t launch_t(const Meta& m, const vx_geom& geo, const void* q, const void
   if constexpr (sizeof(KV) == 2) {
     if (dk == 128 && P == 16)
       return launch_mfma<16>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out, lse,
-                             po, pml, st);
+                             po, pml, max_pages, st);
     if (dk == 128 && P == 64)
       return launch_mfma<64>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out, lse,
-                             po, pml, st);
+                             po, pml, max_pages, st);
   }
 #endif
   if (dk == 128 && P == 16)
@@ -443,14 +456,16 @@ hipError_t launch_attention_gqa(const Meta& m, const vx_geom& g, const void* q,
                                 const void* k_pool, const void* v_pool, const int32_t* sel,
                                 int sel_stride, const int32_t* sel_count, float sm_scale,
                                 int num_splits, int pages_per_split, float* out, float* lse,
-                                float* part_o, float* part_ml, hipStream_t s) {
+                                float* part_o, float* part_ml, int max_pages, hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   const float qscale = sm_scale * kLog2e;
   if (g.kv_dtype == VX_F32)
     return launch_t<float, float>(m, g, q, k_pool, v_pool, sel, sel_stride, sel_count, qscale,
-                                  num_splits, pages_per_split, out, lse, part_o, part_ml, s);
+                                  num_splits, pages_per_split, out, lse, part_o, part_ml, max_pages,
+                                  s);
   return launch_t<uint16_t, uint16_t>(m, g, q, k_pool, v_pool, sel, sel_stride, sel_count, qscale,
-                                      num_splits, pages_per_split, out, lse, part_o, part_ml, s);
+                                      num_splits, pages_per_split, out, lse, part_o, part_ml,
+                                      max_pages, s);
 }
 
 hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* part_o,

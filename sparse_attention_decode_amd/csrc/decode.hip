@@ -15,26 +15,23 @@
 namespace vx {
 namespace {
 
-constexpr int kStepWaves = 8;
-
-template <int G, int P>
-__global__ __launch_bounds__(64 * kStepWaves) void decode_seg_kernel(SegArgs a,
-                                                                     const uint16_t* __restrict__ vp,
-                                                                     float qscale,
-                                                                     float* __restrict__ out,
-                                                                     float* __restrict__ lse) {
+template <int G, int P, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
+                                                             const uint16_t* __restrict__ vp,
+                                                             float qscale, float* __restrict__ out,
+                                                             float* __restrict__ lse) {
   // keys [cap_keys + 256], then the physical page of every entry [cap_keys]
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   __shared__ int32_t sel_l[kMaxPagesPerSplit];
   __shared__ int32_t cnt_l;
   __shared__ int pg_phys[kMaxPagesPerSplit];
   __shared__ int pg_nv[kMaxPagesPerSplit];
-  __shared__ MfmaShared<G, kStepWaves> sm;
-  static_assert(kMaxPagesPerSplit <= 64 * kStepWaves, "one page-list entry per thread");
+  __shared__ MfmaShared<G, NW> sm;
+  static_assert(kMaxPagesPerSplit <= 64 * NW, "one page-list entry per thread");
 
   const int seg = blockIdx.x;
   int* pid_l = (int*)(dyn + a.cap_keys + 256);
-  index_segment<uint16_t, uint16_t, 128, G, kStepWaves>(a, seg, dyn, pid_l, sel_l, &cnt_l);
+  index_segment<uint16_t, uint16_t, 128, G, NW>(a, seg, dyn, pid_l, sel_l, &cnt_l);
 
   const Meta& m = a.m;
   const int b = seg / a.hkv, g = seg % a.hkv;
@@ -49,31 +46,37 @@ __global__ __launch_bounds__(64 * kStepWaves) void decode_seg_kernel(SegArgs a,
     pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
   }
   __syncthreads();  // page list ready
-  mfma_attend<G, P, kStepWaves>(sm, pg_phys, pg_nv, count, b, g, a.hkv, qa,
-                                (const uint16_t*)a.kp, vp, qscale, 1, 0, out, lse, nullptr,
-                                nullptr);
+  mfma_attend<G, P, NW>(sm, pg_phys, pg_nv, count, b, g, a.hkv, qa, (const uint16_t*)a.kp, vp,
+                        qscale, 1, 0, out, lse, nullptr, nullptr);
+}
+
+template <int G, int P>
+hipError_t launch_g(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
+                    int max_pages, hipStream_t s) {
+  dim3 grid(a.m.batch * a.hkv);
+  const size_t lds = (size_t)(2 * a.cap_keys + 256) * sizeof(uint32_t);
+  if constexpr (G <= 4) {
+    if (gqa_attn_waves(G, max_pages) == 16) {
+      hipLaunchKernelGGL((decode_seg_kernel<G, P, 16>), grid, dim3(1024), lds, s, a,
+                         (const uint16_t*)v_pool, qscale, out, lse);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_seg_kernel<G, P, 8>), grid, dim3(512), lds, s, a,
+                     (const uint16_t*)v_pool, qscale, out, lse);
+  return hipGetLastError();
 }
 
 template <int P>
 hipError_t launch_p(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
-                    hipStream_t s) {
-  dim3 grid(a.m.batch * a.hkv), block(64 * kStepWaves);
-  const size_t lds = (size_t)(2 * a.cap_keys + 256) * sizeof(uint32_t);
-#define VX_STEP(GG)                                                                             \
-  case GG:                                                                                      \
-    hipLaunchKernelGGL((decode_seg_kernel<GG, P>), grid, block, lds, s, a,                     \
-                       (const uint16_t*)v_pool, qscale, out, lse);                              \
-    break;
+                    int max_pages, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    VX_STEP(1)
-    VX_STEP(2)
-    VX_STEP(4)
-    VX_STEP(8)
-    default:
-      return hipErrorInvalidValue;
+    case 1: return launch_g<1, P>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 2: return launch_g<2, P>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 4: return launch_g<4, P>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 8: return launch_g<8, P>(a, v_pool, qscale, out, lse, max_pages, s);
+    default: return hipErrorInvalidValue;
   }
-#undef VX_STEP
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -114,8 +117,8 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
   a.sel_count = sel_count;
   a.cap_keys = (max_pages + 63) / 64 * 64;
   const float qscale = sm_scale * kLog2e;
-  if (m.page_size == 16) return launch_p<16>(a, v_pool, qscale, out, lse, s);
-  return launch_p<64>(a, v_pool, qscale, out, lse, s);
+  if (m.page_size == 16) return launch_p<16>(a, v_pool, qscale, out, lse, max_pages, s);
+  return launch_p<64>(a, v_pool, qscale, out, lse, max_pages, s);
 }
 
 }  // namespace vx

@@ -5,23 +5,22 @@
 namespace vx {
 namespace {
 
-#ifndef VX_SEG_WAVES
-#define VX_SEG_WAVES 8
-#endif
-constexpr int kSegWaves = VX_SEG_WAVES;  // waves per block
+// Waves per block: 16 for short segments (more page loads in flight at
+// once), 8 for long ones (a block's work then needs fewer waves, and more
+// blocks fit a compute unit); the bound is kMaxSegPagesFor16.
 
-template <typename QT, typename KV, int DK, int GG>
-__global__ __launch_bounds__(64 * kSegWaves) void index_seg_kernel(SegArgs a) {
+template <typename QT, typename KV, int DK, int GG, int NW>
+__global__ __launch_bounds__(64 * NW) void index_seg_kernel(SegArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // cap_keys + 256 words
-  index_segment<QT, KV, DK, GG, kSegWaves>(a, blockIdx.x, keys, nullptr, nullptr, nullptr);
+  index_segment<QT, KV, DK, GG, NW>(a, blockIdx.x, keys, nullptr, nullptr, nullptr);
 }
 
-template <typename QT, typename KV, int DK>
-hipError_t launch_dk(const SegArgs& a, hipStream_t s) {
+template <typename QT, typename KV, int DK, int NW>
+hipError_t launch_nw(const SegArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
-  dim3 grid(a.m.batch * a.hkv), block(64 * kSegWaves);
+  dim3 grid(a.m.batch * a.hkv), block(64 * NW);
   const size_t lds = (size_t)(a.cap_keys + 256) * sizeof(uint32_t);
-#define VX_SEG(GG) hipLaunchKernelGGL((index_seg_kernel<QT, KV, DK, GG>), grid, block, lds, s, a)
+#define VX_SEG(GG) hipLaunchKernelGGL((index_seg_kernel<QT, KV, DK, GG, NW>), grid, block, lds, s, a)
   switch (G) {
     case 1: VX_SEG(1); break;
     case 2: VX_SEG(2); break;
@@ -31,6 +30,12 @@ hipError_t launch_dk(const SegArgs& a, hipStream_t s) {
   }
 #undef VX_SEG
   return hipGetLastError();
+}
+
+template <typename QT, typename KV, int DK>
+hipError_t launch_dk(const SegArgs& a, int max_pages, hipStream_t s) {
+  if (max_pages <= kMaxSegPagesFor16) return launch_nw<QT, KV, DK, 16>(a, s);
+  return launch_nw<QT, KV, DK, 8>(a, s);
 }
 
 }  // namespace
@@ -63,8 +68,10 @@ hipError_t launch_index_gqa(const Meta& m, const vx_geom& g, const void* q, cons
   a.cap_keys = (max_pages + 63) / 64 * 64;
   const bool f32 = g.kv_dtype == VX_F32;
   if (g.head_dim_k == 64)
-    return f32 ? launch_dk<float, float, 64>(a, s) : launch_dk<uint16_t, uint16_t, 64>(a, s);
-  return f32 ? launch_dk<float, float, 128>(a, s) : launch_dk<uint16_t, uint16_t, 128>(a, s);
+    return f32 ? launch_dk<float, float, 64>(a, max_pages, s)
+               : launch_dk<uint16_t, uint16_t, 64>(a, max_pages, s);
+  return f32 ? launch_dk<float, float, 128>(a, max_pages, s)
+             : launch_dk<uint16_t, uint16_t, 128>(a, max_pages, s);
 }
 
 }  // namespace vx

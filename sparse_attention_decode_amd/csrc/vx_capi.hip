@@ -394,7 +394,8 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const voi
                                  plan.pages_per_split, out, lse, part_o, part_ml, stream);
   else
     e = vx::launch_attention_gqa(m, *geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
-                                 S, plan.pages_per_split, out, lse, part_o, part_ml, stream);
+                                 S, plan.pages_per_split, out, lse, part_o, part_ml,
+                                 pages->max_pages, stream);
   if (e != hipSuccess) return hip_status(e, "attention kernel launch");
   if (S > 1) {
     e = vx::launch_merge(pages->batch, geom->num_q_heads, geom->head_dim_v, S, part_o, part_ml, out,

@@ -189,7 +189,7 @@ hipError_t launch_attention_gqa(const Meta& m, const vx_geom& g, const void* q,
                                 const void* k_pool, const void* v_pool, const int32_t* sel,
                                 int sel_stride, const int32_t* sel_count, float sm_scale,
                                 int num_splits, int pages_per_split, float* out, float* lse,
-                                float* part_o, float* part_ml, hipStream_t s);
+                                float* part_o, float* part_ml, int max_pages, hipStream_t s);
 hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
                                 const void* k_pool, const int32_t* sel, int sel_stride,
                                 const int32_t* sel_count, float sm_scale, int num_splits,
@@ -201,6 +201,13 @@ hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* 
 // Largest selection one attention split streams: its page list sits in LDS,
 // one entry per thread of the block that fills it (blocks have >= 256).
 constexpr int kMaxPagesPerSplit = 128;
+// Waves per block of the GQA bf16 attention (standalone and whole-step
+// kernels alike, so both sum in the same order): 16 for short segments with
+// G <= 4 (more chunks in flight at once), else 8.
+constexpr int kMaxSegPagesFor16 = 512;
+inline int gqa_attn_waves(int G, int max_pages) {
+  return (G <= 4 && max_pages <= kMaxSegPagesFor16) ? 16 : 8;
+}
 // Largest page capacity for which the whole-step kernel keeps every entry's
 // key and physical page in LDS.
 constexpr int kMaxFusedStepPages = 4096;
