@@ -26,6 +26,7 @@ SMALL = {
     "large_small": W.spec("largebatch_bf16", batch=6,
                           lengths=("lognormal", 4000, math.log(2.0), 1000, 16000)),
     "mla_small": W.spec("mla_bf16", batch=4, lengths=("uniform", 2000, 6000)),
+    "mla16_small": W.spec("mla_bf16", batch=3, num_q_heads=16, lengths=("uniform", 1500, 5000)),
 }
 
 
