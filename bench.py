@@ -127,6 +127,63 @@ def cpu_baseline(w, step, seconds):
                       f"numpy fp64, one thread, {t_total:.1f} s"}
 
 
+def sources_hash():
+    """sha256 over the kernel sources: HBM traffic figures taken with other
+    sources no longer describe these kernels."""
+    import hashlib
+    d = os.path.join(ROOT, "sparse_attention_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json (rocprofv3
+    FETCH_SIZE and WRITE_SIZE passes, calibrated), or None when they were
+    taken on other kernel sources or not at all."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get("workloads", {}).get(workload)
+    if not e or e.get("kernel") != kernel or e.get("sources_sha256") != sources_hash():
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
+def approx_recall(w, step):
+    """recall@k of the approximate selection against the exact one on the
+    same scores: per (sequence, KV head), |approx ∩ exact| / min(k, candidates),
+    forced pages excluded."""
+    import torch
+    from sparse_attention_decode_amd import binding as V
+    s = w.spec
+    sel_e = torch.full_like(step.sel, -1)
+    cnt_e = torch.zeros_like(step.sel_count)
+    V.vx_topk_pages(step.pages, s.num_kv_heads, step.scores, step.k, step.n_sink, step.n_local,
+                    V.VX_TOPK_EXACT, None, sel_e, step.k_out, cnt_e)
+    torch.cuda.synchronize()
+    a, ca = step.sel.cpu().numpy(), step.sel_count.cpu().numpy()
+    e, ce = sel_e.cpu().numpy(), cnt_e.cpu().numpy()
+    rec = []
+    for b in range(s.batch):
+        n = w.n_pages(b)
+        forced = set(range(min(n, step.n_sink))) | set(range(max(0, n - step.n_local), n))
+        want = min(step.k, n - len(forced))
+        if want <= 0:
+            continue
+        for g in range(s.num_kv_heads):
+            sa = set(a[b, g, :ca[b, g]].tolist()) - forced
+            se = set(e[b, g, :ce[b, g]].tolist()) - forced
+            rec.append(len(sa & se) / want)
+    return {"mean": float(np.mean(rec)), "min": float(np.min(rec)), "segments": len(rec)}
+
+
 def copy_calibration():
     import torch
     n = 1 << 28  # 1 GiB of fp32
@@ -165,6 +222,10 @@ def main():
     torch.cuda.synchronize()
     cent_b, kv_b, tokens = step_bytes(w0, base)
     plan = base.plan()
+    recall = approx_recall(w0, base) if mode == V.VX_TOPK_APPROX else None
+    if recall:
+        log(f"approximate top-k recall@k: mean {recall['mean']:.4f}, min {recall['min']:.4f} "
+            f"over {recall['segments']} segments")
     total_b = cent_b + kv_b
     R = a.replicas or max(1, min(16, math.ceil(1.0e9 / total_b)))
     log(f"step touches {total_b / 1e6:.1f} MB (centroids {cent_b / 1e6:.1f}, selected KV "
@@ -285,9 +346,12 @@ def main():
         "stage_us": stage_us,
         "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBPS, "traffic": None, "kernel": dom,
+                     "frac": achieved / PEAK_GBPS,
+                     "traffic": measured_traffic(a.workload, dom), "kernel": dom,
                      "bytes_per_launch": stage_bytes[dom]},
     }
+    if recall:
+        result["approx_recall_at_k"] = recall
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w0, base, a.cpu_seconds)
