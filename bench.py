@@ -141,19 +141,19 @@ def sources_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from profiles/traffic.json (rocprofv3
-    FETCH_SIZE and WRITE_SIZE passes, calibrated), or None when they were
-    taken on other kernel sources or not at all."""
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of a stage's kernels from profiles/traffic.json
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, calibrated), or None when they
+    were taken on other kernel sources or not at all."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     e = t.get("workloads", {}).get(workload)
-    if not e or e.get("kernel") != kernel or e.get("sources_sha256") != sources_hash():
+    if not e or e.get("sources_sha256") != sources_hash() or stage not in e.get("stages", {}):
         return None
-    return e["hbm_bytes_per_launch"]
+    return e["stages"][stage]["hbm_bytes_per_launch"]
 
 
 def approx_recall(w, step):
