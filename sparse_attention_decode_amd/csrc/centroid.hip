@@ -18,14 +18,18 @@ namespace {
 template <typename T> struct Pair;
 template <> struct Pair<float> {
   using raw = float2;
+  static __device__ __forceinline__ float2 load(const float* p) { return *(const float2*)p; }
+  static __device__ __forceinline__ float2 widen(float2 w) { return w; }
   static __device__ __forceinline__ float2 get(const float* p) { return *(const float2*)p; }
   static __device__ __forceinline__ void put(float* p, float2 v) { *(float2*)p = v; }
 };
 template <> struct Pair<uint16_t> {
-  static __device__ __forceinline__ float2 get(const uint16_t* p) {
-    uint32_t w = *(const uint32_t*)p;
+  using raw = uint32_t;  // two bf16
+  static __device__ __forceinline__ uint32_t load(const uint16_t* p) { return *(const uint32_t*)p; }
+  static __device__ __forceinline__ float2 widen(uint32_t w) {
     return make_float2(bf16_lo(w), bf16_hi(w));
   }
+  static __device__ __forceinline__ float2 get(const uint16_t* p) { return widen(load(p)); }
   static __device__ __forceinline__ void put(uint16_t* p, float2 v) {
     uint32_t w = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
     *(uint32_t*)p = w;
@@ -34,29 +38,31 @@ template <> struct Pair<uint16_t> {
 
 // Recompute the centroid of one page for the dim pair owned by `pair`.
 // `nv` valid tokens; if `slot` >= 0 that token's value comes from `fresh`
-// (the just-appended key) instead of memory.
+// (the just-appended key) instead of memory. Every token's load is issued
+// in batches of 32 (bf16) or 16 (fp32) tokens before the batch is added; the
+// sums still run in token order.
 template <typename KV>
 __device__ __forceinline__ void refresh_pair(const KV* __restrict__ kp, int P, int hkv, int dk,
                                              int pid, int nv, int pair, int slot, float2 fresh,
                                              float* __restrict__ cent,
                                              uint16_t* __restrict__ cent_bf16) {
+  constexpr int kTok = sizeof(KV) == 2 ? 32 : 16;  // 32 raw registers either way
   const int g = pair / (dk / 2);
   const int d = 2 * (pair % (dk / 2));
   const KV* base = kp + ((size_t)pid * hkv + g) * (size_t)P * dk + d;
-  // Loads of 16 tokens are issued together; the sums still run in token order.
   float s0 = 0.f, s1 = 0.f;
-  for (int t0 = 0; t0 < nv; t0 += 16) {
-    float2 x[16];
+  for (int t0 = 0; t0 < nv; t0 += kTok) {
+    typename Pair<KV>::raw x[kTok];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kTok; ++u) {
       const int t = t0 + u;
-      x[u] = t < nv ? Pair<KV>::get(base + (size_t)t * dk) : make_float2(0.f, 0.f);
+      if (t < nv) x[u] = Pair<KV>::load(base + (size_t)t * dk);
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kTok; ++u) {
       const int t = t0 + u;
       if (t < nv) {
-        const float2 v = (t == slot) ? fresh : x[u];
+        const float2 v = (t == slot) ? fresh : Pair<KV>::widen(x[u]);
         s0 += v.x;
         s1 += v.y;
       }

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                                                              const uint16_t* __restrict__ vp,
                                                              float qscale, float* __restrict__ out,
                                                              float* __restrict__ lse) {
-  // keys [cap_keys + 256], then the physical page of every entry [cap_keys]
+  // keys [cap_keys + kSelectExtraWords], then the physical page of every entry [cap_keys]
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   __shared__ int32_t sel_l[kMaxPagesPerSplit];
   __shared__ int32_t cnt_l;
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   static_assert(kMaxPagesPerSplit <= 64 * NW, "one page-list entry per thread");
 
   const int seg = blockIdx.x;
-  int* pid_l = (int*)(dyn + a.cap_keys + 256);
+  int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
   index_segment<uint16_t, uint16_t, 128, G, NW>(a, seg, dyn, pid_l, sel_l, &cnt_l);
 
   const Meta& m = a.m;
@@ -54,7 +54,7 @@ template <int G, int P>
 hipError_t launch_g(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
                     int max_pages, hipStream_t s) {
   dim3 grid(a.m.batch * a.hkv);
-  const size_t lds = (size_t)(2 * a.cap_keys + 256) * sizeof(uint32_t);
+  const size_t lds = (size_t)(2 * a.cap_keys + kSelectExtraWords) * sizeof(uint32_t);
   if constexpr (G <= 4) {
     if (gqa_attn_waves(G, max_pages) == 16) {
       hipLaunchKernelGGL((decode_seg_kernel<G, P, 16>), grid, dim3(1024), lds, s, a,

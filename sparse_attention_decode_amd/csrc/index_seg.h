@@ -46,8 +46,8 @@ struct SegArgs {
   int cap_keys;
 };
 
-// The index of segment seg = b * Hkv + g by a block of NW waves. keys: LDS,
-// cap_keys + 256 words (16-byte aligned). pid_lds (nullable, cap_keys ints)
+// The index of segment seg = b * Hkv + g by a block of NW waves (NW <= 16).
+// keys: LDS, cap_keys + kSelectExtraWords words (16-byte aligned). pid_lds (nullable, cap_keys ints)
 // receives the physical page of every entry in use; sel_lds / count_lds
 // (nullable) a copy of the selection. Ends after the selection is written;
 // its LDS copies are visible to the block after a barrier.
@@ -58,6 +58,7 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   constexpr int PPI = 64 / W;  // pages per load instruction
   constexpr int kChunk = kSegChunk * PPI;
   static_assert(kChunk <= 64, "one page id per lane");
+  static_assert(NW <= 16, "block select reduction words");
 
   const Meta& m = a.m;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -164,10 +165,15 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
     emit(p, c4, own);
   }
   __syncthreads();  // every key of the segment is in LDS
-  if (w == 0)
-    wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode,
-                     a.mode == VX_TOPK_APPROX ? a.rnd[seg] : 0u, a.sel + (size_t)seg * a.stride,
-                     a.stride, a.sel_count + seg, lane, sel_lds, count_lds);
+  const uint32_t rnd = a.mode == VX_TOPK_APPROX ? a.rnd[seg] : 0u;
+  if (n > kBlockSelectMin)
+    block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + 256, n, a.k, a.n_sink,
+                          a.n_local, a.mode, rnd, a.sel + (size_t)seg * a.stride, a.stride,
+                          a.sel_count + seg, sel_lds, count_lds);
+  else if (w == 0)
+    wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd,
+                     a.sel + (size_t)seg * a.stride, a.stride, a.sel_count + seg, lane, sel_lds,
+                     count_lds);
 }
 
 }  // namespace vx

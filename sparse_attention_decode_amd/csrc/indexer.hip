@@ -11,7 +11,7 @@ namespace {
 
 template <typename QT, typename KV, int DK, int GG, int NW>
 __global__ __launch_bounds__(64 * NW) void index_seg_kernel(SegArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // cap_keys + 256 words
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // cap_keys + kSelectExtraWords
   index_segment<QT, KV, DK, GG, NW>(a, blockIdx.x, keys, nullptr, nullptr, nullptr);
 }
 
@@ -19,7 +19,7 @@ template <typename QT, typename KV, int DK, int NW>
 hipError_t launch_nw(const SegArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   dim3 grid(a.m.batch * a.hkv), block(64 * NW);
-  const size_t lds = (size_t)(a.cap_keys + 256) * sizeof(uint32_t);
+  const size_t lds = (size_t)(a.cap_keys + kSelectExtraWords) * sizeof(uint32_t);
 #define VX_SEG(GG) hipLaunchKernelGGL((index_seg_kernel<QT, KV, DK, GG, NW>), grid, block, lds, s, a)
   switch (G) {
     case 1: VX_SEG(1); break;

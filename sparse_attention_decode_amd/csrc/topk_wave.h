@@ -107,6 +107,54 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t r, in
   return out;
 }
 
+// Ordered compaction (ascending page index) of the survivors: forced pages,
+// candidates with (key & mask) > prefix, and r of those with (key & mask) ==
+// prefix taken in index order from offset `off`, cyclic over the `members`
+// of that tie group. One wave; ballot + mbcnt ranks keep the order.
+__device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, int n, int n_sink,
+                                             int n_local, uint32_t prefix, uint32_t mask,
+                                             uint32_t r, uint32_t off, uint32_t members,
+                                             int32_t* __restrict__ out, int stride,
+                                             int32_t* __restrict__ count_out, int lane,
+                                             int32_t* __restrict__ out_lds,
+                                             int32_t* __restrict__ count_lds) {
+  uint32_t written = 0, tie_seen = 0;
+  for (int base0 = 0; base0 < n; base0 += 64 * kU) {
+    uint32_t kvs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base0 + 64 * u + lane;
+      kvs[u] = i < n ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+    const int i = base0 + 64 * u + lane;
+    const bool in = i < n;
+    const uint32_t kv = kvs[u];
+    const bool forced = in && (i < n_sink || i >= n - n_local);
+    const bool cand = kv != 0u;
+    const bool above = cand && (kv & mask) > prefix;
+    const bool tie = cand && (kv & mask) == prefix;
+    const unsigned long long tmask = __ballot(tie);
+    const uint32_t trank = tie_seen + rank_below(tmask);
+    tie_seen += (uint32_t)__popcll(tmask);
+    bool take = forced || above;
+    if (tie && members) take = take || ((trank + members - off) % members) < r;
+    const unsigned long long smask = __ballot(take);
+    if (take) {
+      out[written + rank_below(smask)] = i;
+      if (out_lds) out_lds[written + rank_below(smask)] = i;
+    }
+    written += (uint32_t)__popcll(smask);
+    }
+  }
+  for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
+  if (lane == 0) {
+    *count_out = (int32_t)written;
+    if (count_lds) *count_lds = (int32_t)written;
+  }
+}
+
 }  // namespace topk_detail
 
 // Select for one segment whose n keys are already in this wave's LDS
@@ -215,42 +263,101 @@ __device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
     }
   }
 
-  // Ordered compaction (ascending page index).
-  uint32_t written = 0, tie_seen = 0;
-  for (int base0 = 0; base0 < n; base0 += 64 * kU) {
-    uint32_t kvs[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = base0 + 64 * u + lane;
-      kvs[u] = i < n ? keys[i] : 0u;
+  topk_detail::wave_compact(keys, n, n_sink, n_local, prefix, mask, r, off, members, out, stride,
+                            count_out, lane, out_lds, count_lds);
+}
+
+// Select for one segment with all NW waves of a block (every thread calls
+// it; n is the same for all). keys / hist as for wave_select_keys; `red` is
+// 2 * NW words of LDS. The min / max sweep and each digit pass's histogram
+// are shared by the waves; every wave reads the finished histogram and finds
+// the same digit, so no broadcast is needed; wave 0 compacts. Same result as
+// wave_select_keys: the selection rule has one answer.
+template <int NW>
+__device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
+                                                  uint32_t* __restrict__ hist,
+                                                  uint32_t* __restrict__ red, int n, int k,
+                                                  int n_sink, int n_local, int mode,
+                                                  uint32_t rnd_word, int32_t* __restrict__ out,
+                                                  int stride, int32_t* __restrict__ count_out,
+                                                  int32_t* __restrict__ out_lds = nullptr,
+                                                  int32_t* __restrict__ count_lds = nullptr) {
+  using namespace topk_detail;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nf = min(n, n_sink + n_local);
+  const int nc = n - nf;
+  const int kk = min(k, nc);
+  uint32_t prefix = 0, mask = 0, r = (uint32_t)kk, off = 0, members = (uint32_t)nc;
+  if (kk > 0 && kk < nc) {
+    uint32_t kmax = 0u, kminc = 0u;
+    for (int i = t; i < n; i += 64 * NW) {
+      const uint32_t kv = keys[i];
+      if (kv) { kmax = max(kmax, kv); kminc = max(kminc, ~kv); }
     }
+    kmax = wave_max(kmax);
+    kminc = wave_max(kminc);
+    if (lane == 0) { red[w] = kmax; red[NW + w] = kminc; }
+    __syncthreads();
+    kmax = 0u;
+    kminc = 0u;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-    const int i = base0 + 64 * u + lane;
-    const bool in = i < n;
-    const uint32_t kv = kvs[u];
-    const bool forced = in && (i < n_sink || i >= n - n_local);
-    const bool cand = kv != 0u;
-    const bool above = cand && (kv & mask) > prefix;
-    const bool tie = cand && (kv & mask) == prefix;
-    const unsigned long long tmask = __ballot(tie);
-    const uint32_t trank = tie_seen + rank_below(tmask);
-    tie_seen += (uint32_t)__popcll(tmask);
-    bool take = forced || above;
-    if (tie && members) take = take || ((trank + members - off) % members) < r;
-    const unsigned long long smask = __ballot(take);
-    if (take) {
-      out[written + rank_below(smask)] = i;
-      if (out_lds) out_lds[written + rank_below(smask)] = i;
-    }
-    written += (uint32_t)__popcll(smask);
+    for (int v = 0; v < NW; ++v) { kmax = max(kmax, red[v]); kminc = max(kminc, red[NW + v]); }
+    const uint32_t kmin = ~kminc;
+    if (mode == VX_TOPK_APPROX) {
+      const float mn = key_score(kmin), mx = key_score(kmax);
+      const float wdt = __fsub_rn(mx, mn);
+      const bool spread = wdt > 0.f;
+      const float inv = spread ? __fdiv_rn(256.f, wdt) : 0.f;
+      if (t < 64) *(uint4*)(hist + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+      for (int i = t; i < n; i += 64 * NW) {
+        const uint32_t kv = keys[i];
+        if (kv) {
+          uint32_t bk = 0;
+          if (spread) {
+            const float x = floorf(__fmul_rn(__fsub_rn(key_score(kv), mn), inv));
+            bk = x >= 255.f ? 255u : (uint32_t)x;
+          }
+          keys[i] = (bk << 24) | 1u;  // nonzero; digit 3 is the bucket
+          atomicAdd(&hist[bk], 1u);
+        }
+      }
+      __syncthreads();
+      const Digit dg = find_digit(hist, r, lane);
+      prefix = dg.d << 24;
+      mask = 0xff000000u;
+      r -= dg.above;
+      members = dg.count;
+      off = members ? rnd_word % members : 0u;
+    } else if (kmin == kmax) {
+      prefix = kmin;  // every candidate ties: index order decides
+      mask = 0xffffffffu;
+    } else {
+      const int top = __clz(kmin ^ kmax) / 8;
+      mask = top ? 0xffffffffu << (32 - 8 * top) : 0u;
+      prefix = kmin & mask;
+      for (int shift = 24 - 8 * top; shift >= 0; shift -= 8) {
+        __syncthreads();  // the previous pass's readers are done with hist
+        if (t < 64) *(uint4*)(hist + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+        for (int i = t; i < n; i += 64 * NW) {
+          const uint32_t kv = keys[i];
+          if (kv && (kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        const Digit dg = find_digit(hist, r, lane);
+        prefix |= dg.d << shift;
+        mask |= 255u << shift;
+        r -= dg.above;
+        members = dg.count;
+        if (dg.count == r) break;  // same decision in every wave
+      }
     }
   }
-  for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
-  if (lane == 0) {
-    *count_out = (int32_t)written;
-    if (count_lds) *count_lds = (int32_t)written;
-  }
+  __syncthreads();  // keys final, histogram readers done
+  if (w == 0)
+    wave_compact(keys, n, n_sink, n_local, prefix, mask, r, off, members, out, stride, count_out,
+                 lane, out_lds, count_lds);
 }
 
 // Select for one segment: `sc` points at its n scores, `keys` / `hist` at

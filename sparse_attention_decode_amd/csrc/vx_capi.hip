@@ -208,7 +208,7 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   out->pages_per_split = pps;
   out->score_pages_per_block = 4 * kScorePagesPerWave;
   out->score_blocks = (p->total_pages + out->score_pages_per_block - 1) / out->score_pages_per_block;
-  out->topk_threads = 64 * topk_waves(p->max_pages);
+  out->topk_threads = p->max_pages > vx::kBlockSelectMin ? 512 : 64;
   const int hq = g->num_q_heads, dv = g->head_dim_v;
   size_t ws = 0;
   if (S > 1) {

@@ -211,6 +211,11 @@ inline int gqa_attn_waves(int G, int max_pages) {
 // Largest page capacity for which the whole-step kernel keeps every entry's
 // key and physical page in LDS.
 constexpr int kMaxFusedStepPages = 4096;
+// LDS words a segment's selection needs besides its keys: the 256-word
+// histogram and the block select's 2 * 16 reduction words.
+constexpr int kSelectExtraWords = 256 + 32;
+// Segments longer than this are selected by every wave of the block.
+constexpr int kBlockSelectMin = 256;
 // Largest per-sequence page count the top-k supports (LDS resident keys).
 constexpr int kMaxTopkPages = 16000;
 

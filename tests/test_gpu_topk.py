@@ -90,8 +90,8 @@ def test_topk_bit_exact(k, n_sink, n_local, mode):
             assert cnt[b, g] == int((want >= 0).sum())
 
 
-def test_topk_large_segments_one_wave_per_block():
-    """Segments past the 4-waves-per-block LDS budget (max_pages > ~3800)."""
+def test_topk_large_segments():
+    """Long segments (one block per segment) next to a 3-page one."""
     hkv, batch = 2, 3
     rng = np.random.default_rng(5)
     ns = np.array([5000, 3, 4100])
