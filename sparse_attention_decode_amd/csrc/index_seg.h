@@ -120,8 +120,13 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
       for (int t = 0; t < kSegChunk; ++t) {
         const int p = cb + t * PPI + sub;
         const int pid = __shfl(my_pid, t * PPI + sub);
-        r[t] = p < pw1 ? *(const float4*)(a.cent + ((size_t)pid * a.hkv + g) * DK + 4 * dl)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        // centroid rows are streamed once per step: non-temporal loads
+        const u32x4 raw =
+            p < pw1 ? __builtin_nontemporal_load(
+                          (const u32x4*)(a.cent + ((size_t)pid * a.hkv + g) * DK + 4 * dl))
+                    : u32x4{0u, 0u, 0u, 0u};
+        r[t] = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
+                           __uint_as_float(raw.w));
       }
 #pragma unroll
       for (int t = 0; t < kSegChunk; ++t) {

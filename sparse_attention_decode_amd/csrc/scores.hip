@@ -136,7 +136,11 @@ __global__ __launch_bounds__(64 * kWaves) void index_gqa_kernel(IndexArgs a) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int ch = i * 64 + lane;
-        rows[u][i] = (FULL || ch < nchunk) ? r[ch] : make_float4(0.f, 0.f, 0.f, 0.f);
+        // centroid rows are streamed once per step: non-temporal loads
+        const u32x4 raw = (FULL || ch < nchunk) ? __builtin_nontemporal_load((const u32x4*)(r + ch))
+                                                : u32x4{0u, 0u, 0u, 0u};
+        rows[u][i] = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y),
+                                 __uint_as_float(raw.z), __uint_as_float(raw.w));
       }
     }
   }
