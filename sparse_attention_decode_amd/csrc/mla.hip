@@ -33,26 +33,65 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 
 // ------------------------------------------------------------------ scoring
 // grid (ceil(max_pages / 64), B), 4 waves; wave w scores the 16 pages
-// [64 * blockIdx.x + 16 w, +16) of sequence blockIdx.y.
+// [64 * blockIdx.x + 16 w, +16) of sequence blockIdx.y. With `refresh`, the
+// block holding a sequence's newest page first recomputes that page's
+// centroid (fp32 and its bf16 copy) from its keys, in token order with one
+// IEEE divide per column, the cache stage's arithmetic; the barrier before
+// scoring orders it before the page's bf16 row is read.
 template <int MT>
 __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ cent,
+                                                         const uint16_t* __restrict__ kp,
+                                                         float* __restrict__ cent32,
+                                                         uint16_t* __restrict__ cent, int refresh,
                                                          float scale, float* __restrict__ scores) {
+  constexpr int kQPer = (16 * MT * (DK / 8) + 255) / 256;  // query vectors per thread
   __shared__ __attribute__((aligned(16))) uint16_t qs[16 * MT * ROW];
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
   const int row0 = m.indptr[b];
   const int cap = m.indptr[b + 1] - row0;
-  int n = (seq_len_clamped(m, b) + m.page_size - 1) / m.page_size;
+  const int L = seq_len_clamped(m, b);
+  int n = (L + m.page_size - 1) / m.page_size;
   n = n > cap ? cap : n;
   const int blk0 = blockIdx.x * 64;
   if (blk0 >= n) return;  // whole block: no barrier reached
 
-  // Stage this sequence's query rows (16 * MT heads x 576) in LDS.
+  // This sequence's query rows (16 * MT heads x 576): all loads issued, then stored in LDS.
   const uint16_t* qb = q + (size_t)b * (16 * MT) * DK;
-  for (int c = threadIdx.x; c < 16 * MT * (DK / 8); c += 256) {
-    const int h = c / (DK / 8), k8 = c % (DK / 8);
-    *(u32x4*)(qs + h * ROW + 8 * k8) = *(const u32x4*)(qb + h * DK + 8 * k8);
+  u32x4 qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int c = t + 256 * u;
+    if (c < 16 * MT * (DK / 8)) qv[u] = *(const u32x4*)(qb + (c / (DK / 8)) * DK + 8 * (c % (DK / 8)));
+  }
+  if (refresh && n - 1 < blk0 + 64) {  // the newest page is in this block's range
+    const int P = m.page_size;
+    const int pn = n - 1;
+    const int nv = min(P, L - pn * P);
+    const int pid = phys_page(m, row0 + pn);
+    const uint16_t* kb = kp + (size_t)pid * P * DK;
+    for (int pr = t; pr < DK / 2; pr += 256) {
+      float s0 = 0.f, s1 = 0.f;
+      for (int t0 = 0; t0 < nv; t0 += 32) {
+        uint32_t x[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          if (t0 + u < nv) x[u] = *(const uint32_t*)(kb + (size_t)(t0 + u) * DK + 2 * pr);
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          if (t0 + u < nv) { s0 += bf16_lo(x[u]); s1 += bf16_hi(x[u]); }
+      }
+      const float c0 = s0 / (float)nv, c1 = s1 / (float)nv;
+      const size_t o = (size_t)pid * DK + 2 * pr;
+      *(float2*)(cent32 + o) = make_float2(c0, c1);
+      *(uint32_t*)(cent + o) = (uint32_t)f32_to_bf16(c0) | ((uint32_t)f32_to_bf16(c1) << 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int c = t + 256 * u;
+    if (c < 16 * MT * (DK / 8)) *(u32x4*)(qs + (c / (DK / 8)) * ROW + 8 * (c % (DK / 8))) = qv[u];
   }
   __syncthreads();
 
@@ -316,16 +355,17 @@ __global__ __launch_bounds__(64 * kMlaWaves) void attn_mla_kernel(
 }  // namespace
 
 hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,
-                                   const uint16_t* cent_bf16, float scale, float* scores,
-                                   int max_pages, hipStream_t s) {
+                                   const void* k_pool, float* cent32, uint16_t* cent_bf16,
+                                   int refresh, float scale, float* scores, int max_pages,
+                                   hipStream_t s) {
   if (m.nnz == 0 || m.batch == 0) return hipSuccess;
   dim3 grid((max_pages + 63) / 64, m.batch), block(256);
   if (g.num_q_heads == 32)
-    hipLaunchKernelGGL(scores_mla_kernel<2>, grid, block, 0, s, m, (const uint16_t*)q, cent_bf16,
-                       scale, scores);
+    hipLaunchKernelGGL(scores_mla_kernel<2>, grid, block, 0, s, m, (const uint16_t*)q,
+                       (const uint16_t*)k_pool, cent32, cent_bf16, refresh, scale, scores);
   else if (g.num_q_heads == 16)
-    hipLaunchKernelGGL(scores_mla_kernel<1>, grid, block, 0, s, m, (const uint16_t*)q, cent_bf16,
-                       scale, scores);
+    hipLaunchKernelGGL(scores_mla_kernel<1>, grid, block, 0, s, m, (const uint16_t*)q,
+                       (const uint16_t*)k_pool, cent32, cent_bf16, refresh, scale, scores);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

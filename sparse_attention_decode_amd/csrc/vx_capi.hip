@@ -289,8 +289,9 @@ vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom, const void*
   const vx::Meta m = meta_of(pages);
   hipError_t e;
   if (geom->mla)
-    e = vx::launch_scores_mla_sized(m, *geom, q, (const uint16_t*)centroids, score_scale, scores,
-                                    pages->max_pages, stream);
+    e = vx::launch_scores_mla_sized(m, *geom, q, nullptr, nullptr,
+                                    const_cast<uint16_t*>((const uint16_t*)centroids), 0,
+                                    score_scale, scores, pages->max_pages, stream);
   else
     e = vx::launch_scores_gqa(m, *geom, q, nullptr, const_cast<float*>((const float*)centroids),
                               nullptr, 0, score_scale, scores, stream);
@@ -332,13 +333,9 @@ vx_status vx_index_pages(const vx_pages* pages, const vx_geom* geom, const void*
   hipError_t e = hipSuccess;
   if (pages->total_pages > 0) {
     if (geom->mla) {
-      if (refresh_newest) {
-        e = vx::launch_centroid_append(m, *geom, const_cast<void*>(k_pool), nullptr, nullptr,
-                                       nullptr, nullptr, centroids, (uint16_t*)cent_bf16, stream);
-        if (e != hipSuccess) return hip_status(e, "centroid kernel launch");
-      }
-      e = vx::launch_scores_mla_sized(m, *geom, q, (const uint16_t*)cent_bf16, score_scale, scores,
-                                      pages->max_pages, stream);
+      e = vx::launch_scores_mla_sized(m, *geom, q, k_pool, centroids, (uint16_t*)cent_bf16,
+                                      refresh_newest, score_scale, scores, pages->max_pages,
+                                      stream);
     } else {
       e = vx::launch_index_gqa(m, *geom, q, k_pool, centroids, (uint16_t*)cent_bf16,
                                refresh_newest, score_scale, scores, k, n_sink, n_local, mode,

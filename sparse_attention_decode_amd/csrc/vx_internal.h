@@ -178,9 +178,12 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
                                   hipStream_t s);
+// MLA scores on the bf16 centroids; refresh != 0 first recomputes each
+// sequence's newest page (fp32 centroid and its bf16 copy) from k_pool.
 hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,
-                                   const uint16_t* cent_bf16, float scale, float* scores,
-                                   int max_pages, hipStream_t s);
+                                   const void* k_pool, float* cent32, uint16_t* cent_bf16,
+                                   int refresh, float scale, float* scores, int max_pages,
+                                   hipStream_t s);
 hipError_t launch_topk_sized(const Meta& m, int hkv, const float* scores, int k, int n_sink,
                              int n_local, int mode, const uint32_t* rand_u32, int32_t* sel,
                              int sel_stride, int32_t* sel_count, int max_pages,
