@@ -159,20 +159,12 @@ def measured_traffic(workload, stage):
     return e["stages"][stage]["hbm_bytes_per_launch"]
 
 
-def approx_recall(w, step):
-    """recall@k of the approximate selection against the exact one on the
-    same scores: per (sequence, KV head), |approx ∩ exact| / min(k, candidates),
-    forced pages excluded."""
-    import torch
-    from sparse_attention_decode_amd import binding as V
+def overlap(w, step, sel_a, cnt_a, sel_b, cnt_b):
+    """Mean and minimum over (sequence, KV head) of |A ∩ B| / min(k, candidates),
+    forced pages excluded: the recall@k of selection A against selection B."""
     s = w.spec
-    sel_e = torch.full_like(step.sel, -1)
-    cnt_e = torch.zeros_like(step.sel_count)
-    V.vx_topk_pages(step.pages, s.num_kv_heads, step.scores, step.k, step.n_sink, step.n_local,
-                    V.VX_TOPK_EXACT, None, sel_e, step.k_out, cnt_e)
-    torch.cuda.synchronize()
-    a, ca = step.sel.cpu().numpy(), step.sel_count.cpu().numpy()
-    e, ce = sel_e.cpu().numpy(), cnt_e.cpu().numpy()
+    a, ca = sel_a.cpu().numpy(), cnt_a.cpu().numpy()
+    e, ce = sel_b.cpu().numpy(), cnt_b.cpu().numpy()
     rec = []
     for b in range(s.batch):
         n = w.n_pages(b)
@@ -185,6 +177,32 @@ def approx_recall(w, step):
             se = set(e[b, g, :ce[b, g]].tolist()) - forced
             rec.append(len(sa & se) / want)
     return {"mean": float(np.mean(rec)), "min": float(np.min(rec)), "segments": len(rec)}
+
+
+def approx_recall(w, step):
+    """recall@k of the approximate selection against the exact one on the
+    same scores."""
+    import torch
+    from sparse_attention_decode_amd import binding as V
+    s = w.spec
+    sel_e = torch.full_like(step.sel, -1)
+    cnt_e = torch.zeros_like(step.sel_count)
+    V.vx_topk_pages(step.pages, s.num_kv_heads, step.scores, step.k, step.n_sink, step.n_local,
+                    V.VX_TOPK_EXACT, None, sel_e, step.k_out, cnt_e)
+    torch.cuda.synchronize()
+    return overlap(w, step, step.sel, step.sel_count, sel_e, cnt_e)
+
+
+def rope_unaware_recall(w, step):
+    """MLA: recall@k of the selection scored on the 512 latent columns only
+    against the rope-aware selection (all 576 columns)."""
+    import torch
+    from sparse_attention_decode_amd.step import DecodeStep
+    alt = DecodeStep(w, score_dim=512)
+    alt.rebuild_centroids()
+    alt.index(refresh=False)
+    torch.cuda.synchronize()
+    return overlap(w, step, alt.sel, alt.sel_count, step.sel, step.sel_count)
 
 
 def copy_calibration():
@@ -288,6 +306,10 @@ def main():
     if recall:
         log(f"approximate top-k recall@k: mean {recall['mean']:.4f}, min {recall['min']:.4f} "
             f"over {recall['segments']} segments")
+    rope = rope_unaware_recall(w0, base) if sp.mla and mode == V.VX_TOPK_EXACT else None
+    if rope:
+        log(f"rope-unaware MLA selection vs rope-aware, recall@k: mean {rope['mean']:.4f}, "
+            f"min {rope['min']:.4f}")
     total_b = cent_b + kv_b
     R = a.replicas or max(1, min(16, math.ceil(1.0e9 / total_b)))
     log(f"step touches {total_b / 1e6:.1f} MB (centroids {cent_b / 1e6:.1f}, selected KV "
@@ -414,6 +436,8 @@ def main():
     }
     if recall:
         result["approx_recall_at_k"] = recall
+    if rope:
+        result["mla_rope_unaware_recall_at_k"] = rope
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w0, base, a.cpu_seconds)

@@ -104,6 +104,11 @@ typedef struct vx_geom {
   int32_t mla;
   vx_dtype q_dtype;
   vx_dtype kv_dtype;
+  /* Columns the indexer scores: 0 or head_dim_k = all of them. MLA also
+   * takes 512: the latent columns only, a rope-unaware indexer (Vortex paper
+   * note, "Key results > MLA": routing on the rope part matters; this option
+   * measures how much). Attention always uses every column. */
+  int32_t score_dim;
 } vx_geom;
 
 /* Launch plan chosen by the workload planner (host only). */

@@ -91,15 +91,21 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def page_scores(q: np.ndarray, cent: np.ndarray, num_kv_heads: int,
-                scale: float) -> np.ndarray:
+                scale: float, score_dim: int = None) -> np.ndarray:
     """Indexer scoring: query times centroids.
 
     Vortex paper note, "System design > 1. vFlow": the indexer scores blocks
     by a matrix product of the query with the cached centroids. Heads of one
     GQA group share their KV head's pages, so the group's query heads are
     summed: s[g][p] = scale * sum_{h in group g} sum_d q[h][d] cent[p][g][d].
+    ``score_dim`` (optional) keeps only the first score_dim columns of q and
+    the centroids: the rope-unaware MLA indexer of "Key results > MLA" scores
+    on the 512 latent columns and ignores the 64 rope columns.
     Returns [Hkv][n] float64.
     """
+    if score_dim is not None:
+        q = q[:, :score_dim]
+        cent = cent[..., :score_dim]
     Hq = q.shape[0]
     G = Hq // num_kv_heads
     n = cent.shape[0]
@@ -260,16 +266,17 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_len: int,
 def decode_sequence(seq: dict, *, page_size: int, num_kv_heads: int, k: int,
                     n_sink: int, n_local: int, score_scale: float,
                     sm_scale: float, mla: bool = False, head_dim_v: int = None,
-                    approx: bool = False) -> dict:
+                    approx: bool = False, score_dim: int = None) -> dict:
     """The whole step for one sequence: cache stage, scoring, selection,
     attention. ``seq`` holds q, k, v (v None for MLA), seq_len and rand_u32
-    ([Hkv] uint32 draws for the approximate selection)."""
+    ([Hkv] uint32 draws for the approximate selection); ``score_dim`` as in
+    page_scores."""
     q, kk, vv, L = seq["q"], seq["k"], seq["v"], seq["seq_len"]
     if mla:
         vv = kk[..., :head_dim_v]
     cent = centroids(kk, L, page_size)
     score_cent = round_to_bf16(cent) if mla else cent
-    scores = page_scores(q, score_cent, num_kv_heads, score_scale)
+    scores = page_scores(q, score_cent, num_kv_heads, score_scale, score_dim)
     k_out = k + n_sink + n_local
     sel = np.full((num_kv_heads, k_out), -1, dtype=np.int64)
     for g in range(num_kv_heads):

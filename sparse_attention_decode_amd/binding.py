@@ -45,7 +45,7 @@ class VxPages(ctypes.Structure):
 class VxGeom(ctypes.Structure):
     _fields_ = [("num_q_heads", c_int32), ("num_kv_heads", c_int32), ("head_dim_k", c_int32),
                 ("head_dim_v", c_int32), ("mla", c_int32), ("q_dtype", c_int32),
-                ("kv_dtype", c_int32)]
+                ("kv_dtype", c_int32), ("score_dim", c_int32)]
 
 
 class VxPlan(ctypes.Structure):
@@ -136,10 +136,12 @@ def make_pages(batch, page_size, num_pool_pages, total_pages, max_pages, indptr,
                    _ptr(page_ids), _ptr(seq_lens))
 
 
-def make_geom(num_q_heads, num_kv_heads, head_dim_k, head_dim_v, mla, q_dtype, kv_dtype) -> VxGeom:
+def make_geom(num_q_heads, num_kv_heads, head_dim_k, head_dim_v, mla, q_dtype, kv_dtype,
+              score_dim: int = 0) -> VxGeom:
     q = q_dtype if isinstance(q_dtype, int) else dtype_code(q_dtype)
     kv = kv_dtype if isinstance(kv_dtype, int) else dtype_code(kv_dtype)
-    return VxGeom(num_q_heads, num_kv_heads, head_dim_k, head_dim_v, int(mla), q, kv)
+    return VxGeom(num_q_heads, num_kv_heads, head_dim_k, head_dim_v, int(mla), q, kv,
+                  int(score_dim))
 
 
 def vx_centroid_update(pages: VxPages, geom: VxGeom, k_pool, v_pool, first_token, k_new, v_new,

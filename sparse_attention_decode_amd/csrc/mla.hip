@@ -38,7 +38,7 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 // centroid (fp32 and its bf16 copy) from its keys, in token order with one
 // IEEE divide per column, the cache stage's arithmetic; the barrier before
 // scoring orders it before the page's bf16 row is read.
-template <int MT>
+template <int MT, int KS>
 __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ kp,
                                                          float* __restrict__ cent32,
@@ -102,9 +102,9 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
   const bool valid = p < n;
   const uint16_t* crow = cent + (size_t)(valid ? phys_page(m, row0 + p) : 0) * DK + 8 * q4;
 
-  u32x4 bf[KSTEPS];
+  u32x4 bf[KS];  // KS k steps of 32 columns: 18 = all 576, 16 = the 512 latent ones
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
     bf[ks] = valid ? *(const u32x4*)(crow + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
 
   f32x4 acc[MT];
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
     acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t* arow = qs + (16 * mt + col) * ROW + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) acc[mt] = mfma(*(const u32x4*)(arow + 32 * ks), bf[ks], acc[mt]);
+    for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma(*(const u32x4*)(arow + 32 * ks), bf[ks], acc[mt]);
   }
   float s = 0.f;
 #pragma unroll
@@ -360,14 +360,18 @@ hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* 
                                    hipStream_t s) {
   if (m.nnz == 0 || m.batch == 0) return hipSuccess;
   dim3 grid((max_pages + 63) / 64, m.batch), block(256);
-  if (g.num_q_heads == 32)
-    hipLaunchKernelGGL(scores_mla_kernel<2>, grid, block, 0, s, m, (const uint16_t*)q,
-                       (const uint16_t*)k_pool, cent32, cent_bf16, refresh, scale, scores);
-  else if (g.num_q_heads == 16)
-    hipLaunchKernelGGL(scores_mla_kernel<1>, grid, block, 0, s, m, (const uint16_t*)q,
-                       (const uint16_t*)k_pool, cent32, cent_bf16, refresh, scale, scores);
-  else
+  const bool latent_only = g.score_dim == DV;
+#define VX_MLA_SC(MT, KS)                                                                     \
+  hipLaunchKernelGGL((scores_mla_kernel<MT, KS>), grid, block, 0, s, m, (const uint16_t*)q,  \
+                     (const uint16_t*)k_pool, cent32, cent_bf16, refresh, scale, scores)
+  if (g.num_q_heads == 32) {
+    if (latent_only) VX_MLA_SC(2, DV / 32); else VX_MLA_SC(2, KSTEPS);
+  } else if (g.num_q_heads == 16) {
+    if (latent_only) VX_MLA_SC(1, DV / 32); else VX_MLA_SC(1, KSTEPS);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef VX_MLA_SC
   return hipGetLastError();
 }
 

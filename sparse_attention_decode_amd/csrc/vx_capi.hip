@@ -65,6 +65,9 @@ vx_status check_geom(const vx_geom* g) {
              "MLA geometry %dx%d (supported: 576 key, 512 value)", g->head_dim_k, g->head_dim_v);
     VX_CHECK(g->q_dtype == VX_BF16 && g->kv_dtype == VX_BF16, VX_ERR_UNSUPPORTED,
              "MLA needs bf16 q and KV");
+    VX_CHECK(g->score_dim == 0 || g->score_dim == 576 || g->score_dim == 512, VX_ERR_UNSUPPORTED,
+             "MLA score_dim %d (supported: 0 or 576 = all columns, 512 = latent only)",
+             g->score_dim);
   } else {
     VX_CHECK(g->head_dim_k == g->head_dim_v, VX_ERR_UNSUPPORTED, "GQA needs head_dim_k == head_dim_v");
     VX_CHECK(g->head_dim_k == 64 || g->head_dim_k == 128, VX_ERR_UNSUPPORTED,
@@ -72,6 +75,8 @@ vx_status check_geom(const vx_geom* g) {
     VX_CHECK(g->q_dtype == g->kv_dtype, VX_ERR_UNSUPPORTED, "q and KV dtypes differ");
     VX_CHECK(g->num_kv_heads * g->head_dim_k <= 2048, VX_ERR_UNSUPPORTED,
              "num_kv_heads * head_dim > 2048");
+    VX_CHECK(g->score_dim == 0 || g->score_dim == g->head_dim_k, VX_ERR_UNSUPPORTED,
+             "GQA scores every column (score_dim 0 or head_dim_k)");
   }
   return VX_OK;
 }
@@ -225,7 +230,7 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 1; }
+int32_t vx_abi_version(void) { return 2; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {

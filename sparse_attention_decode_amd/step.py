@@ -21,7 +21,8 @@ __all__ = ["DecodeStep"]
 class DecodeStep:
     def __init__(self, w: Workload, mode: int = V.VX_TOPK_EXACT, num_splits: int = 0,
                  k: Optional[int] = None, n_sink: Optional[int] = None,
-                 n_local: Optional[int] = None, with_lse: bool = True, fused: bool = True):
+                 n_local: Optional[int] = None, with_lse: bool = True, fused: bool = True,
+                 score_dim: int = 0):
         s = w.spec
         dev = w.device
         self.w = w
@@ -35,8 +36,9 @@ class DecodeStep:
         self.score_scale, self.sm_scale = s.scales()
         self.pages = V.make_pages(s.batch, s.page_size, w.pool_pages, w.nnz, w.max_pages,
                                   w.d_indptr, w.d_page_ids, w.d_seq_lens)
+        self.score_dim = score_dim
         self.geom = V.make_geom(s.num_q_heads, s.num_kv_heads, s.head_dim_k, s.head_dim_v,
-                                s.mla, w.q.dtype, w.k_pool.dtype)
+                                s.mla, w.q.dtype, w.k_pool.dtype, score_dim)
         H = s.num_kv_heads
         self.centroids = torch.zeros((w.pool_pages, H, s.head_dim_k), dtype=torch.float32,
                                      device=dev)

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 1
+    assert lib.vx_abi_version() == 2
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -34,8 +34,8 @@ def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
     return V.make_pages(batch, page_size, pool, nnz, maxp, p, p, p)
 
 
-def geom(hq=16, hkv=8, dk=128, dv=128, mla=0, qd=V.VX_BF16, kvd=V.VX_BF16):
-    return V.make_geom(hq, hkv, dk, dv, mla, qd, kvd)
+def geom(hq=16, hkv=8, dk=128, dv=128, mla=0, qd=V.VX_BF16, kvd=V.VX_BF16, score_dim=0):
+    return V.make_geom(hq, hkv, dk, dv, mla, qd, kvd, score_dim)
 
 
 def status_of(fn, *a, **kw):
@@ -73,6 +73,8 @@ def test_bad_pages_rejected(kw, status):
     (dict(hkv=2, mla=1, dk=576, dv=512, hq=32), V.VX_ERR_INVALID_ARG),
     (dict(hkv=1, mla=1, dk=512, dv=512, hq=32), V.VX_ERR_UNSUPPORTED),
     (dict(hkv=32, hq=32, dk=128, dv=128), V.VX_ERR_UNSUPPORTED),  # 32*128 > 2048
+    (dict(score_dim=64), V.VX_ERR_UNSUPPORTED),  # GQA scores every column
+    (dict(hkv=1, mla=1, dk=576, dv=512, hq=32, score_dim=500), V.VX_ERR_UNSUPPORTED),
 ])
 def test_bad_geometry_rejected(kw, status):
     assert status_of(V.vx_page_scores, pages(), geom(**kw), BAD, BAD, 1.0, BAD, stream=0) == status

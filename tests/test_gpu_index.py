@@ -152,11 +152,11 @@ def test_idle_slots(base, headroom):
 
 # ---- vx_decode_step: the whole step in one call ---------------------------
 
-def step_vs_calls(w, num_splits=0, mode=V.VX_TOPK_EXACT, appends=2):
+def step_vs_calls(w, num_splits=0, mode=V.VX_TOPK_EXACT, appends=2, **kw):
     """vx_decode_step against vx_centroid_update + vx_page_scores +
     vx_topk_pages + vx_sparse_decode on separate buffers: same bits."""
-    sep = DecodeStep(w, mode=mode, fused=False, num_splits=num_splits)
-    one = DecodeStep(w, mode=mode, fused=True, num_splits=num_splits)
+    sep = DecodeStep(w, mode=mode, fused=False, num_splits=num_splits, **kw)
+    one = DecodeStep(w, mode=mode, fused=True, num_splits=num_splits, **kw)
     sep.rebuild_centroids()
     one.rebuild_centroids()
     used = used_pages(w)
@@ -212,3 +212,15 @@ def test_fused_decode_step_matches_oracle(name):
     T.sync()
     differing = check_step_against_oracle(w, step, range(w.batch))
     assert differing <= max(1, w.batch * w.spec.num_kv_heads // 20)
+
+
+@pytest.mark.parametrize("name", ["mla_small", "mla16_small"])
+def test_mla_latent_only_scoring(name):
+    """The rope-unaware MLA indexer (score on the 512 latent columns):
+    oracle parity for every sequence, and the whole-step call equals the
+    separate calls bit for bit."""
+    from test_gpu_parity import pipeline_check
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=20), "cpu", seed=17))
+    _, _, differing = pipeline_check(w, range(w.batch), DecodeStep(w, score_dim=512))
+    assert differing <= max(1, w.batch // 20)
+    step_vs_calls(w, score_dim=512)

@@ -107,6 +107,28 @@ def test_scores_sum_over_group_heads_and_zero_query():
     np.testing.assert_array_equal(O.page_scores(np.zeros((Hq, D)), cent, Hkv, 1.0), 0.0)
 
 
+def test_scores_latent_only_drops_exactly_the_rope_columns():
+    """score_dim = 512 of 576 (the rope-unaware MLA indexer): one-hot queries
+    in a latent column score as before, in a rope column score zero; with the
+    query's rope columns zero the two scorers agree; score_dim = Dk is the
+    plain scorer."""
+    rng = np.random.default_rng(31)
+    Hq, D, lat, n = 4, 576, 512, 6
+    cent = rng.standard_normal((n, 1, D))
+    for d in (0, 300, 511, 512, 575):
+        q = np.zeros((Hq, D))
+        q[2, d] = 1.0
+        s = O.page_scores(q, cent, 1, 0.5, score_dim=lat)
+        want = 0.5 * cent[:, 0, d] if d < lat else np.zeros(n)
+        np.testing.assert_allclose(s[0], want, rtol=1e-15)
+    q = rng.standard_normal((Hq, D))
+    np.testing.assert_array_equal(O.page_scores(q, cent, 1, 0.5, score_dim=D),
+                                  O.page_scores(q, cent, 1, 0.5))
+    q[:, lat:] = 0.0
+    np.testing.assert_allclose(O.page_scores(q, cent, 1, 0.5, score_dim=lat),
+                               O.page_scores(q, cent, 1, 0.5), rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- selection
 
 def test_forced_pages_cases():

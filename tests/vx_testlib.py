@@ -31,7 +31,8 @@ def oracle_seq(w: W.Workload, step: DecodeStep, b: int, approx: bool = False) ->
     r = O.decode_sequence(seq, page_size=s.page_size, num_kv_heads=s.num_kv_heads, k=step.k,
                           n_sink=step.n_sink, n_local=step.n_local,
                           score_scale=step.score_scale, sm_scale=step.sm_scale, mla=s.mla,
-                          head_dim_v=s.head_dim_v, approx=approx)
+                          head_dim_v=s.head_dim_v, approx=approx,
+                          score_dim=step.score_dim or None)
     r["seq"] = seq
     return r
 
@@ -62,8 +63,9 @@ def check_scores(w, step, b, ref):
     n = ref["centroids"].shape[0]
     lo = int(w.indptr[b])
     got = step.scores[:, lo:lo + n].double().cpu().numpy()
-    q = ref["seq"]["q"]
-    cent = O.round_to_bf16(ref["centroids"]) if s.mla else ref["centroids"]
+    d = step.score_dim or s.head_dim_k  # columns scored
+    q = ref["seq"]["q"][:, :d]
+    cent = (O.round_to_bf16(ref["centroids"]) if s.mla else ref["centroids"])[..., :d]
     G = s.num_q_heads // s.num_kv_heads
     bound = np.zeros((s.num_kv_heads, n))
     for g in range(s.num_kv_heads):
