@@ -13,7 +13,7 @@
 //   D (16 x 16):  lane holds rows 4*q4 + i (i < 4), column (l % 16)
 // A and B read the k elements from the same offsets, so the contraction is
 // exact whatever order the hardware sums them in.
-#include "vx_internal.h"
+#include "topk_wave.h"
 
 namespace vx {
 namespace {
@@ -124,232 +124,393 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 }
 
 // ---------------------------------------------------------------- attention
-// One block (8 waves) per (sequence b, split s); the split holds a balanced
-// share of the selected pages. Pages are consumed as 64-token chunks. Each
-// chunk is staged in LDS twice: row-major (the B operand of q.k^T reads a
-// token's 8 consecutive columns) and value columns transposed (the B operand
-// of P.V reads 8 consecutive tokens of one column); the transpose is done in
-// registers on 8x8 bf16 blocks, so both operands are single 16-byte LDS
-// reads; in the transposed copy, the 8-token groups of column r sit at
-// group index ^ ((r / 8) % 8), which spreads a wave's stores over the LDS
-// banks. The next kRing chunks are in flight in registers while one is
-// consumed. Logits: wave w < 4 MT computes the 16x16 tile (head tile w % MT,
-// token tile w / MT); row maxima and sums are exchanged through LDS. P.V:
-// wave w owns head tile w % MT and value columns [part * 512 / NP, +512 / NP)
-// with NP = 8 / MT, so its accumulators stay small enough for two waves per
-// SIMD.
-constexpr int kMlaWaves = 8;
-constexpr int CHT = 64;                 // tokens per chunk
-constexpr int NTT = CHT / 16;           // token tiles per chunk
-#ifndef VX_MLA_RING
-#define VX_MLA_RING 1
-#endif
-constexpr int kRing = VX_MLA_RING;      // chunks in flight per block
-constexpr int VT_ROW = CHT + 8;         // padded transposed-V row (bf16), 144 B
-constexpr int PROW = CHT + 8;           // padded P row (bf16)
+// One block of 4 MT waves (MT head tiles of 16) per (sequence b, split s);
+// the split holds a balanced share of the selected pages, consumed one
+// 64-token page (a "chunk") at a time. Wave w works on head tile mt = w / 4
+// and quarter u = w % 4: token tile u (tokens 16 u ..) in q.k^T, value
+// columns 128 u .. 128 u + 127 in P.V.
+//
+// Staging: every chunk goes straight from HBM into LDS with direct loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 * lane)
+// through a ring of two chunk slots, so the next chunk streams in while the
+// current one is consumed and no register holds staging data. A slot is 72
+// wave-wide 1 KB loads; the lane -> (token t, 16-byte granule g) map of each
+// load is chosen so that both MFMA operand reads below hit distinct 16-byte
+// bank groups within every 8 and every 16 lanes:
+//   latent granule g < 64:  load 16 (g / 16) + t / 4,
+//                           lane 16 (t % 4) + ((g ^ t) % 16);
+//   rope granule g >= 64:   load 64 + t / 8,
+//                           lane 8 (t % 8) + (((g - 64) ^ t) % 8).
+// q.k^T  v_mfma_f32_16x16x32_bf16, A = the tile's query rows (registers),
+//        B = key granules (lane: token l % 16, 8 columns per k step). Row
+//        maxima of the four token tiles are exchanged through LDS.
+// P.V    lane (q4, c) reads tokens 8 q4 .. 8 q4 + 7 of each 32-token half,
+//        columns 8 c .. 8 c + 7 of its quarter (eight 16-byte reads); taking
+//        N-tile e's columns as {8 c + e}, element e of the lane's eight rows
+//        is its B fragment (byte permutes); P, bf16 through LDS, is the A
+//        operand.
+// Softmax: probabilities are taken against a per-row reference maximum that
+// moves only when some logit of a chunk exceeds it by more than kLazy (log2
+// units); below that, probabilities up to 2^kLazy are used as they are. The
+// waves raise a flag in LDS when they see such a logit; only then (and
+// always at the first chunk) are the chunk's row maxima exchanged, the
+// accumulators rescaled and P recomputed. Each lane sums the probabilities
+// of its own token; the sums are reduced once, at the end.
+constexpr int CHT = 64;                   // tokens per chunk (one page)
+constexpr int kChunkLoads = CHT * DK / 8 / 64;   // 72 wave-wide 16-byte loads
+constexpr int kSlotBytes = kChunkLoads * 1024;
+constexpr int PROW = CHT + 8;             // padded P row (bf16), 144 B
+constexpr float kLazy = 8.f;
+static_assert(DV == 4 * 128, "four 128-column value quarters");
 
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
-  const uint32_t wv = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (wv >> 16) : (wv & 0xffffu);
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);  // v_cvt_pk_bf16_f32, round to nearest even
 }
 
-template <int MT>
-__global__ __launch_bounds__(64 * kMlaWaves) void attn_mla_kernel(
-    Meta m, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
-    const int32_t* __restrict__ sel, int stride, const int32_t* __restrict__ sel_count,
-    float qscale, int S, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int HQ = 16 * MT;
-  constexpr int NP = kMlaWaves / MT;  // value-column parts
-  constexpr int NT2 = DV / NP / 16;   // 16-column tiles per wave
-  static_assert(DV / 8 * (CHT / 8) == 64 * kMlaWaves, "one 8x8 staging block per thread");
-  static_assert(CHT * 8 == 64 * kMlaWaves, "one rope vector per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t krow[CHT * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[DV * VT_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[MT][16 * PROW];
-  __shared__ float rmax[MT][NTT][16];
-  __shared__ float rsum[MT][NTT][16];
-  __shared__ int pg_phys[kMaxPagesPerSplit];
+// B fragment e of P.V: element e of each of the lane's eight value rows.
+__device__ __forceinline__ u32x4 column_frag(const u32x4* v, int e) {
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  auto word = [&](const u32x4& x) {
+    return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+  };
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(word(v[1]), word(v[0]), sel);
+  r.y = __builtin_amdgcn_perm(word(v[3]), word(v[2]), sel);
+  r.z = __builtin_amdgcn_perm(word(v[5]), word(v[4]), sel);
+  r.w = __builtin_amdgcn_perm(word(v[7]), word(v[6]), sel);
+  return r;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Block barrier for LDS data only. __syncthreads() would also wait for the
+// direct loads in flight into the other slot (they write LDS); here only this
+// wave's own LDS reads and writes are completed (lgkmcnt 0) before the
+// barrier, and the signal fences keep the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// LDS of the attention part. The two slots are separate arrays: the
+// compiler then sees that reads of one slot do not depend on direct loads
+// still in flight into the other.
+#define VX_MLA_ATTN_LDS(MT)                                              \
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];   \
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];   \
+  __shared__ __attribute__((aligned(16))) uint16_t pl[16 * (MT) * PROW]; \
+  __shared__ float rmax[4][16 * (MT)];                                   \
+  __shared__ int flag[4 * (MT)];                                         \
+  __shared__ int pg_phys[kMaxPagesPerSplit];                             \
   __shared__ int pg_nv[kMaxPagesPerSplit];
 
+// Entries [p0, p1) of the selection's stride belong to split s of S.
+__device__ __forceinline__ void mla_split(int stride, int s, int S, int& p0, int& p1) {
+  p0 = (int)(((long)stride * s) / S);
+  p1 = min((int)(((long)stride * (s + 1)) / S), p0 + kMaxPagesPerSplit);
+}
+
+// Attention of sequence b's query heads over the np pages listed in
+// pg_phys / pg_nv (LDS, visible to the block); split s of S. Called by
+// every thread of the block.
+template <int MT>
+__device__ __forceinline__ void mla_attend(uint8_t* slot0, uint8_t* slot1, uint16_t* pl,
+                                           float (*rmax)[16 * MT], int* flag, const int* pg_phys,
+                                           const int* pg_nv, int np, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ kp, int b, int s, int S,
+                                           float qscale, float* __restrict__ out,
+                                           float* __restrict__ lse, float* __restrict__ part_o,
+                                           float* __restrict__ part_ml) {
+  constexpr int HQ = 16 * MT;
+  constexpr int NW = 4 * MT;
+  constexpr int LPW = kChunkLoads / NW;  // loads per wave per chunk
+  static_assert(kChunkLoads % NW == 0 && 64 % NW == 0, "loads split evenly");
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int mt = w >> 2, u = w & 3;
   const int col = lane & 15, q4 = lane >> 4;
-  const int mt = w % MT, part = w / MT;
-  const bool qk_wave = w < NTT * MT;
-  const int nt = w / MT;  // token tile of the logit tile (qk waves)
-  const int item = blockIdx.x;
-  const int s = item % S, b = item / S;
-  const int row0 = m.indptr[b];
-  const int cap = m.indptr[b + 1] - row0;
-  const int L = seq_len_clamped(m, b);
-  const int count = cap > 0 ? min(sel_count[b], stride) : 0;
-  const int p0 = (int)(((long)count * s) / S);
-  const int np = min((int)(((long)count * (s + 1)) / S) - p0, kMaxPagesPerSplit);
-  const int P = m.page_size;  // 64 (checked on the host): one chunk per page
 
-  static_assert(kMaxPagesPerSplit <= 64 * kMlaWaves, "one page-list entry per thread");
-  if (t < np) {
-    int lp = sel[(size_t)b * stride + p0 + t];
-    lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);
-    pg_phys[t] = phys_page(m, row0 + lp);
-    pg_nv[t] = max(0, min(P, L - lp * P));
-  }
-
+  // query rows 16 mt + col, columns 32 ks + 8 q4 .. +7
   u32x4 qf[KSTEPS];
   {
     const uint16_t* qrow = q + ((size_t)b * HQ + 16 * mt + col) * DK + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *(const u32x4*)(qrow + 32 * ks);
   }
-  f32x4 o[NT2];
+
+  // Per-lane parts of the slot layout (see above).
+  // Direct loads w + NW k: latent load i (< 64) fetches token 4 (i % 16) + lane / 16,
+  // granule 16 (i / 16) + ((lane ^ t) % 16); t % 16 depends on i only through i % 4 = w % 4.
+  const int src_lat = (lane >> 4) * DK + 8 * ((lane ^ (4 * (w & 3) + (lane >> 4))) & 15);
+  const int src_rope = (lane >> 3) * DK + 8 * (64 + ((lane ^ (lane >> 3)) & 7));
+  // q.k^T reads: token 16 u + col, granule 4 ks + q4.
+  int qk_off[6];
 #pragma unroll
-  for (int x = 0; x < NT2; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k4 = 0; k4 < 4; ++k4)
+    qk_off[k4] = (4 * u + (col >> 2)) * 1024 + (16 * (col & 3) + (((4 * k4 + q4) ^ col) & 15)) * 16;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+    qk_off[4 + k2] = (64 + 2 * u + (col >> 3)) * 1024 + (8 * (col & 7) + (((4 * k2 + q4) ^ col) & 7)) * 16;
+  // P.V reads: token 32 kb + 8 q4 + r, granule 16 u + col.
+  int pv_off[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    pv_off[r] = (16 * u + 2 * q4 + (r >> 2)) * 1024 + (16 * (r & 3) + ((col ^ (8 * (q4 & 1) + r)) & 15)) * 16;
+
+  f32x4 o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[4], lrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { mrow[i] = kNegBig; lrow[i] = 0.f; }
-  __syncthreads();  // page list ready
 
-  const int cpp = P / CHT;
-  const int nchunks = np * cpp;
-  // Valid tokens of chunk c; chunks past the end (the ring's tail) are empty
-  // and contribute exactly nothing (p = 0, alpha = 1).
-  auto chunk_valid = [&](int c) {
-    return c < nchunks ? min(CHT, pg_nv[c / cpp] - (c % cpp) * CHT) : 0;
-  };
-  // staging roles: an 8x8 (token x column) block of value columns + one rope vector
-  const int dg = t & 63, tg = t >> 6;      // columns 8 dg.., tokens 8 tg..
-  const int rr = t >> 3, rg = t & 7;       // rope: token rr, columns 512 + 8 rg..
-  // Ring of kRing chunks in flight; a load past the end re-reads the last chunk.
-  u32x4 vb[kRing][8], rp[kRing];
-  auto prefetch = [&](int c, u32x4* v, u32x4& r) {
-    c = min(c, nchunks - 1);
-    const uint16_t* src = kp + ((size_t)pg_phys[c / cpp] * P + (size_t)(c % cpp) * CHT) * DK;
+  // This wave's loads w + NW k of chunk c, straight into its slot.
+  auto issue = [&](int c, uint8_t* slot_c) {
+    const uint16_t* page = kp + (size_t)__builtin_amdgcn_readfirstlane(pg_phys[c]) * CHT * DK;
+    uint8_t* slot = slot_c + 1024 * w;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = __builtin_nontemporal_load((const u32x4*)(src + (8 * tg + i) * DK + 8 * dg));
-    r = __builtin_nontemporal_load((const u32x4*)(src + rr * DK + DV + 8 * rg));
-  };
-
-  const int dcol0 = part * (DV / NP);
-  if (nchunks > 0) {
-#pragma unroll
-    for (int d = 0; d < kRing; ++d) prefetch(d, vb[d], rp[d]);
-  }
-  for (int c0 = 0; c0 < nchunks; c0 += kRing) {
-#pragma unroll
-  for (int d = 0; d < kRing; ++d) {
-    const int c = c0 + d;
-    const int nv = chunk_valid(c);
-    __syncthreads();  // (A) previous chunk fully consumed
-    {
-      u32x4 x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = (8 * tg + i < nv) ? vb[d][i] : u32x4{0u, 0u, 0u, 0u};
-        *(u32x4*)(krow + (8 * tg + i) * ROW + 8 * dg) = x[i];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x4 y;
-        y.x = half_of(x[0], e) | (half_of(x[1], e) << 16);
-        y.y = half_of(x[2], e) | (half_of(x[3], e) << 16);
-        y.z = half_of(x[4], e) | (half_of(x[5], e) << 16);
-        y.w = half_of(x[6], e) | (half_of(x[7], e) << 16);
-        *(u32x4*)(vt + (8 * dg + e) * VT_ROW + 8 * (tg ^ (dg & 7))) = y;
-      }
-      *(u32x4*)(krow + rr * ROW + DV + 8 * rg) = (rr < nv) ? rp[d] : u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < LPW; ++k) {
+      const int i = w + NW * k;
+      const int off = k < 64 / NW ? 4 * (i & 15) * DK + 128 * (i >> 4) + src_lat
+                                  : 8 * (i - 64) * DK + src_rope;
+      __builtin_amdgcn_global_load_lds((const void*)(page + off), (lds_void*)(slot + 1024 * NW * k),
+                                       16, 0, 0);
     }
-    prefetch(c + kRing, vb[d], rp[d]);
-    __syncthreads();  // (B) chunk c staged
+  };
+  // Chunk c: consumed from `slot`; chunk c + 1 streams into `other`.
+  auto chunk = [&](int c, const uint8_t* slot, uint8_t* other) {
+    // Wait for this wave's loads of chunk c (vmcnt 0: nothing else is in
+    // flight here, except chunk 1 at c = 0, issued together with chunk 0);
+    // the barrier then makes every wave's share visible and ends every read
+    // of chunk c - 1, whose slot chunk c + 1 takes.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    __syncthreads();  // (A)
+    if (c >= 1 && c + 1 < np) issue(c + 1, other);
+    const int nv = pg_nv[c];
 
-    float z[4];
-    if (qk_wave) {
-      f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
-      const uint16_t* kr = krow + (16 * nt + col) * ROW + 8 * q4;
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ks += 2) {
-        a0 = mfma(qf[ks], *(const u32x4*)(kr + 32 * ks), a0);
-        a1 = mfma(qf[ks + 1], *(const u32x4*)(kr + 32 * (ks + 1)), a1);
-      }
-      const bool ok = 16 * nt + col < nv;
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int off = ks < 16 ? qk_off[ks & 3] + (ks >> 2) * 16384 : qk_off[4 + (ks - 16)];
+      sacc = mfma(qf[ks], *(const u32x4*)(slot + off), sacc);
+    }
+    const bool tok_ok = 16 * u + col < nv;
+    // Probabilities against the current reference maxima; a wave that sees
+    // a logit above its row's reference + kLazy raises the block's flag.
+    float z[4], p[4];
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = tok_ok ? sacc[i] * qscale : -INFINITY;
+      need = need || z[i] > mrow[i] + kLazy;
+      p[i] = __builtin_amdgcn_exp2f(z[i] - mrow[i]);
+    }
+    const bool wave_need = __ballot(need) != 0;
+    if (lane == 0) flag[w] = wave_need ? 1 : 0;
+    auto write_p = [&]() {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pl[(16 * mt + 4 * q4 + i) * PROW + 16 * u + col] = (uint16_t)bf16_bits(p[i]);
+    };
+    write_p();
+    barrier_lds();  // (B) P and the flags of the whole chunk in LDS
+    int any = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) any |= flag[v];
+    if (any) {
+      // Rare (always at the first chunk): move every row's reference to
+      // max(reference, chunk maximum), rescale, recompute P. The flags are
+      // the same for every wave, so the whole block takes this branch.
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[i] = ok ? (a0[i] + a1[i]) * qscale : -INFINITY;
         const float mx = group_max<16>(z[i]);
-        if (col == 0) rmax[mt][nt][4 * q4 + i] = mx;
+        if (col == 0) rmax[u][16 * mt + 4 * q4 + i] = mx;
       }
-    }
-    __syncthreads();  // (C) row maxima of every token tile
-    float mnew[4], alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q4 + i;
-      float mx = rmax[mt][0][r];
-#pragma unroll
-      for (int u = 1; u < NTT; ++u) mx = fmaxf(mx, rmax[mt][u][r]);
-      mnew[i] = fmaxf(mrow[i], mx);
-      alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mnew[i]);
-    }
-    if (qk_wave) {
+      barrier_lds();
+      float alpha[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(z[i] - mnew[i]);
-        const float sum = group_sum<16>(e);
-        if (col == 0) rsum[mt][nt][4 * q4 + i] = sum;
-        pl[mt][(4 * q4 + i) * PROW + 16 * nt + col] = f32_to_bf16(e);
+        const int r = 16 * mt + 4 * q4 + i;
+        const float mx = fmaxf(fmaxf(rmax[0][r], rmax[1][r]), fmaxf(rmax[2][r], rmax[3][r]));
+        const float mref = fmaxf(mrow[i], mx);
+        alpha[i] = __builtin_amdgcn_exp2f(mrow[i] - mref);
+        mrow[i] = mref;
+        p[i] = __builtin_amdgcn_exp2f(z[i] - mref);
+        lrow[i] *= alpha[i];
       }
-    }
-    __syncthreads();  // (D) P and row sums ready
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q4 + i;
-      float sum = rsum[mt][0][r];
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int u = 1; u < NTT; ++u) sum += rsum[mt][u][r];
-      lrow[i] = lrow[i] * alpha[i] + sum;
-      mrow[i] = mnew[i];
+        for (int i = 0; i < 4; ++i) o[e][i] *= alpha[i];
+      write_p();
+      barrier_lds();  // P rewritten; every wave has read the flags and maxima
     }
 #pragma unroll
-    for (int x = 0; x < NT2; ++x)
+    for (int i = 0; i < 4; ++i) lrow[i] += p[i];  // this lane's token; summed at the end
+
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[x][i] *= alpha[i];
+    for (int kb = 0; kb < CHT / 32; ++kb) {
+      u32x4 v[8];
 #pragma unroll
-    for (int k2 = 0; k2 < CHT / 32; ++k2) {
-      const u32x4 pa = *(const u32x4*)(pl[mt] + col * PROW + 32 * k2 + 8 * q4);
+      for (int r = 0; r < 8; ++r) v[r] = *(const u32x4*)(slot + pv_off[r] + 8192 * kb);
+      if (nv < CHT) {  // rows past the page's valid tokens hold no data: make them zero
 #pragma unroll
-      for (int x = 0; x < NT2; ++x)
-      {
-        const int r = dcol0 + 16 * x + col;  // value column; its token groups are swizzled
-        o[x] = mfma(pa, *(const u32x4*)(vt + r * VT_ROW + 8 * ((4 * k2 + q4) ^ ((r >> 3) & 7))),
-                    o[x]);
+        for (int r = 0; r < 8; ++r)
+          if (32 * kb + 8 * q4 + r >= nv) v[r] = u32x4{0u, 0u, 0u, 0u};
       }
+      const u32x4 pa = *(const u32x4*)(pl + (16 * mt + col) * PROW + 32 * kb + 8 * q4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = mfma(pa, column_frag(v, e), o[e]);
     }
-  }
+  };
+
+  if (np > 0) issue(0, slot0);
+  if (np > 1) issue(1, slot1);
+  for (int c = 0; c < np; c += 2) {
+    chunk(c, slot0, slot1);
+    if (c + 1 < np) chunk(c + 1, slot1, slot0);
   }
 
-  // results: rows 4*q4 + i of head tile mt, columns dcol0 + 16 x + col
+  // Row sums: over the 16 tokens of the lane group, then the four token tiles.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lrow[i] = group_sum<16>(lrow[i]);
+  __syncthreads();
+  if (col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rmax[u][16 * mt + 4 * q4 + i] = lrow[i];
+  }
+  __syncthreads();
+
+  // results: rows 16 mt + 4 q4 + i, columns 128 u + 8 col + e
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int head = 16 * mt + 4 * q4 + i;
+    const float l = (rmax[0][head] + rmax[1][head]) + (rmax[2][head] + rmax[3][head]);
+    const int d0 = 128 * u + 8 * col;
     if (S == 1) {
-      const float inv = lrow[i] > 0.f ? 1.f / lrow[i] : 0.f;
-      float* dst = out + ((size_t)b * HQ + head) * DV + dcol0 + col;
-#pragma unroll
-      for (int x = 0; x < NT2; ++x) dst[16 * x] = o[x][i] * inv;
-      if (lse && part == 0 && col == 0)
-        lse[(size_t)b * HQ + head] = lrow[i] > 0.f ? (mrow[i] + log2f(lrow[i])) * kLn2 : -INFINITY;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* dst = out + ((size_t)b * HQ + head) * DV + d0;
+      *(float4*)dst = make_float4(o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv);
+      *(float4*)(dst + 4) = make_float4(o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv);
+      if (lse && u == 0 && col == 0)
+        lse[(size_t)b * HQ + head] = l > 0.f ? (mrow[i] + log2f(l)) * kLn2 : -INFINITY;
     } else {
       const size_t ps = ((size_t)b * HQ + head) * S + s;
-      float* dst = part_o + ps * DV + dcol0 + col;
-#pragma unroll
-      for (int x = 0; x < NT2; ++x) dst[16 * x] = o[x][i];
-      if (part == 0 && col == 0) {
+      float* dst = part_o + ps * DV + d0;
+      *(float4*)dst = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+      *(float4*)(dst + 4) = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
+      if (u == 0 && col == 0) {
         part_ml[2 * ps] = mrow[i];
-        part_ml[2 * ps + 1] = lrow[i];
+        part_ml[2 * ps + 1] = l;
       }
     }
   }
+}
+
+// Attention over a selection made by the caller (sel / sel_count).
+template <int MT>
+__global__ __launch_bounds__(256 * MT) void attn_mla_kernel(
+    Meta m, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
+    const int32_t* __restrict__ sel, int stride, const int32_t* __restrict__ sel_count,
+    float qscale, int S, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  VX_MLA_ATTN_LDS(MT)
+  static_assert(kMaxPagesPerSplit <= 256 * MT, "one page-list entry per thread");
+  const int t = threadIdx.x;
+  const int s = blockIdx.x % S, b = blockIdx.x / S;
+  // The split is over the stride, not the count, so the split's entries load
+  // together with the count instead of after it; entries at or past the
+  // count are dropped.
+  int p0, p1;
+  mla_split(stride, s, S, p0, p1);
+  const int row0 = m.indptr[b];
+  const int cap = m.indptr[b + 1] - row0;
+  const int L = seq_len_clamped(m, b);
+  const int count = cap > 0 ? min(sel_count[b], stride) : 0;
+  const int np = max(0, min(p1, count) - p0);
+  // m.page_size == CHT (checked on the host): one chunk per page
+  if (t < p1 - p0) {
+    int lp = sel[(size_t)b * stride + p0 + t];
+    if (t < np) {
+      lp = lp < 0 ? 0 : (lp >= cap ? cap - 1 : lp);
+      pg_phys[t] = phys_page(m, row0 + lp);
+      pg_nv[t] = max(0, min(CHT, L - lp * CHT));
+    }
+  }
+  __syncthreads();  // page list ready
+  mla_attend<MT>(slot0, slot1, pl, rmax, flag, pg_phys, pg_nv, np, q, kp, b, s, S, qscale, out,
+                 lse, part_o, part_ml);
+}
+
+// Selection and attention in one kernel (the decode step after scoring):
+// every split block of sequence b selects b's pages from its scores itself
+// (the same radix top-k as the top-k kernels, so the same selection), block
+// s == 0 writes sel / sel_count, and each block attends over its split's
+// share. The keys and the selected ids use the chunk slots before any
+// chunk is loaded.
+struct MlaStepArgs {
+  Meta m;
+  const uint16_t* q;
+  const uint16_t* kp;
+  const float* scores;
+  int k, n_sink, n_local, mode;
+  const uint32_t* rnd;
+  int32_t* sel;
+  int stride;
+  int32_t* sel_count;
+  float qscale;
+  int S;
+  float* out;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+  int cap_keys;
+};
+
+template <int MT>
+__global__ __launch_bounds__(256 * MT) void decode_mla_kernel(MlaStepArgs a) {
+  VX_MLA_ATTN_LDS(MT)
+  __shared__ int32_t cnt_l;
+  constexpr int NW = 4 * MT;
+  static_assert(kMaxPagesPerSplit <= 256 * MT, "one page-list entry per thread");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int s = blockIdx.x % a.S, b = blockIdx.x / a.S;
+  const Meta& m = a.m;
+  const int row0 = m.indptr[b];
+  const int cap = m.indptr[b + 1] - row0;
+  const int L = seq_len_clamped(m, b);
+  const int n = min(min((L + CHT - 1) / CHT, cap), a.cap_keys);
+  uint32_t* keys = (uint32_t*)slot0;  // cap_keys + kSelectExtraWords words
+  int32_t* sel_l = (int32_t*)slot1;   // the selection, ascending
+  for (int i = t; i < n; i += 64 * NW)
+    keys[i] = (i < a.n_sink || i >= n - a.n_local) ? 0u : topk_detail::score_key(a.scores[row0 + i]);
+  __syncthreads();
+  const uint32_t rnd = a.mode == VX_TOPK_APPROX ? a.rnd[b] : 0u;
+  int32_t* gsel = s == 0 ? a.sel + (size_t)b * a.stride : nullptr;
+  int32_t* gcnt = s == 0 ? a.sel_count + b : nullptr;
+  if (n > kBlockSelectMin)
+    block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + 256, n, a.k, a.n_sink,
+                          a.n_local, a.mode, rnd, gsel, a.stride, gcnt, sel_l, &cnt_l);
+  else if (w == 0)
+    wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd, gsel,
+                     a.stride, gcnt, lane, sel_l, &cnt_l);
+  __syncthreads();  // selection in LDS
+  int p0, p1;
+  mla_split(a.stride, s, a.S, p0, p1);
+  const int count = min(cnt_l, a.stride);
+  const int np = max(0, min(p1, count) - p0);
+  if (t < np) {
+    const int lp = sel_l[p0 + t];
+    pg_phys[t] = phys_page(m, row0 + lp);
+    pg_nv[t] = max(0, min(CHT, L - lp * CHT));
+  }
+  __syncthreads();  // page list ready; keys and selection no longer read
+  mla_attend<MT>(slot0, slot1, pl, rmax, flag, pg_phys, pg_nv, np, a.q, a.kp, b, s, a.S, a.qscale,
+                 a.out, a.lse, a.part_o, a.part_ml);
 }
 
 }  // namespace
@@ -375,6 +536,49 @@ hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* 
   return hipGetLastError();
 }
 
+bool decode_step_mla_fusable(int max_pages, int sel_stride) {
+  const int cap_keys = (max_pages + 63) / 64 * 64;
+  return (size_t)(cap_keys + kSelectExtraWords) * 4 <= (size_t)kSlotBytes &&
+         (size_t)sel_stride * 4 <= (size_t)kSlotBytes;
+}
+
+hipError_t launch_decode_step_mla(const Meta& m, const vx_geom& g, const void* q,
+                                  const void* k_pool, const float* scores, int k, int n_sink,
+                                  int n_local, int mode, const uint32_t* rnd, int32_t* sel,
+                                  int sel_stride, int32_t* sel_count, float sm_scale,
+                                  int num_splits, float* out, float* lse, float* part_o,
+                                  float* part_ml, int max_pages, hipStream_t s) {
+  if (m.batch == 0) return hipSuccess;
+  MlaStepArgs a{};
+  a.m = m;
+  a.q = (const uint16_t*)q;
+  a.kp = (const uint16_t*)k_pool;
+  a.scores = scores;
+  a.k = k;
+  a.n_sink = n_sink;
+  a.n_local = n_local;
+  a.mode = mode;
+  a.rnd = rnd;
+  a.sel = sel;
+  a.stride = sel_stride;
+  a.sel_count = sel_count;
+  a.qscale = sm_scale * kLog2e;
+  a.S = num_splits;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.cap_keys = (max_pages + 63) / 64 * 64;
+  dim3 grid(m.batch * num_splits);
+  if (g.num_q_heads == 32)
+    hipLaunchKernelGGL(decode_mla_kernel<2>, grid, dim3(512), 0, s, a);
+  else if (g.num_q_heads == 16)
+    hipLaunchKernelGGL(decode_mla_kernel<1>, grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
                                 const void* k_pool, const int32_t* sel, int sel_stride,
                                 const int32_t* sel_count, float sm_scale, int num_splits,
@@ -382,13 +586,13 @@ hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
                                 float* part_ml, hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   const float qscale = sm_scale * kLog2e;
-  dim3 grid(m.batch * num_splits), block(64 * kMlaWaves);
+  dim3 grid(m.batch * num_splits);
   if (g.num_q_heads == 32)
-    hipLaunchKernelGGL(attn_mla_kernel<2>, grid, block, 0, s, m, (const uint16_t*)q,
+    hipLaunchKernelGGL(attn_mla_kernel<2>, grid, dim3(512), 0, s, m, (const uint16_t*)q,
                        (const uint16_t*)k_pool, sel, sel_stride, sel_count, qscale, num_splits,
                        out, lse, part_o, part_ml);
   else if (g.num_q_heads == 16)
-    hipLaunchKernelGGL(attn_mla_kernel<1>, grid, block, 0, s, m, (const uint16_t*)q,
+    hipLaunchKernelGGL(attn_mla_kernel<1>, grid, dim3(256), 0, s, m, (const uint16_t*)q,
                        (const uint16_t*)k_pool, sel, sel_stride, sel_count, qscale, num_splits,
                        out, lse, part_o, part_ml);
   else

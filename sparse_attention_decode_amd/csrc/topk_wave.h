@@ -110,7 +110,8 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t r, in
 // Ordered compaction (ascending page index) of the survivors: forced pages,
 // candidates with (key & mask) > prefix, and r of those with (key & mask) ==
 // prefix taken in index order from offset `off`, cyclic over the `members`
-// of that tie group. One wave; ballot + mbcnt ranks keep the order.
+// of that tie group. One wave; ballot + mbcnt ranks keep the order. out /
+// count_out (global) and out_lds / count_lds may each be null.
 __device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, int n, int n_sink,
                                              int n_local, uint32_t prefix, uint32_t mask,
                                              uint32_t r, uint32_t off, uint32_t members,
@@ -142,15 +143,16 @@ __device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, 
     if (tie && members) take = take || ((trank + members - off) % members) < r;
     const unsigned long long smask = __ballot(take);
     if (take) {
-      out[written + rank_below(smask)] = i;
+      if (out) out[written + rank_below(smask)] = i;
       if (out_lds) out_lds[written + rank_below(smask)] = i;
     }
     written += (uint32_t)__popcll(smask);
     }
   }
-  for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
+  if (out)
+    for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
   if (lane == 0) {
-    *count_out = (int32_t)written;
+    if (count_out) *count_out = (int32_t)written;
     if (count_lds) *count_lds = (int32_t)written;
   }
 }

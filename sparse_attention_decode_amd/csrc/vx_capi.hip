@@ -226,6 +226,19 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   return VX_OK;
 }
 
+// Per-split partial outputs and (m, l) pairs in the workspace (S > 1), laid
+// out as make_plan sizes them.
+void split_buffers(const vx_pages* p, const vx_geom* g, int S, void* ws, float** part_o,
+                   float** part_ml) {
+  *part_o = nullptr;
+  *part_ml = nullptr;
+  if (S <= 1) return;
+  *part_o = (float*)ws;
+  *part_ml = (float*)((char*)ws + align_up((size_t)p->batch * g->num_q_heads * S *
+                                               g->head_dim_v * sizeof(float),
+                                           256));
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,13 +396,7 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const voi
   const int S = plan.num_splits;
   float* part_o = nullptr;
   float* part_ml = nullptr;
-  if (S > 1) {
-    part_o = (float*)workspace;
-    part_ml = (float*)((char*)workspace +
-                       align_up((size_t)pages->batch * geom->num_q_heads * S * geom->head_dim_v *
-                                    sizeof(float),
-                                256));
-  }
+  split_buffers(pages, geom, S, workspace, &part_o, &part_ml);
   hipError_t e;
   if (geom->mla)
     e = vx::launch_attention_mla(m, *geom, q, k_pool, sel, sel_stride, sel_count, sm_scale, S,
@@ -445,6 +452,29 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
         sel_count, out, lse, pages->max_pages, stream);
     return hip_status(e, "decode step kernel launch");
+  }
+  if (geom->mla && pages->total_pages > 0 &&
+      vx::decode_step_mla_fusable(pages->max_pages, sel_stride)) {
+    // scores, then selection + attention in one kernel, then the merge
+    const vx::Meta m = meta_of(pages);
+    const int S = plan.num_splits;
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
+    split_buffers(pages, geom, S, workspace, &part_o, &part_ml);
+    hipError_t e = vx::launch_scores_mla_sized(m, *geom, q, k_pool, centroids,
+                                               (uint16_t*)cent_bf16, refresh_newest, score_scale,
+                                               scores, pages->max_pages, stream);
+    if (e != hipSuccess) return hip_status(e, "score kernel launch");
+    e = vx::launch_decode_step_mla(m, *geom, q, k_pool, scores, k, n_sink, n_local, mode,
+                                   rand_u32, sel, sel_stride, sel_count, sm_scale, S, out, lse,
+                                   part_o, part_ml, pages->max_pages, stream);
+    if (e != hipSuccess) return hip_status(e, "decode step kernel launch");
+    if (S > 1) {
+      e = vx::launch_merge(pages->batch, geom->num_q_heads, geom->head_dim_v, S, part_o, part_ml,
+                           out, lse, stream);
+      if (e != hipSuccess) return hip_status(e, "merge kernel launch");
+    }
+    return VX_OK;
   }
   if ((st = vx_index_pages(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
                            score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,

@@ -198,6 +198,17 @@ hipError_t launch_attention_mla(const Meta& m, const vx_geom& g, const void* q,
                                 const int32_t* sel_count, float sm_scale, int num_splits,
                                 int pages_per_split, float* out, float* lse, float* part_o,
                                 float* part_ml, hipStream_t s);
+// MLA step after scoring in one kernel: every split block selects its
+// sequence's pages from the scores (block s == 0 writes sel / sel_count),
+// then attends over its share. Fusable when the keys and the selection fit
+// the kernel's LDS.
+bool decode_step_mla_fusable(int max_pages, int sel_stride);
+hipError_t launch_decode_step_mla(const Meta& m, const vx_geom& g, const void* q,
+                                  const void* k_pool, const float* scores, int k, int n_sink,
+                                  int n_local, int mode, const uint32_t* rnd, int32_t* sel,
+                                  int sel_stride, int32_t* sel_count, float sm_scale,
+                                  int num_splits, float* out, float* lse, float* part_o,
+                                  float* part_ml, int max_pages, hipStream_t s);
 hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* part_o,
                         const float* part_ml, float* out, float* lse, hipStream_t s);
 
