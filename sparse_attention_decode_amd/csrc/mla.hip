@@ -32,12 +32,15 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 }
 
 // ------------------------------------------------------------------ scoring
-// grid (ceil(max_pages / 64), B), 4 waves; wave w scores the 16 pages
-// [64 * blockIdx.x + 16 w, +16) of sequence blockIdx.y. With `refresh`, the
-// block holding a sequence's newest page first recomputes that page's
-// centroid (fp32 and its bf16 copy) from its keys, in token order with one
-// IEEE divide per column, the cache stage's arithmetic; the barrier before
-// scoring orders it before the page's bf16 row is read.
+// grid (ceil(max_pages / 64) [+ 1 with refresh], B), 4 waves. Scoring block
+// x: wave w scores the 16 pages [64 x + 16 w, +16) of sequence blockIdx.y;
+// each lane loads its page id and centroid slice before the query rows are
+// staged, so the block waits on two dependent loads, not three. With
+// `refresh`, the last block of each row instead recomputes the sequence's
+// newest page centroid (fp32 and its bf16 copy) from its keys, in token
+// order with one IEEE divide per column (the cache stage's arithmetic), and
+// scores that page from the new bf16 row in LDS; the scoring blocks skip
+// it. The per-page arithmetic is the same in both kinds of block.
 template <int MT, int KS>
 __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ kp,
@@ -45,19 +48,24 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
                                                          uint16_t* __restrict__ cent, int refresh,
                                                          float scale, float* __restrict__ scores) {
   constexpr int kQPer = (16 * MT * (DK / 8) + 255) / 256;  // query vectors per thread
+  constexpr int kQuads = DK / 4;                           // 4-column groups of a key row
   __shared__ __attribute__((aligned(16))) uint16_t qs[16 * MT * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t newrow[DK];
   const int b = blockIdx.y;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
+  const int col = lane & 15, q4 = lane >> 4;
   const int row0 = m.indptr[b];
   const int cap = m.indptr[b + 1] - row0;
   const int L = seq_len_clamped(m, b);
   int n = (L + m.page_size - 1) / m.page_size;
   n = n > cap ? cap : n;
+  const bool refresh_block = refresh && blockIdx.x == gridDim.x - 1;
+  const int n_scored = refresh ? n - 1 : n;  // pages the scoring blocks take
   const int blk0 = blockIdx.x * 64;
-  if (blk0 >= n) return;  // whole block: no barrier reached
+  if (refresh_block ? n == 0 : blk0 >= n_scored) return;  // whole block: no barrier reached
 
-  // This sequence's query rows (16 * MT heads x 576): all loads issued, then stored in LDS.
+  // This sequence's query rows (16 * MT heads x 576), loaded now, stored in LDS below.
   const uint16_t* qb = q + (size_t)b * (16 * MT) * DK;
   u32x4 qv[kQPer];
 #pragma unroll
@@ -65,27 +73,44 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
     const int c = t + 256 * u;
     if (c < 16 * MT * (DK / 8)) qv[u] = *(const u32x4*)(qb + (c / (DK / 8)) * DK + 8 * (c % (DK / 8)));
   }
-  if (refresh && n - 1 < blk0 + 64) {  // the newest page is in this block's range
+  // This lane's page and its centroid slice (B operand: page col, 8 columns per k step).
+  const int p = refresh_block ? n - 1 : blk0 + 16 * w + col;
+  const bool valid = refresh_block ? col == 0 && w == 0 : p < n_scored;
+  u32x4 bf[KS];  // KS k steps of 32 columns: 18 = all 576, 16 = the 512 latent ones
+  if (!refresh_block) {
+    const uint16_t* crow = cent + (size_t)(valid ? phys_page(m, row0 + p) : 0) * DK + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bf[ks] = valid ? *(const u32x4*)(crow + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+  } else {
+    // Newest page: thread t < 144 sums columns 4t .. 4t+3 over the valid
+    // tokens in order, all of its loads in flight at once.
     const int P = m.page_size;
-    const int pn = n - 1;
-    const int nv = min(P, L - pn * P);
-    const int pid = phys_page(m, row0 + pn);
-    const uint16_t* kb = kp + (size_t)pid * P * DK;
-    for (int pr = t; pr < DK / 2; pr += 256) {
-      float s0 = 0.f, s1 = 0.f;
-      for (int t0 = 0; t0 < nv; t0 += 32) {
-        uint32_t x[32];
+    const int nv = min(P, L - (n - 1) * P);
+    const int pid = phys_page(m, row0 + n - 1);
+    if (t < kQuads) {
+      const uint16_t* kb = kp + (size_t)pid * P * DK + 4 * t;
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      for (int t0 = 0; t0 < nv; t0 += 64) {
+        uint2 x[64];
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
-          if (t0 + u < nv) x[u] = *(const uint32_t*)(kb + (size_t)(t0 + u) * DK + 2 * pr);
+        for (int u = 0; u < 64; ++u)
+          if (t0 + u < nv) x[u] = *(const uint2*)(kb + (size_t)(t0 + u) * DK);
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
-          if (t0 + u < nv) { s0 += bf16_lo(x[u]); s1 += bf16_hi(x[u]); }
+        for (int u = 0; u < 64; ++u)
+          if (t0 + u < nv) {
+            s0 += bf16_lo(x[u].x); s1 += bf16_hi(x[u].x);
+            s2 += bf16_lo(x[u].y); s3 += bf16_hi(x[u].y);
+          }
       }
-      const float c0 = s0 / (float)nv, c1 = s1 / (float)nv;
-      const size_t o = (size_t)pid * DK + 2 * pr;
-      *(float2*)(cent32 + o) = make_float2(c0, c1);
-      *(uint32_t*)(cent + o) = (uint32_t)f32_to_bf16(c0) | ((uint32_t)f32_to_bf16(c1) << 16);
+      const float fn = (float)nv;
+      const float c0 = s0 / fn, c1 = s1 / fn, c2 = s2 / fn, c3 = s3 / fn;
+      const size_t o = (size_t)pid * DK + 4 * t;
+      *(float4*)(cent32 + o) = make_float4(c0, c1, c2, c3);
+      const uint2 h = make_uint2((uint32_t)f32_to_bf16(c0) | ((uint32_t)f32_to_bf16(c1) << 16),
+                                 (uint32_t)f32_to_bf16(c2) | ((uint32_t)f32_to_bf16(c3) << 16));
+      *(uint2*)(cent + o) = h;
+      *(uint2*)(newrow + 4 * t) = h;
     }
   }
 #pragma unroll
@@ -94,18 +119,14 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
     if (c < 16 * MT * (DK / 8)) *(u32x4*)(qs + (c / (DK / 8)) * ROW + 8 * (c % (DK / 8))) = qv[u];
   }
   __syncthreads();
-
-  const int base = blk0 + 16 * w;
-  if (base >= n) return;
-  const int col = lane & 15, q4 = lane >> 4;
-  const int p = base + col;
-  const bool valid = p < n;
-  const uint16_t* crow = cent + (size_t)(valid ? phys_page(m, row0 + p) : 0) * DK + 8 * q4;
-
-  u32x4 bf[KS];  // KS k steps of 32 columns: 18 = all 576, 16 = the 512 latent ones
+  if (refresh_block) {
+    if (w != 0) return;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    bf[ks] = valid ? *(const u32x4*)(crow + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < KS; ++ks)
+      bf[ks] = valid ? *(const u32x4*)(newrow + 8 * q4 + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+  } else if (blk0 + 16 * w >= n_scored) {
+    return;
+  }
 
   f32x4 acc[MT];
 #pragma unroll
@@ -115,12 +136,12 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma(*(const u32x4*)(arow + 32 * ks), bf[ks], acc[mt]);
   }
-  float s = 0.f;
+  float sc = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) s += (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  if (lane < 16 && valid) scores[row0 + p] = s * scale;
+  for (int mt = 0; mt < MT; ++mt) sc += (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
+  sc += __shfl_xor(sc, 16);
+  sc += __shfl_xor(sc, 32);
+  if (lane < 16 && valid) scores[row0 + p] = sc * scale;
 }
 
 // ---------------------------------------------------------------- attention
@@ -520,7 +541,7 @@ hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* 
                                    int refresh, float scale, float* scores, int max_pages,
                                    hipStream_t s) {
   if (m.nnz == 0 || m.batch == 0) return hipSuccess;
-  dim3 grid((max_pages + 63) / 64, m.batch), block(256);
+  dim3 grid((max_pages + 63) / 64 + (refresh ? 1 : 0), m.batch), block(256);
   const bool latent_only = g.score_dim == DV;
 #define VX_MLA_SC(MT, KS)                                                                     \
   hipLaunchKernelGGL((scores_mla_kernel<MT, KS>), grid, block, 0, s, m, (const uint16_t*)q,  \
