@@ -172,7 +172,7 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   __syncthreads();  // every key of the segment is in LDS
   const uint32_t rnd = a.mode == VX_TOPK_APPROX ? a.rnd[seg] : 0u;
   if (n > kBlockSelectMin)
-    block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + 256, n, a.k, a.n_sink,
+    block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + kSelectHistWords, n, a.k, a.n_sink,
                           a.n_local, a.mode, rnd, a.sel + (size_t)seg * a.stride, a.stride,
                           a.sel_count + seg, sel_lds, count_lds);
   else if (w == 0)

@@ -514,7 +514,7 @@ __global__ __launch_bounds__(256 * MT) void decode_mla_kernel(MlaStepArgs a) {
   int32_t* gsel = s == 0 ? a.sel + (size_t)b * a.stride : nullptr;
   int32_t* gcnt = s == 0 ? a.sel_count + b : nullptr;
   if (n > kBlockSelectMin)
-    block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + 256, n, a.k, a.n_sink,
+    block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + kSelectHistWords, n, a.k, a.n_sink,
                           a.n_local, a.mode, rnd, gsel, a.stride, gcnt, sel_l, &cnt_l);
   else if (w == 0)
     wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd, gsel,

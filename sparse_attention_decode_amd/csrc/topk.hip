@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64 * kTopkBlockWaves) void topk_block_kernel(
   for (int i = threadIdx.x; i < n; i += 64 * kTopkBlockWaves)
     keys[i] = (i < n_sink || i >= n - n_local) ? 0u : topk_detail::score_key(sc[i]);
   __syncthreads();
-  block_select_keys<kTopkBlockWaves>(keys, keys + cap_keys, keys + cap_keys + 256, n, k, n_sink,
+  block_select_keys<kTopkBlockWaves>(keys, keys + cap_keys, keys + cap_keys + kSelectHistWords, n, k, n_sink,
                                      n_local, mode, mode == VX_TOPK_APPROX ? rnd[seg] : 0u,
                                      sel + (size_t)seg * stride, stride, sel_count + seg);
 }

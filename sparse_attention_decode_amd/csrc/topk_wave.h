@@ -140,7 +140,12 @@ __device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, 
     const uint32_t trank = tie_seen + rank_below(tmask);
     tie_seen += (uint32_t)__popcll(tmask);
     bool take = forced || above;
-    if (tie && members) take = take || ((trank + members - off) % members) < r;
+    if (tie && members) {
+      // cyclic position from off: trank, off < members, so one wrap at most
+      uint32_t pos = trank + members - off;
+      pos = pos >= members ? pos - members : pos;
+      take = take || pos < r;
+    }
     const unsigned long long smask = __ballot(take);
     if (take) {
       if (out) out[written + rank_below(smask)] = i;
@@ -154,6 +159,90 @@ __device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, 
   if (lane == 0) {
     if (count_out) *count_out = (int32_t)written;
     if (count_lds) *count_lds = (int32_t)written;
+  }
+}
+
+// Number of tie ranks g in [0, x) that are taken: (g - off) mod members < r,
+// the cyclic window of length r starting at off (x <= members).
+__device__ __forceinline__ uint32_t ties_taken_below(uint32_t x, uint32_t r, uint32_t off,
+                                                     uint32_t members) {
+  const uint32_t end = off + r;  // window [off, end), wrapping past members
+  uint32_t c = x > off ? min(x, min(end, members)) - off : 0u;
+  if (end > members) c += min(x, end - members);
+  return c;
+}
+
+// wave_compact with all NW waves of the block: wave w takes a contiguous
+// range of the keys; one barrier publishes each range's counts (taken
+// forced / above keys, tie members), from which every wave derives its
+// output offset and its first tie rank; the order of the output is the
+// same as wave_compact's. `red` is 2 * NW words of LDS.
+template <int NW>
+__device__ __forceinline__ void block_compact(const uint32_t* __restrict__ keys, int n, int n_sink,
+                                              int n_local, uint32_t prefix, uint32_t mask,
+                                              uint32_t r, uint32_t off, uint32_t members,
+                                              int32_t* __restrict__ out, int stride,
+                                              int32_t* __restrict__ count_out,
+                                              int32_t* __restrict__ out_lds,
+                                              int32_t* __restrict__ count_lds,
+                                              uint32_t* __restrict__ red) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int per = (n + NW - 1) / NW;
+  const int lo = min(n, w * per), hi = min(n, lo + per);
+  auto classify = [&](int i, bool& sure, bool& tie) {
+    const bool in = i < hi;
+    const uint32_t kv = in ? keys[i] : 0u;
+    const bool forced = in && (i < n_sink || i >= n - n_local);
+    const bool cand = kv != 0u;
+    sure = forced || (cand && (kv & mask) > prefix);
+    tie = cand && (kv & mask) == prefix;
+  };
+  uint32_t n_sure = 0, n_tie = 0;
+  for (int base = lo; base < hi; base += 64) {
+    bool sure, tie;
+    classify(base + lane, sure, tie);
+    n_sure += (uint32_t)__popcll(__ballot(sure));
+    n_tie += (uint32_t)__popcll(__ballot(tie));
+  }
+  if (lane == 0) { red[w] = n_sure; red[NW + w] = n_tie; }
+  __syncthreads();
+  uint32_t out0 = 0, tie0 = 0, total = 0, ties_before = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t a = red[v], c = red[NW + v];
+    const uint32_t taken = members ? ties_taken_below(ties_before + c, r, off, members) -
+                                         ties_taken_below(ties_before, r, off, members)
+                                   : 0u;
+    if (v < w) { out0 += a + taken; tie0 += c; }
+    total += a + taken;
+    ties_before += c;
+  }
+  uint32_t written = out0, tie_seen = tie0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    bool sure, tie;
+    classify(i, sure, tie);
+    const unsigned long long tmask = __ballot(tie);
+    const uint32_t trank = tie_seen + rank_below(tmask);
+    tie_seen += (uint32_t)__popcll(tmask);
+    bool take = sure;
+    if (tie && members) {
+      uint32_t pos = trank + members - off;
+      pos = pos >= members ? pos - members : pos;
+      take = take || pos < r;
+    }
+    const unsigned long long smask = __ballot(take);
+    if (take) {
+      if (out) out[written + rank_below(smask)] = i;
+      if (out_lds) out_lds[written + rank_below(smask)] = i;
+    }
+    written += (uint32_t)__popcll(smask);
+  }
+  if (out)
+    for (int i = (int)total + t; i < stride; i += 64 * NW) out[i] = -1;
+  if (t == 0) {
+    if (count_out) *count_out = (int32_t)total;
+    if (count_lds) *count_lds = (int32_t)total;
   }
 }
 
@@ -270,11 +359,11 @@ __device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
 }
 
 // Select for one segment with all NW waves of a block (every thread calls
-// it; n is the same for all). keys / hist as for wave_select_keys; `red` is
-// 2 * NW words of LDS. The min / max sweep and each digit pass's histogram
+// it; n is the same for all). keys as for wave_select_keys; `hist` is
+// kSelectHistWords words of LDS, `red` 2 * NW more. The min / max sweep and each digit pass's histogram
 // are shared by the waves; every wave reads the finished histogram and finds
-// the same digit, so no broadcast is needed; wave 0 compacts. Same result as
-// wave_select_keys: the selection rule has one answer.
+// the same digit, so no broadcast is needed; the waves compact together.
+// Same result as wave_select_keys: the selection rule has one answer.
 template <int NW>
 __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
                                                   uint32_t* __restrict__ hist,
@@ -299,6 +388,8 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
     kmax = wave_max(kmax);
     kminc = wave_max(kminc);
     if (lane == 0) { red[w] = kmax; red[NW + w] = kminc; }
+    // histograms 0 and 1 start at zero; pass j zeroes histogram (j + 2) % 3
+    if (t < 128) *(uint4*)(hist + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     kmax = 0u;
     kminc = 0u;
@@ -310,8 +401,6 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
       const float wdt = __fsub_rn(mx, mn);
       const bool spread = wdt > 0.f;
       const float inv = spread ? __fdiv_rn(256.f, wdt) : 0.f;
-      if (t < 64) *(uint4*)(hist + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
-      __syncthreads();
       for (int i = t; i < n; i += 64 * NW) {
         const uint32_t kv = keys[i];
         if (kv) {
@@ -338,16 +427,19 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
       const int top = __clz(kmin ^ kmax) / 8;
       mask = top ? 0xffffffffu << (32 - 8 * top) : 0u;
       prefix = kmin & mask;
-      for (int shift = 24 - 8 * top; shift >= 0; shift -= 8) {
-        __syncthreads();  // the previous pass's readers are done with hist
-        if (t < 64) *(uint4*)(hist + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
+      // One barrier per pass: pass j counts into histogram j % 3, which was
+      // zeroed during pass j - 2 (or at the start), and zeroes histogram
+      // (j + 2) % 3, whose last readers finished before this pass's barrier.
+      int j = 0;
+      for (int shift = 24 - 8 * top; shift >= 0; shift -= 8, ++j) {
+        uint32_t* h = hist + 256 * (j % 3);
         for (int i = t; i < n; i += 64 * NW) {
           const uint32_t kv = keys[i];
-          if (kv && (kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+          if (kv && (kv & mask) == prefix) atomicAdd(&h[(kv >> shift) & 255u], 1u);
         }
         __syncthreads();
-        const Digit dg = find_digit(hist, r, lane);
+        if (t < 64) *(uint4*)(hist + 256 * ((j + 2) % 3) + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
+        const Digit dg = find_digit(h, r, lane);
         prefix |= dg.d << shift;
         mask |= 255u << shift;
         r -= dg.above;
@@ -357,9 +449,8 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
     }
   }
   __syncthreads();  // keys final, histogram readers done
-  if (w == 0)
-    wave_compact(keys, n, n_sink, n_local, prefix, mask, r, off, members, out, stride, count_out,
-                 lane, out_lds, count_lds);
+  block_compact<NW>(keys, n, n_sink, n_local, prefix, mask, r, off, members, out, stride,
+                    count_out, out_lds, count_lds, red);
 }
 
 // Select for one segment: `sc` points at its n scores, `keys` / `hist` at

@@ -227,7 +227,8 @@ inline int gqa_attn_waves(int G, int max_pages) {
 constexpr int kMaxFusedStepPages = 4096;
 // LDS words a segment's selection needs besides its keys: the 256-word
 // histogram and the block select's 2 * 16 reduction words.
-constexpr int kSelectExtraWords = 256 + 32;
+constexpr int kSelectHistWords = 3 * 256;  // three rotating digit histograms
+constexpr int kSelectExtraWords = kSelectHistWords + 32;
 // Segments longer than this are selected by every wave of the block.
 constexpr int kBlockSelectMin = 256;
 // Largest per-sequence page count the top-k supports (LDS resident keys).
