@@ -234,9 +234,12 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom,
  * followed by vx_sparse_decode with the same arguments (the latter's sel /
  * sel_count being the former's outputs). When the plan has one split per
  * (sequence, KV head) and the geometry is GQA, bf16, Dk = 128 with
- * sel_stride <= 128 and max_pages <= 4096, it is one kernel with a block per
- * (sequence, KV head) that indexes and then attends over its own selection;
- * otherwise the two calls' kernels run in turn.
+ * sel_stride <= 256 and max_pages <= 4096, it is one kernel with a block per
+ * (sequence, KV head) that indexes and then attends over its own selection.
+ * MLA: the scorer, then one kernel in which every split block selects its
+ * sequence's pages from the scores (the first split writes sel / sel_count)
+ * and attends over its share, then the split merge. Otherwise the two calls'
+ * kernels run in turn.
  * workspace == NULL: writes the bytes needed to *workspace_bytes (those of
  * vx_sparse_decode) and returns VX_OK; otherwise *workspace_bytes must be at
  * least that. */

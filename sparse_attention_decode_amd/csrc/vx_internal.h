@@ -214,7 +214,7 @@ hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* 
 
 // Largest selection one attention split streams: its page list sits in LDS,
 // one entry per thread of the block that fills it (blocks have >= 256).
-constexpr int kMaxPagesPerSplit = 128;
+constexpr int kMaxPagesPerSplit = 256;
 // Waves per block of the GQA bf16 attention (standalone and whole-step
 // kernels alike, so both sum in the same order): 16 for short segments with
 // G <= 4 (more chunks in flight at once), else 8.

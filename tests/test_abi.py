@@ -142,13 +142,15 @@ def test_planner_splits_and_workspace():
     # an explicit split count is honoured (balanced splits, largest one reported)
     plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 7, 256)
     assert plan["num_splits"] == 7 and plan["pages_per_split"] == 3
-    # never more splits than selected pages, never more than 128 pages per split
+    # never more splits than selected pages, never more than 256 pages per split
     plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64), g.__class__(2, 1, 64, 64, 0, 0, 0), 9, 0, 256)
     assert plan["num_splits"] == 9
     plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=200), g, 131, 1, 256)
-    assert plan["pages_per_split"] <= 128 and plan["num_splits"] == 2
+    assert plan["pages_per_split"] == 131 and plan["num_splits"] == 1
     plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=300), g, 260, 1, 256)
-    assert plan["pages_per_split"] <= 128 and plan["num_splits"] == 3
+    assert plan["pages_per_split"] <= 256 and plan["num_splits"] == 2
+    plan = V.vx_plan_decode(pages(batch=4096, nnz=2000000, pool=2000000, maxp=600), g, 520, 1, 256)
+    assert plan["pages_per_split"] <= 256 and plan["num_splits"] == 3
     # MLA: one block per sequence and split
     mla = V.make_geom(32, 1, 576, 512, 1, V.VX_BF16, V.VX_BF16)
     plan = V.vx_plan_decode(pages(batch=32, nnz=20480, pool=25600, maxp=1024, page_size=64), mla, 34, 0, 256)
@@ -224,7 +226,8 @@ def test_plan_reports_the_whole_step_kernel():
     big = pages(batch=32, nnz=6144, pool=7680, maxp=256)
     assert V.vx_plan_decode(big, g, 18, 0, 256)["fused_step"] == 1
     assert V.vx_plan_decode(big, g, 18, 2, 256)["fused_step"] == 0  # two splits
-    assert V.vx_plan_decode(big, g, 131, 0, 256)["fused_step"] == 0  # selection > 128 pages
+    assert V.vx_plan_decode(big, g, 131, 0, 256)["fused_step"] == 1
+    assert V.vx_plan_decode(big, g, 257, 0, 256)["fused_step"] == 0  # selection > 256 pages
     assert V.vx_plan_decode(big, geom(qd=V.VX_F32, kvd=V.VX_F32), 18, 0, 256)["fused_step"] == 0
     huge = pages(batch=32, nnz=200000, pool=200000, maxp=5000)
     assert V.vx_plan_decode(huge, g, 18, 0, 256)["fused_step"] == 0  # capacity > 4096 pages
