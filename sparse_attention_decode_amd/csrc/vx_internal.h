@@ -225,8 +225,8 @@ inline int gqa_attn_waves(int G, int max_pages) {
 // Largest page capacity for which the whole-step kernel keeps every entry's
 // key and physical page in LDS.
 constexpr int kMaxFusedStepPages = 4096;
-// LDS words a segment's selection needs besides its keys: the 256-word
-// histogram and the block select's 2 * 16 reduction words.
+// LDS words a segment's selection needs besides its keys: three 256-word
+// digit histograms and the block select's 2 * 16 reduction words.
 constexpr int kSelectHistWords = 3 * 256;  // three rotating digit histograms
 constexpr int kSelectExtraWords = kSelectHistWords + 32;
 // Segments longer than this are selected by every wave of the block.

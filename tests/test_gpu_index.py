@@ -87,6 +87,24 @@ def test_large_capacity():
     check_step_against_oracle(w, step, range(3))
 
 
+def test_very_large_capacity():
+    """A page capacity of ~8200 pages (beyond the whole-step kernel's 4096):
+    the indexer and attention kernels give the same bits as the separate
+    calls, and match the oracle."""
+    sp = W.spec("gqa_bf16", batch=2, num_q_heads=4, num_kv_heads=2,
+                lengths=("list", (3000, 70)), headroom_tokens=130000)
+    w = W.make(sp, "cuda", seed=13)
+    assert w.max_pages > 8000
+    fused_vs_separate(w, appends=1)
+    step = DecodeStep(w)
+    step.rebuild_centroids()
+    step.run()
+    T.sync()
+    check_step_against_oracle(w, step, range(2))
+    del w, step
+    torch.cuda.empty_cache()
+
+
 def check_step_against_oracle(w, step, sample):
     out = step.out.cpu().double().numpy()
     lse = step.lse.cpu().double().numpy()
