@@ -164,29 +164,28 @@ VX_DEV void mfma_attend(MfmaShared<G, NW>& sm, const int* pg_phys, const int* pg
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < G * DK / 4; t += blockDim.x) {
-    const int h = t / (DK / 4), d = (t % (DK / 4)) * 4;
+  // One output element per thread (the waves' sum in wave order).
+  for (int t = threadIdx.x; t < G * DK; t += blockDim.x) {
+    const int h = t / DK, d = t % DK;
     float mmax = kNegBig;
 #pragma unroll
     for (int v = 0; v < NW; ++v) mmax = fmaxf(mmax, sm.red_ml[v][h][0]);
-    float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f, acc = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
       const float wt = __builtin_amdgcn_exp2f(sm.red_ml[v][h][0] - mmax);
       lsum = fmaf(sm.red_ml[v][h][1], wt, lsum);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(sm.red_o[v][h][d + e], wt, acc[e]);
+      acc = fmaf(sm.red_o[v][h][d], wt, acc);
     }
     const int head = g * G + h;
     if (S == 1) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      *(float4*)(out + ((size_t)b * hq + head) * DK + d) =
-          make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      out[((size_t)b * hq + head) * DK + d] = acc * inv;
       if (lse && d == 0)
         lse[(size_t)b * hq + head] = lsum > 0.f ? (mmax + log2f(lsum)) * kLn2 : -INFINITY;
     } else {
       const size_t ps = ((size_t)b * hq + head) * S + s;
-      *(float4*)(part_o + ps * DK + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      part_o[ps * DK + d] = acc;
       if (d == 0) {
         part_ml[2 * ps] = mmax;
         part_ml[2 * ps + 1] = lsum;

@@ -3,9 +3,9 @@
 //
 // Vortex paper note, "Key results > MLA": the rope part matters for routing,
 // so pages are scored on all 576 columns; "System design > 3. Execution
-// backend" adds an attention kernel for general MLA geometry. Both kernels
-// here are dense bf16 contractions across the query heads and run on the
-// gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
+// backend" adds an attention kernel for general MLA geometry. The scoring
+// and attention here are dense bf16 contractions across the query heads on
+// the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
 // MFMA operand layout used throughout (lane l, 16 = l % 16, q4 = l / 16):
 //   A (16 x 32):  lane holds row (l % 16), k elements 8*q4 .. 8*q4+7
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 
 // ---------------------------------------------------------------- attention
 // One block of 4 MT waves (MT head tiles of 16) per (sequence b, split s);
-// the split holds a balanced share of the selected pages, consumed one
+// the split holds an even share of the selection's entries, consumed one
 // 64-token page (a "chunk") at a time. Wave w works on head tile mt = w / 4
 // and quarter u = w % 4: token tile u (tokens 16 u ..) in q.k^T, value
 // columns 128 u .. 128 u + 127 in P.V.
@@ -163,8 +163,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 //   rope granule g >= 64:   load 64 + t / 8,
 //                           lane 8 (t % 8) + (((g - 64) ^ t) % 8).
 // q.k^T  v_mfma_f32_16x16x32_bf16, A = the tile's query rows (registers),
-//        B = key granules (lane: token l % 16, 8 columns per k step). Row
-//        maxima of the four token tiles are exchanged through LDS.
+//        B = key granules (lane: token l % 16, 8 columns per k step).
 // P.V    lane (q4, c) reads tokens 8 q4 .. 8 q4 + 7 of each 32-token half,
 //        columns 8 c .. 8 c + 7 of its quarter (eight 16-byte reads); taking
 //        N-tile e's columns as {8 c + e}, element e of the lane's eight rows
