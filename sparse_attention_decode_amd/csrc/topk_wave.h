@@ -206,17 +206,19 @@ __device__ __forceinline__ void block_compact(const uint32_t* __restrict__ keys,
   }
   if (lane == 0) { red[w] = n_sure; red[NW + w] = n_tie; }
   __syncthreads();
-  uint32_t out0 = 0, tie0 = 0, total = 0, ties_before = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const uint32_t a = red[v], c = red[NW + v];
-    const uint32_t taken = members ? ties_taken_below(ties_before + c, r, off, members) -
-                                         ties_taken_below(ties_before, r, off, members)
-                                   : 0u;
-    if (v < w) { out0 += a + taken; tie0 += c; }
-    total += a + taken;
-    ties_before += c;
-  }
+  // Lane v < NW takes range v's counts; wave scans give every range's first
+  // tie rank and output offset.
+  const uint32_t a_v = lane < NW ? red[lane] : 0u;
+  const uint32_t c_v = lane < NW ? red[NW + lane] : 0u;
+  const uint32_t ties_before = prefix_sum(c_v) - c_v;
+  const uint32_t taken = members ? ties_taken_below(ties_before + c_v, r, off, members) -
+                                       ties_taken_below(ties_before, r, off, members)
+                                 : 0u;
+  const uint32_t take_v = a_v + taken;
+  const uint32_t take_incl = prefix_sum(take_v);
+  const uint32_t out0 = (uint32_t)__builtin_amdgcn_readlane((int)(take_incl - take_v), w);
+  const uint32_t tie0 = (uint32_t)__builtin_amdgcn_readlane((int)ties_before, w);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)take_incl, NW - 1);
   uint32_t written = out0, tie_seen = tie0;
   for (int base = lo; base < hi; base += 64) {
     const int i = base + lane;
