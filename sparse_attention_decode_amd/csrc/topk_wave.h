@@ -393,10 +393,8 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
     // histograms 0 and 1 start at zero; pass j zeroes histogram (j + 2) % 3
     if (t < 128) *(uint4*)(hist + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    kmax = 0u;
-    kminc = 0u;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) { kmax = max(kmax, red[v]); kminc = max(kminc, red[NW + v]); }
+    kmax = wave_max(lane < NW ? red[lane] : 0u);
+    kminc = wave_max(lane < NW ? red[NW + lane] : 0u);
     const uint32_t kmin = ~kminc;
     if (mode == VX_TOPK_APPROX) {
       const float mn = key_score(kmin), mx = key_score(kmax);
