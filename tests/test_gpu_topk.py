@@ -102,3 +102,24 @@ def test_topk_large_segments():
         for g in range(hkv):
             want = O.topk_exact(scores[b * hkv + g].astype(np.float64), 64, 1, 1)
             np.testing.assert_array_equal(sel[b, g][:len(want)], want)
+
+
+@pytest.mark.parametrize("mode", [V.VX_TOPK_EXACT, V.VX_TOPK_APPROX])
+def test_topk_maximum_segment(mode):
+    """A segment at the largest supported page count (16000: its keys and
+    histograms take more than 64 KB of LDS) next to a short one; exact mode
+    against the oracle, approximate mode against the oracle's reading of it."""
+    hkv, batch = 1, 2
+    rng = np.random.default_rng(9)
+    ns = np.array([16000, 40])
+    scores = [rng.standard_normal(n).astype(np.float32) for n in ns]
+    rnd = rng.integers(0, 2**32, size=(batch, hkv), dtype=np.uint64).astype(np.uint32)
+    sel, cnt = run_topk(ns, scores, hkv, 200, 1, 2, mode, rnd)
+    for b in range(batch):
+        s64 = scores[b].astype(np.float64)
+        if mode == V.VX_TOPK_EXACT:
+            want = O.topk_exact(s64, 200, 1, 2)
+        else:
+            want = O.topk_approx(scores[b], 200, 1, 2, int(rnd[b, 0]))
+        np.testing.assert_array_equal(sel[b, 0][:len(want)], want)  # padded with -1
+        assert cnt[b, 0] == int((want >= 0).sum())
