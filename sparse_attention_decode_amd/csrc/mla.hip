@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
                                                          float scale, float* __restrict__ scores) {
   constexpr int kQPer = (16 * MT * (DK / 8) + 255) / 256;  // query vectors per thread
   constexpr int kQuads = DK / 4;                           // 4-column groups of a key row
+  static_assert(kQuads <= 256, "the refresh takes one 4-column group per thread");
   __shared__ __attribute__((aligned(16))) uint16_t qs[16 * MT * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t newrow[DK];
   const int b = blockIdx.y;
