@@ -242,3 +242,15 @@ def test_mla_latent_only_scoring(name):
     _, _, differing = pipeline_check(w, range(w.batch), DecodeStep(w, score_dim=512))
     assert differing <= max(1, w.batch // 20)
     step_vs_calls(w, score_dim=512)
+
+
+@pytest.mark.parametrize("k,n_sink,n_local", [(0, 1, 1), (3, 0, 0), (200, 1, 1), (5, 2, 0),
+                                              (5, 0, 3)])
+@pytest.mark.parametrize("name", ["gqa_small", "mla_small", "mla16_small"])
+def test_step_selection_budgets(name, k, n_sink, n_local):
+    """The whole-step kernels select inside the attention kernel: other
+    budgets and forced windows (none, k = 0, k beyond the page count) give
+    the same bits as the separate calls, and the oracle's attention."""
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=20), "cpu", seed=23))
+    one = step_vs_calls(w, appends=1, k=k, n_sink=n_sink, n_local=n_local)
+    assert check_step_against_oracle(w, one, range(w.batch)) <= max(1, w.batch // 20)
