@@ -216,6 +216,28 @@ def copy_calibration():
     log("copy calibration: 5 launches, each reads 1 GiB and writes 1 GiB")
 
 
+def stream_copy_GBps():
+    """Bytes moved per second by a plain device copy of 1 GiB (1 GiB read +
+    1 GiB written), the streaming rate this machine reaches, reported next to
+    the step's rate."""
+    import torch
+    n = 1 << 28
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 5 * 2 * (n * 4) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
 def dense_compare(a):
     """Decode attention over the selected pages vs over every page (k = all
     pages, the same kernels), at a shape like the pages' kernel ablation:
@@ -392,6 +414,8 @@ def main():
         del g
     log("stage us: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
 
+    copy_gbps = stream_copy_GBps()
+    log(f"streaming copy of 1 GiB: {copy_gbps:.0f} GB/s (read + write)")
     t_step = ms_step / 1e3
     s = sp
     seqs_per_s = s.batch / t_step
@@ -427,6 +451,7 @@ def main():
         "step_bytes": total_b,
         "step_hbm_GBps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_GBPS,
+        "stream_copy_GBps": copy_gbps,
         "stage_us": stage_us,
         "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
