@@ -39,6 +39,13 @@ pinned by closed forms, invariants, brute force or an independent library
 routine (tests/test_oracle_pins.py). ``topk_approx`` follows this project's
 reading of an undescribed mechanism and is pinned only by the invariants its
 reading implies (parity unpinned against the pages themselves).
+
+An alternative cache stage and scorer, ``page_bounds`` and ``bound_scores``,
+states the query-aware page bounds of Quest (Tang et al., "Quest:
+Query-Aware Sparsity for Efficient Long-Context LLM Inference", ICML 2024),
+which the Vortex paper note names as its other baseline ("Paper context",
+"Key results > User-side latency"): per page the elementwise minimum and maximum of its keys,
+and as the page's score an upper bound of q . k over its tokens.
 """
 
 from __future__ import annotations
@@ -50,7 +57,7 @@ import numpy as np
 __all__ = [
     "num_pages", "valid_tokens", "centroids", "round_to_bf16", "page_scores",
     "forced_pages", "topk_exact", "topk_approx", "approx_buckets",
-    "attention", "decode_sequence",
+    "attention", "decode_sequence", "page_bounds", "bound_scores",
 ]
 
 
@@ -115,6 +122,43 @@ def page_scores(q: np.ndarray, cent: np.ndarray, num_kv_heads: int,
         per_head = heads @ cent[:, g, :].T  # [G][n]
         s[g] = scale * per_head.sum(axis=0)
     return s
+
+
+def page_bounds(k: np.ndarray, seq_len: int, page_size: int) -> tuple[np.ndarray, np.ndarray]:
+    """Alternative cache stage (Quest's page metadata): for each page in use
+    and KV head, the elementwise minimum and maximum of the page's valid
+    keys. Returns (lo, hi), each [n][Hkv][Dk]."""
+    n = num_pages(seq_len, page_size)
+    hkv, dk = k.shape[1], k.shape[3]
+    lo = np.zeros((n, hkv, dk))
+    hi = np.zeros((n, hkv, dk))
+    for p in range(n):
+        keys = k[p, :, :valid_tokens(seq_len, page_size, p), :]  # [Hkv][nv][Dk]
+        lo[p] = keys.min(axis=1)
+        hi[p] = keys.max(axis=1)
+    return lo, hi
+
+
+def bound_scores(q: np.ndarray, lo: np.ndarray, hi: np.ndarray, num_kv_heads: int,
+                 scale: float) -> np.ndarray:
+    """Alternative scorer (Quest's criticality bound), for a GQA group: with
+    Q the group-summed query of KV head g (the query the centroid scorer
+    uses), the score of page p is scale * sum over dims d of
+    max(Q_d * lo_d, Q_d * hi_d). Since lo_d <= k_d <= hi_d for every key k of
+    the page, each term bounds Q_d * k_d from above, so the score bounds
+    scale * Q . k for every token of the page, and is the least such bound
+    that depends on lo and hi alone (the box's best corner attains it).
+    Returns [Hkv][n]."""
+    hq = q.shape[0]
+    G = hq // num_kv_heads
+    n = lo.shape[0]
+    out = np.zeros((num_kv_heads, n))
+    for g in range(num_kv_heads):
+        Q = q[g * G:(g + 1) * G].sum(axis=0)  # [Dk]
+        a = Q[None, :] * lo[:, g, :]  # [n][Dk]
+        b = Q[None, :] * hi[:, g, :]
+        out[g] = np.maximum(a, b).sum(axis=1)
+    return out * scale
 
 
 def forced_pages(n: int, n_sink: int, n_local: int) -> list[int]:
@@ -266,17 +310,23 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_len: int,
 def decode_sequence(seq: dict, *, page_size: int, num_kv_heads: int, k: int,
                     n_sink: int, n_local: int, score_scale: float,
                     sm_scale: float, mla: bool = False, head_dim_v: int = None,
-                    approx: bool = False, score_dim: int = None) -> dict:
+                    approx: bool = False, score_dim: int = None,
+                    indexer: str = "centroid") -> dict:
     """The whole step for one sequence: cache stage, scoring, selection,
     attention. ``seq`` holds q, k, v (v None for MLA), seq_len and rand_u32
     ([Hkv] uint32 draws for the approximate selection); ``score_dim`` as in
-    page_scores."""
+    page_scores; ``indexer`` "centroid" (the method) or "bounds" (Quest's
+    page bounds, GQA only)."""
     q, kk, vv, L = seq["q"], seq["k"], seq["v"], seq["seq_len"]
     if mla:
         vv = kk[..., :head_dim_v]
     cent = centroids(kk, L, page_size)
-    score_cent = round_to_bf16(cent) if mla else cent
-    scores = page_scores(q, score_cent, num_kv_heads, score_scale, score_dim)
+    if indexer == "bounds":
+        lo, hi = page_bounds(kk, L, page_size)
+        scores = bound_scores(q, lo, hi, num_kv_heads, score_scale)
+    else:
+        score_cent = round_to_bf16(cent) if mla else cent
+        scores = page_scores(q, score_cent, num_kv_heads, score_scale, score_dim)
     k_out = k + n_sink + n_local
     sel = np.full((num_kv_heads, k_out), -1, dtype=np.int64)
     for g in range(num_kv_heads):
@@ -286,4 +336,7 @@ def decode_sequence(seq: dict, *, page_size: int, num_kv_heads: int, k: int,
         else:
             sel[g] = topk_exact(scores[g], k, n_sink, n_local)
     out, lse = attention(q, kk, vv, L, page_size, sel, sm_scale, num_kv_heads)
-    return {"centroids": cent, "scores": scores, "sel": sel, "out": out, "lse": lse}
+    r = {"centroids": cent, "scores": scores, "sel": sel, "out": out, "lse": lse}
+    if indexer == "bounds":
+        r["lo"], r["hi"] = lo, hi
+    return r

@@ -339,3 +339,101 @@ def test_approx_buckets_closed_form():
     np.testing.assert_array_equal(
         O.approx_buckets(np.array([-1.0, -0.75, -0.5, 1.0], np.float32)), [0, 32, 64, 255])
     np.testing.assert_array_equal(O.approx_buckets(np.full(7, 2.5, np.float32)), 0)
+
+
+# ---------------------------------------------- page bounds (Quest-style indexer)
+
+def test_page_bounds_brute_force_and_garbage_ignored():
+    """min/max over the valid tokens of each page, taken element by element
+    with Python's own min/max; slots past the last token hold garbage that
+    must not leak in."""
+    rng = np.random.default_rng(5)
+    P, L, Hkv, D = 4, 10, 2, 3
+    k = rng.standard_normal((4, Hkv, P, D))
+    k[2, :, 2:, :] = 1e9   # page 2 holds 2 tokens; the rest is garbage
+    k[3] = -1e9            # capacity page, not in use
+    lo, hi = O.page_bounds(k, L, P)
+    assert lo.shape == (3, Hkv, D)
+    for p in range(3):
+        nv = min(P, L - p * P)
+        for g in range(Hkv):
+            for d in range(D):
+                col = [k[p, g, t, d] for t in range(nv)]
+                assert lo[p, g, d] == min(col) and hi[p, g, d] == max(col)
+
+
+def test_bound_scores_is_best_corner_of_the_box():
+    """The score equals the largest group-summed logit over the 2^D corners
+    of the page's min/max box (a linear function's maximum over a box sits
+    at a corner), found here by enumeration."""
+    import itertools
+    rng = np.random.default_rng(6)
+    Hq, Hkv, D, n = 4, 2, 4, 3
+    q = rng.standard_normal((Hq, D))
+    lo = rng.standard_normal((n, Hkv, D))
+    hi = lo + rng.random((n, Hkv, D))
+    s = O.bound_scores(q, lo, hi, Hkv, 0.5)
+    for g in range(Hkv):
+        for p in range(n):
+            best = -np.inf
+            for bits in itertools.product((0, 1), repeat=D):
+                c = np.where(np.array(bits) == 1, hi[p, g], lo[p, g])
+                val = sum(float(q[h] @ c) for h in (2 * g, 2 * g + 1))
+                best = max(best, val)
+            np.testing.assert_allclose(s[g, p], 0.5 * best, rtol=1e-13)
+
+
+def test_bound_scores_bounds_every_token_and_is_exact_for_one_token():
+    """Upper bound of scale * sum_h q_h . k over every valid token; a page
+    with a single valid token scores exactly its logit."""
+    rng = np.random.default_rng(7)
+    P, L, Hq, Hkv, D = 8, 41, 6, 2, 16
+    k = rng.standard_normal((6, Hkv, P, D))
+    q = rng.standard_normal((Hq, D))
+    lo, hi = O.page_bounds(k, L, P)
+    s = O.bound_scores(q, lo, hi, Hkv, 0.25)
+    n = -(-L // P)
+    for g in range(Hkv):
+        for p in range(n):
+            nv = min(P, L - p * P)
+            logits = [0.25 * sum(float(q[h] @ k[p, g, t]) for h in range(3 * g, 3 * g + 3))
+                      for t in range(nv)]
+            assert s[g, p] >= max(logits) - 1e-12
+            if nv == 1:
+                np.testing.assert_allclose(s[g, p], logits[0], rtol=1e-13)
+    assert L % P == 1  # the last page holds one token
+
+
+def test_bound_scores_hand_worked():
+    """Worked by hand, one head: q = (1, -1); page keys (0, 1), (2, -1) ->
+    lo (0, -1), hi (2, 1); bound max(0, 2) + max(1, -1) = 3, attained by the
+    key (2, -1). Keys (1, 0), (0, 1) with q = (1, 1): box corner (1, 1)
+    gives 2 though no key exceeds 1 (the bound is loose there)."""
+    k = np.zeros((2, 1, 2, 2))
+    k[0, 0, 0], k[0, 0, 1] = (0, 1), (2, -1)
+    k[1, 0, 0], k[1, 0, 1] = (1, 0), (0, 1)
+    lo, hi = O.page_bounds(k, 4, 2)
+    np.testing.assert_array_equal(lo[0, 0], [0, -1])
+    np.testing.assert_array_equal(hi[0, 0], [2, 1])
+    assert O.bound_scores(np.array([[1.0, -1.0]]), lo[:1], hi[:1], 1, 1.0)[0, 0] == 3.0
+    assert O.bound_scores(np.array([[1.0, 1.0]]), lo[1:], hi[1:], 1, 1.0)[0, 0] == 2.0
+
+
+def test_decode_sequence_bounds_indexer():
+    """indexer="bounds" ranks pages by the bound: a page whose keys straddle
+    the query direction beats one whose mean is higher but whose keys are
+    all alike. P=2, L=6, one head, q = (1, 0), k=1, no forced pages."""
+    k = np.zeros((3, 1, 2, 2))
+    k[0, 0, 0], k[0, 0, 1] = (1, 0), (1, 0)     # mean 1, max 1
+    k[1, 0, 0], k[1, 0, 1] = (3, 0), (-2.5, 0)  # mean 0.25, max 3
+    k[2, 0, 0], k[2, 0, 1] = (0, 0), (0, 0)
+    v = np.ones((3, 1, 2, 2))
+    seq = {"q": np.array([[1.0, 0.0]]), "k": k, "v": v, "seq_len": 6,
+           "rand_u32": np.zeros(1, np.uint32)}
+    kw = dict(page_size=2, num_kv_heads=1, k=1, n_sink=0, n_local=0, score_scale=1.0,
+              sm_scale=1.0)
+    cent = O.decode_sequence(seq, **kw)
+    bnd = O.decode_sequence(seq, indexer="bounds", **kw)
+    assert list(cent["sel"][0]) == [0]
+    assert list(bnd["sel"][0]) == [1]
+    np.testing.assert_allclose(bnd["scores"][0], [1, 3, 0])
