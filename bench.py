@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_bf16", choices=sorted(DESCR))
     ap.add_argument("--mode", default="exact", choices=["exact", "approx"])
+    ap.add_argument("--indexer", default="centroid", choices=["centroid", "bounds"],
+                    help="bounds: the Quest-style page-bounds indexer (GQA workloads)")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 1 GB touched")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -66,14 +68,15 @@ def log(msg):
 
 
 def step_bytes(w, step):
-    """Algorithmic bytes of one step: every in-use page's centroid row once,
-    plus the valid tokens of every selected page (K and V rows)."""
+    """Algorithmic bytes of one step: every in-use page's centroid row (or,
+    for the bounds indexer, its min and max rows in the KV dtype) once, plus
+    the valid tokens of every selected page (K and V rows)."""
     s = w.spec
     sel = step.sel.cpu().numpy()
     cnt = step.sel_count.cpu().numpy()
     P = s.page_size
     kv_elt = 4 if s.kv_dtype == "f32" else 2
-    cent_elt = 2 if s.mla else 4
+    cent_elt = 2 * kv_elt if step.indexer == "bounds" else (2 if s.mla else 4)
     n_pages = np.array([w.n_pages(b) for b in range(s.batch)])
     cent_bytes = int(n_pages.sum()) * s.num_kv_heads * s.head_dim_k * cent_elt
     row = (s.head_dim_k if s.mla else s.head_dim_k + s.head_dim_v) * kv_elt
@@ -115,7 +118,8 @@ def cpu_baseline(w, step, seconds):
             O.decode_sequence(seqs[b], page_size=s.page_size, num_kv_heads=s.num_kv_heads,
                               k=step.k, n_sink=step.n_sink, n_local=step.n_local,
                               score_scale=step.score_scale, sm_scale=step.sm_scale, mla=s.mla,
-                              head_dim_v=s.head_dim_v, approx=step.mode == 1)
+                              head_dim_v=s.head_dim_v, approx=step.mode == 1,
+                              indexer=step.indexer)
             t_total += time.perf_counter() - t0
             done += 1
             if len(seqs) > 8:
@@ -126,7 +130,8 @@ def cpu_baseline(w, step, seconds):
     distinct = min(done, s.batch)
     return {"value": done / t_total, "unit": "seqs/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} sequence-steps over {distinct} distinct sequences of the same "
-                      f"workload (whole step each: centroids, scores, selection, attention), "
+                      f"workload (whole step each: {'page bounds' if step.indexer == 'bounds' else 'centroids'}, "
+                      f"scores, selection, attention), "
                       f"numpy fp64, one thread, {t_total:.1f} s"}
 
 
@@ -203,6 +208,37 @@ def rope_unaware_recall(w, step):
     alt.index(refresh=False)
     torch.cuda.synchronize()
     return overlap(w, step, alt.sel, alt.sel_count, step.sel, step.sel_count)
+
+
+def attention_mass(w, step):
+    """Mean and minimum over (sequence, query head) of the share of the head's
+    full softmax weight (over every valid token) that falls on the pages
+    selected for its KV head: how much of dense attention the selection keeps.
+    A quality report, computed with plain fp32 torch ops on the GPU."""
+    import torch
+    s = w.spec
+    P, Hkv, D = s.page_size, s.num_kv_heads, s.head_dim_k
+    G = s.num_q_heads // Hkv
+    sel, cnt = step.sel.cpu().numpy(), step.sel_count.cpu().numpy()
+    masses = []
+    for b in range(s.batch):
+        L, n = int(w.seq_lens[b]), w.n_pages(b)
+        if L == 0:
+            continue
+        lo = int(w.indptr[b])
+        ids = torch.from_numpy(w.page_ids[lo:lo + n].astype(np.int64)).to(w.device)
+        k = w.k_pool.index_select(0, ids).float()[..., :D]          # [n][Hkv][P][D]
+        k = k.permute(1, 0, 2, 3).reshape(Hkv, n * P, D)            # [Hkv][nP][D]
+        kt = k.transpose(1, 2).contiguous()
+        q = w.q[b].float()[:, :D].reshape(Hkv, G, D).contiguous()
+        z = torch.matmul(q, kt) * step.sm_scale                       # [Hkv][G][nP]
+        z[..., L:] = float("-inf")
+        pm = torch.softmax(z, dim=-1).reshape(Hkv, G, n, P).sum(-1)  # [Hkv][G][n]
+        for g in range(Hkv):
+            chosen = torch.from_numpy(sel[b, g, :cnt[b, g]].astype(np.int64)).to(w.device)
+            masses.append(pm[g].index_select(1, chosen).sum(-1).cpu())
+    m = torch.cat(masses)
+    return {"mean": float(m.mean()), "min": float(m.min()), "heads": int(m.numel())}
 
 
 def copy_calibration():
@@ -316,10 +352,14 @@ def main():
     torch.cuda.set_device(0)
     mode = V.VX_TOPK_APPROX if a.mode == "approx" else V.VX_TOPK_EXACT
     sp = W.spec(a.workload)
+    bounds = a.indexer == "bounds"
+    if bounds and sp.mla:
+        print("the bounds indexer is implemented for GQA workloads only", file=sys.stderr)
+        sys.exit(2)
     log(f"workload {a.workload}: generating on cuda:0")
     w0 = W.make(sp, "cuda", seed=0)
-    base = DecodeStep(w0, mode=mode)
-    base.rebuild_centroids()
+    base = DecodeStep(w0, mode=mode, indexer=a.indexer)
+    base.rebuild()
     base.run()
     torch.cuda.synchronize()
     cent_b, kv_b, tokens = step_bytes(w0, base)
@@ -332,6 +372,21 @@ def main():
     if rope:
         log(f"rope-unaware MLA selection vs rope-aware, recall@k: mean {rope['mean']:.4f}, "
             f"min {rope['min']:.4f}")
+    quality = None
+    if bounds:
+        cent = DecodeStep(w0, mode=mode)
+        cent.rebuild()
+        cent.run()
+        torch.cuda.synchronize()
+        quality = {"attention_mass_bounds": attention_mass(w0, base),
+                   "attention_mass_centroid": attention_mass(w0, cent),
+                   "overlap_with_centroid": overlap(w0, base, base.sel, base.sel_count,
+                                                    cent.sel, cent.sel_count)}
+        log("selected share of dense softmax weight: bounds "
+            f"{quality['attention_mass_bounds']['mean']:.4f}, centroid "
+            f"{quality['attention_mass_centroid']['mean']:.4f}; selection overlap "
+            f"{quality['overlap_with_centroid']['mean']:.4f}")
+        del cent
     total_b = cent_b + kv_b
     R = a.replicas or max(1, min(16, math.ceil(1.0e9 / total_b)))
     log(f"step touches {total_b / 1e6:.1f} MB (centroids {cent_b / 1e6:.1f}, selected KV "
@@ -339,8 +394,8 @@ def main():
     ws, steps = [w0], [base]
     for _ in range(R - 1):
         w = w0.replicate()
-        st = DecodeStep(w, mode=mode)
-        st.rebuild_centroids()
+        st = DecodeStep(w, mode=mode, indexer=a.indexer)
+        st.rebuild()
         ws.append(w)
         steps.append(st)
     torch.cuda.synchronize()
@@ -391,14 +446,24 @@ def main():
     log(f"{a.steps} steps: {ms_step * 1e3:.2f} us/step (host wall {wall * 1e3 / a.steps * 1e3:.2f} us)")
 
     # per-stage durations (each stage alone, graph replays of all replicas)
-    stages = {
-        "decode_step": lambda st: st.step(),
-        "indexer": lambda st: st.index(),
-        "cache_refresh": lambda st: st.refresh_centroids(),
-        "page_scores": lambda st: st.score(),
-        "topk": lambda st: st.select(),
-        "attention_merge": lambda st: st.attend(),
-    }
+    if bounds:
+        stages = {
+            "indexer": lambda st: (st.bound_score(refresh=True), st.select()),
+            "cache_refresh": lambda st: st.refresh_bounds(),
+            "page_scores": lambda st: st.bound_score(),
+            "bound_scores_refresh": lambda st: st.bound_score(refresh=True),
+            "topk": lambda st: st.select(),
+            "attention_merge": lambda st: st.attend(),
+        }
+    else:
+        stages = {
+            "decode_step": lambda st: st.step(),
+            "indexer": lambda st: st.index(),
+            "cache_refresh": lambda st: st.refresh_centroids(),
+            "page_scores": lambda st: st.score(),
+            "topk": lambda st: st.select(),
+            "attention_merge": lambda st: st.attend(),
+        }
     stage_us = {}
     for name, fn in stages.items():
         g = capture(fn)
@@ -423,10 +488,12 @@ def main():
     step_gbps = total_b / t_step / 1e9
     ref_b = refresh_bytes(w0)
     stage_bytes = {"decode_step": cent_b + ref_b + kv_b, "indexer": cent_b + ref_b,
-                   "page_scores": cent_b, "attention_merge": kv_b}
+                   "page_scores": cent_b, "bound_scores_refresh": cent_b + ref_b,
+                   "attention_merge": kv_b}
+    stage_bytes = {k: v for k, v in stage_bytes.items() if k in stage_us}
     # One kernel per step when the plan fuses it; otherwise the indexer and the
     # attention (+ merge) run in turn and the slower is dominant.
-    if plan["fused_step"]:
+    if plan["fused_step"] and not bounds:
         dom = "decode_step"
     else:
         dom = max(("indexer", "attention_merge"), key=lambda k: stage_us[k])
@@ -445,8 +512,9 @@ def main():
         "dtype": "f32" if s.kv_dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{a.workload}: {DESCR[a.workload]}", "topk_mode": a.mode,
-                   "replicas": R, "hip_graph": True, "num_splits": plan["num_splits"],
-                   "fused_step": bool(plan["fused_step"])},
+                   "indexer": a.indexer, "replicas": R, "hip_graph": True,
+                   "num_splits": plan["num_splits"],
+                   "fused_step": bool(plan["fused_step"]) and not bounds},
         "kv_tokens_per_s": kv_tokens_per_s,
         "step_bytes": total_b,
         "step_hbm_GBps": step_gbps,
@@ -456,13 +524,16 @@ def main():
         "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS,
-                     "traffic": measured_traffic(a.workload, dom), "kernel": dom,
+                     "traffic": None if bounds else measured_traffic(a.workload, dom),
+                     "kernel": dom,
                      "bytes_per_launch": stage_bytes[dom]},
     }
     if recall:
         result["approx_recall_at_k"] = recall
     if rope:
         result["mla_rope_unaware_recall_at_k"] = rope
+    if quality:
+        result["selection_quality"] = quality
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w0, base, a.cpu_seconds)

@@ -14,6 +14,10 @@
  * batch size, a pointer array and a page-index structure): vx_pages below.
  * Section "System design > 3. Execution backend" gives the workload planner
  * (vx_plan_decode) and the radix top-k with its approximate mode.
+ * The Quest-style indexer the paper note measures against ("Paper context",
+ * "Key results > User-side latency") is an alternative cache stage and
+ * scorer: page bounds -> vx_bounds_update, bound scores -> vx_bound_scores;
+ * its selection and attention are vx_topk_pages and vx_sparse_decode.
  *
  * Conventions shared by every entry point
  *   - Every buffer argument is DEVICE memory owned by the caller, unless the
@@ -41,6 +45,7 @@
  *   v_pool     [num_pool_pages][Hkv][P][Dv]    kv_dtype  (MLA: unused, V = K[..., :Dv])
  *   centroids  [num_pool_pages][Hkv][Dk]       fp32      (indexed by physical page)
  *   cent_bf16  [num_pool_pages][Hkv][Dk]       bf16      (RNE of the fp32 centroid)
+ *   bounds     [num_pool_pages][Hkv][Dk/4][2][4] kv_dtype (per 4 dims: 4 key minima, 4 maxima)
  *   scores     [Hkv][total_pages]              fp32      (entry j of page table)
  *   sel        [B][Hkv][sel_stride]            int32     logical page ids, ascending, -1 padded
  *   sel_count  [B][Hkv]                        int32
@@ -182,6 +187,43 @@ vx_status vx_topk_pages(const vx_pages* pages, int32_t num_kv_heads,
                         int32_t n_local, int32_t mode, const uint32_t* rand_u32,
                         int32_t* sel, int32_t sel_stride, int32_t* sel_count,
                         hipStream_t stream);
+
+/* Quest-style cache stage (GQA only; MLA returns VX_ERR_UNSUPPORTED). The
+ * mechanism is Quest's (Tang et al., "Quest: Query-Aware Sparsity for
+ * Efficient Long-Context LLM Inference", ICML 2024), the other baseline of
+ * the Vortex paper note ("Paper context", "Key results > User-side
+ * latency"): per page and KV head, the elementwise minimum and maximum of
+ * the keys of its valid tokens.
+ * bounds[pid][g][d/4][0][d%4] = min over valid t of K[pid][g][t][d],
+ * bounds[pid][g][d/4][1][d%4] = max over the same tokens, in kv_dtype (exact:
+ * the extremes of bf16 keys are bf16 values; the interleaving gives a 16-byte
+ * load both bounds of 4 dims). Pages past a sequence's last token get zeros.
+ * first_token == NULL: rebuild every page-table entry. Otherwise ([B]
+ * device) refresh each sequence's pages holding tokens first_token[b] ..
+ * seq_lens[b]-1, a negative value counting from the end (-1: the newest
+ * token's page). Each refreshed page is recomputed from its keys, so the
+ * result equals a rebuild bit for bit. k_pool is only read: the caller
+ * writes appended keys into it first. */
+vx_status vx_bounds_update(const vx_pages* pages, const vx_geom* geom,
+                           const void* k_pool, const int32_t* first_token,
+                           void* bounds, hipStream_t stream);
+
+/* Quest-style scores (GQA only): with Q[g] = sum over the query heads h of
+ * group g of q[b][h] (fp32, head order) times score_scale,
+ *   scores[g][j] = sum_d max(Q[g][d] * lo[d], Q[g][d] * hi[d]),
+ * lo / hi the bounds rows of entry j's page: an upper bound of
+ * score_scale * sum_h q[b][h] . K_t over every valid token t of the page
+ * (the least one that depends on the bounds alone).
+ * refresh_newest = 1 first recomputes, from k_pool, the bounds of the page
+ * holding each sequence's newest token (exactly vx_bounds_update with
+ * first_token[b] = -1) and scores that page from them; no physical page that
+ * is some sequence's newest page may then appear in another sequence's page
+ * table. j runs over the entries in use; other entries of `scores` are left
+ * untouched. The scores feed vx_topk_pages. */
+vx_status vx_bound_scores(const vx_pages* pages, const vx_geom* geom,
+                          const void* q, const void* k_pool, void* bounds,
+                          int32_t refresh_newest, float score_scale,
+                          float* scores, hipStream_t stream);
 
 /* Indexer, fused (Vortex paper note, "System design > 3. Execution backend":
  * sequence-local operators are fused). One call runs

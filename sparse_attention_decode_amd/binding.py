@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
     "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-    "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
+    "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
+    "vx_bound_scores", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
 
@@ -25,6 +26,7 @@ VX_OK, VX_ERR_INVALID_ARG, VX_ERR_UNSUPPORTED, VX_ERR_WORKSPACE, VX_ERR_HIP = ra
 VX_F32, VX_BF16 = 0, 1
 VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
 ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
+                "vx_bounds_update", "vx_bound_scores",
                 "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
@@ -89,8 +91,12 @@ def load() -> ctypes.CDLL:
                                    c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                    c_int32, c_void_p, POINTER(c_size_t), c_void_p]
     lib.vx_plan_decode.argtypes = [P, G, c_int32, c_int32, c_int32, POINTER(VxPlan)]
+    lib.vx_bounds_update.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.vx_bound_scores.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                    c_void_p, c_void_p]
     for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-                 "vx_sparse_decode", "vx_decode_step", "vx_plan_decode"):
+                 "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
+                 "vx_bound_scores"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -156,6 +162,19 @@ def vx_page_scores(pages: VxPages, geom: VxGeom, q, centroids, score_scale: floa
     _check(load().vx_page_scores(ctypes.byref(pages), ctypes.byref(geom), _ptr(q),
                                  _ptr(centroids), float(score_scale), _ptr(scores),
                                  _stream(stream)))
+
+
+def vx_bounds_update(pages: VxPages, geom: VxGeom, k_pool, first_token, bounds,
+                     stream=None) -> None:
+    _check(load().vx_bounds_update(ctypes.byref(pages), ctypes.byref(geom), _ptr(k_pool),
+                                   _ptr(first_token), _ptr(bounds), _stream(stream)))
+
+
+def vx_bound_scores(pages: VxPages, geom: VxGeom, q, k_pool, bounds, refresh_newest: bool,
+                    score_scale: float, scores, stream=None) -> None:
+    _check(load().vx_bound_scores(ctypes.byref(pages), ctypes.byref(geom), _ptr(q), _ptr(k_pool),
+                                  _ptr(bounds), int(bool(refresh_newest)), float(score_scale),
+                                  _ptr(scores), _stream(stream)))
 
 
 def vx_topk_pages(pages: VxPages, num_kv_heads: int, scores, k: int, n_sink: int, n_local: int,

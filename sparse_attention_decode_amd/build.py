@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvx.so")
 SOURCES = ["vx_capi.hip", "centroid.hip", "scores.hip", "indexer.hip", "topk.hip", "attention.hip",
-           "mla.hip", "decode.hip"]
+           "mla.hip", "decode.hip", "bounds.hip"]
 ARCH = "gfx950"
 
 

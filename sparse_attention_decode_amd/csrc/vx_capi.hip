@@ -243,7 +243,7 @@ void split_buffers(const vx_pages* p, const vx_geom* g, int S, void* ws, float**
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 2; }
+int32_t vx_abi_version(void) { return 3; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {
@@ -314,6 +314,42 @@ vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom, const void*
     e = vx::launch_scores_gqa(m, *geom, q, nullptr, const_cast<float*>((const float*)centroids),
                               nullptr, 0, score_scale, scores, stream);
   return hip_status(e, "score kernel launch");
+}
+
+vx_status vx_bounds_update(const vx_pages* pages, const vx_geom* geom, const void* k_pool,
+                           const int32_t* first_token, void* bounds, hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(!geom->mla, VX_ERR_UNSUPPORTED, "page bounds are implemented for GQA only");
+  VX_CHECK(pages->total_pages == 0 || (k_pool && bounds), VX_ERR_INVALID_ARG,
+           "k_pool or bounds is NULL");
+  if (pages->batch == 0) return VX_OK;
+  return hip_status(vx::launch_bounds_update(meta_of(pages), *geom, k_pool, first_token, bounds,
+                                             stream),
+                    "bounds kernel launch");
+}
+
+vx_status vx_bound_scores(const vx_pages* pages, const vx_geom* geom, const void* q,
+                          const void* k_pool, void* bounds, int32_t refresh_newest,
+                          float score_scale, float* scores, hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(!geom->mla, VX_ERR_UNSUPPORTED, "page bounds are implemented for GQA only");
+  VX_CHECK(refresh_newest == 0 || refresh_newest == 1, VX_ERR_INVALID_ARG,
+           "refresh_newest must be 0 or 1");
+  VX_CHECK(std::isfinite(score_scale), VX_ERR_INVALID_ARG, "score_scale not finite");
+  VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
+  VX_CHECK(pages->total_pages == 0 || (bounds && scores), VX_ERR_INVALID_ARG,
+           "bounds or scores is NULL");
+  VX_CHECK(!refresh_newest || pages->total_pages == 0 || k_pool, VX_ERR_INVALID_ARG,
+           "refresh_newest needs k_pool");
+  if (pages->total_pages == 0) return VX_OK;
+  return hip_status(vx::launch_bound_scores(meta_of(pages), *geom, q, k_pool, bounds,
+                                            refresh_newest, score_scale, scores,
+                                            pages->max_pages, stream),
+                    "bound score kernel launch");
 }
 
 vx_status vx_topk_pages(const vx_pages* pages, int32_t num_kv_heads, const float* scores,

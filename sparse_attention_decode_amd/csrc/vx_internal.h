@@ -209,6 +209,15 @@ hipError_t launch_decode_step_mla(const Meta& m, const vx_geom& g, const void* q
                                   int sel_stride, int32_t* sel_count, float sm_scale,
                                   int num_splits, float* out, float* lse, float* part_o,
                                   float* part_ml, int max_pages, hipStream_t s);
+// Quest-style page bounds (GQA): rebuild every entry (first_token NULL) or
+// refresh each sequence's pages from first_token[b]; bounds in the KV dtype.
+hipError_t launch_bounds_update(const Meta& m, const vx_geom& g, const void* k_pool,
+                                const int32_t* first_token, void* bounds, hipStream_t s);
+// Upper-bound page scores from the bounds; refresh != 0 first recomputes each
+// sequence's newest page's bounds from k_pool.
+hipError_t launch_bound_scores(const Meta& m, const vx_geom& g, const void* q, const void* k_pool,
+                               void* bounds, int refresh, float scale, float* scores,
+                               int max_pages, hipStream_t s);
 hipError_t launch_merge(int batch, int hq, int dv, int num_splits, const float* part_o,
                         const float* part_ml, float* out, float* lse, hipStream_t s);
 

@@ -4,6 +4,10 @@ Owns the device buffers of a workload (centroid cache, scores, selection,
 outputs, workspace) and issues the library's calls in the step's order:
 cache stage (refresh of the newest token's page), scoring, selection,
 attention. Python only marshals arguments; every stage is a gfx950 kernel.
+
+indexer="bounds" swaps the centroid cache stage and scorer for the
+Quest-style page bounds (vx_bounds_update / vx_bound_scores, GQA only);
+selection and attention are unchanged.
 """
 
 from __future__ import annotations
@@ -22,12 +26,15 @@ class DecodeStep:
     def __init__(self, w: Workload, mode: int = V.VX_TOPK_EXACT, num_splits: int = 0,
                  k: Optional[int] = None, n_sink: Optional[int] = None,
                  n_local: Optional[int] = None, with_lse: bool = True, fused: bool = True,
-                 score_dim: int = 0):
+                 score_dim: int = 0, indexer: str = "centroid"):
+        if indexer not in ("centroid", "bounds"):
+            raise ValueError(f"indexer {indexer!r}")
         s = w.spec
         dev = w.device
         self.w = w
         self.mode = mode
         self.fused = fused
+        self.indexer = indexer
         self.num_splits = num_splits
         self.k = s.topk if k is None else k
         self.n_sink = s.n_sink if n_sink is None else n_sink
@@ -44,6 +51,10 @@ class DecodeStep:
                                      device=dev)
         self.cent_bf16 = (torch.zeros((w.pool_pages, H, s.head_dim_k), dtype=torch.bfloat16,
                                       device=dev) if s.mla else None)
+        # [pool][Hkv][Dk/4][2][4]: per 4 dims, their 4 key minima then 4 maxima
+        self.bounds = (torch.zeros((w.pool_pages, H, s.head_dim_k // 4, 2, 4),
+                                   dtype=w.k_pool.dtype, device=dev)
+                       if indexer == "bounds" else None)
         self.scores = torch.zeros((H, max(1, w.nnz)), dtype=torch.float32, device=dev)
         self.sel = torch.full((s.batch, H, self.k_out), -1, dtype=torch.int32, device=dev)
         self.sel_count = torch.zeros((s.batch, H), dtype=torch.int32, device=dev)
@@ -69,6 +80,24 @@ class DecodeStep:
         ft = self.newest if first_token is None else first_token
         V.vx_centroid_update(self.pages, self.geom, w.k_pool, w.v_pool if v_new is not None else None,
                              ft, k_new, v_new, self.centroids, self.cent_bf16, stream)
+
+    def rebuild_bounds(self, stream=None) -> None:
+        V.vx_bounds_update(self.pages, self.geom, self.w.k_pool, None, self.bounds, stream)
+
+    def refresh_bounds(self, first_token=None, stream=None) -> None:
+        ft = self.newest if first_token is None else first_token
+        V.vx_bounds_update(self.pages, self.geom, self.w.k_pool, ft, self.bounds, stream)
+
+    def bound_score(self, refresh: bool = False, stream=None) -> None:
+        V.vx_bound_scores(self.pages, self.geom, self.w.q, self.w.k_pool, self.bounds, refresh,
+                          self.score_scale, self.scores, stream)
+
+    def rebuild(self, stream=None) -> None:
+        """Rebuild the indexer's cache from the whole pool."""
+        if self.indexer == "bounds":
+            self.rebuild_bounds(stream)
+        else:
+            self.rebuild_centroids(stream)
 
     def score(self, stream=None) -> None:
         cent = self.cent_bf16 if self.w.spec.mla else self.centroids
@@ -111,7 +140,11 @@ class DecodeStep:
 
     def run(self, stream=None) -> None:
         """The whole step: cache refresh, scoring, selection, attention."""
-        if self.fused:
+        if self.indexer == "bounds":
+            self.bound_score(refresh=True, stream=stream)
+            self.select(stream=stream)
+            self.attend(stream=stream)
+        elif self.fused:
             self.step(stream=stream)
         else:
             self.refresh_centroids(stream=stream)

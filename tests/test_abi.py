@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 2
+    assert lib.vx_abi_version() == 3
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -234,3 +234,36 @@ def test_plan_reports_the_whole_step_kernel():
     small = pages(batch=2, nnz=40, pool=40, maxp=20)
     assert V.vx_plan_decode(small, g, 18, 0, 256)["fused_step"] == 0  # planner splits
     assert V.vx_plan_decode(small, g, 18, 1, 256)["fused_step"] == 1
+
+
+def test_bounds_argument_checks():
+    """The Quest-style cache stage and scorer: GQA only, pointers and flags
+    checked on the host before any launch; an empty batch is a no-op."""
+    p, g = pages(), geom()
+    mla = geom(hkv=1, mla=1, dk=576, dv=512, hq=32)
+    assert status_of(V.vx_bounds_update, p, mla, BAD, None, BAD, stream=0) == V.VX_ERR_UNSUPPORTED
+    assert status_of(V.vx_bound_scores, p, mla, BAD, BAD, BAD, True, 1.0, BAD,
+                     stream=0) == V.VX_ERR_UNSUPPORTED
+    assert status_of(V.vx_bounds_update, p, g, None, None, BAD, stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_bounds_update, p, g, BAD, None, None, stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_bounds_update, pages(page_size=32), g, BAD, None, BAD,
+                     stream=0) == V.VX_ERR_UNSUPPORTED
+    assert status_of(V.vx_bound_scores, p, geom(dk=96, dv=96), BAD, BAD, BAD, False, 1.0, BAD,
+                     stream=0) == V.VX_ERR_UNSUPPORTED
+    # refresh needs the key pool; scores and bounds are required; the scale finite
+    assert status_of(V.vx_bound_scores, p, g, BAD, None, BAD, True, 1.0, BAD,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_bound_scores, p, g, BAD, None, None, False, 1.0, BAD,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_bound_scores, p, g, BAD, None, BAD, False, 1.0, None,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_bound_scores, p, g, None, None, BAD, False, 1.0, BAD,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_bound_scores, p, g, BAD, None, BAD, False, float("inf"), BAD,
+                     stream=0) == V.VX_ERR_INVALID_ARG
+    lib = V.load()
+    st = lib.vx_bound_scores(ctypes.byref(p), ctypes.byref(g), BAD, BAD, BAD, 2, 1.0, BAD, None)
+    assert st == V.VX_ERR_INVALID_ARG
+    empty = V.make_pages(0, 16, 0, 0, 0, None, None, None)
+    V.vx_bounds_update(empty, g, None, None, None, stream=0)
+    V.vx_bound_scores(empty, g, None, None, None, True, 1.0, None, stream=0)

@@ -1,0 +1,161 @@
+"""The Quest-style indexer (page bounds as the cache stage, their upper-bound
+page scores) against the oracle: bounds exact, scores within the stated
+tolerance, the whole step (bound scores with the newest-page refresh, top-k,
+attention) matching the oracle's step with indexer="bounds"; and the refresh
+paths equal a rebuild bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import vx_testlib as T
+from sparse_attention_decode_amd import workloads as W
+from sparse_attention_decode_amd.step import DecodeStep
+from test_gpu_edges import on_gpu
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+GQA_SMALL = ["tiny_fp32", "gqa_small", "longgen_small", "large_small"]
+
+
+def used(w):
+    return torch.from_numpy(w.page_ids.astype(np.int64)).to(w.device)
+
+
+def check_against_oracle(w, step, sample, selection=True):
+    """Bounds, scores, selection and attention of the sampled sequences;
+    returns the number of (sequence, KV head) selections that differ from the
+    oracle's within its near-tie allowance (their attention is not compared)."""
+    out = step.out.cpu().double().numpy()
+    lse = step.lse.cpu().double().numpy()
+    G = w.spec.num_q_heads // w.spec.num_kv_heads
+    differing = 0
+    for b in sample:
+        r = T.oracle_seq(w, step, b)
+        T.check_bounds(w, step, b, r)
+        T.check_bound_scores(w, step, b, r)
+        if not selection:
+            continue
+        for g, ok in enumerate(T.check_selection(w, step, b, r)):
+            if ok:
+                T.check_attention(w, out[b], lse[b], r["out"], r["lse"],
+                                  heads=range(g * G, (g + 1) * G), tag=f"b={b} g={g}")
+            else:
+                differing += 1
+    return differing
+
+
+@pytest.mark.parametrize("name", GQA_SMALL)
+def test_rebuild_and_scores_match_oracle(name):
+    w = on_gpu(W.make(SMALL[name], "cpu", seed=31))
+    step = DecodeStep(w, indexer="bounds")
+    step.bounds.fill_(7)
+    step.rebuild_bounds()
+    step.bound_score()
+    T.sync()
+    check_against_oracle(w, step, range(w.batch), selection=False)
+    # capacity entries past a sequence's pages in use hold zeros
+    for b in range(w.batch):
+        lo, hi = int(w.indptr[b]), int(w.indptr[b + 1])
+        ids = w.page_ids[lo + w.n_pages(b):hi]
+        if len(ids):
+            t = step.bounds[torch.from_numpy(ids.astype(np.int64)).to(w.device)]
+            assert (t == 0).all()
+
+
+@pytest.mark.parametrize("name", GQA_SMALL)
+def test_step_matches_oracle(name):
+    """run(): bound scores with the newest-page refresh, top-k, attention,
+    after appends, against the oracle for every sequence."""
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=32))
+    step = DecodeStep(w, indexer="bounds")
+    step.rebuild_bounds()
+    for _ in range(5):
+        w.append_token()
+        step.run()
+    T.sync()
+    differing = check_against_oracle(w, step, range(w.batch))
+    assert differing <= max(1, w.batch * w.spec.num_kv_heads // 20)
+
+
+@pytest.mark.parametrize("name", GQA_SMALL)
+def test_refresh_paths_equal_rebuild(name):
+    """After appends (crossing page boundaries): the scorer's fused refresh,
+    vx_bounds_update with first_token -1, and a full rebuild give the same
+    bounds and scores bit for bit; so do other first_token values."""
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=33))
+    fused = DecodeStep(w, indexer="bounds")
+    upd = DecodeStep(w, indexer="bounds")
+    reb = DecodeStep(w, indexer="bounds")
+    fused.rebuild_bounds()
+    upd.rebuild_bounds()
+    ids = used(w)
+    B = w.batch
+    for i in range(20):
+        w.append_token()
+        fused.bound_score(refresh=True)
+        if i % 3 == 0:
+            ft = torch.tensor([[0, 5, -1, -17, 10 ** 6][b % 5] for b in range(B)],
+                              dtype=torch.int32, device=w.device)
+            upd.refresh_bounds(first_token=ft)
+        else:
+            upd.refresh_bounds()
+        upd.bound_score()
+        reb.rebuild_bounds()
+        reb.bound_score()
+        T.sync()
+        assert torch.equal(fused.bounds[ids], reb.bounds[ids])
+        assert torch.equal(upd.bounds[ids], reb.bounds[ids])
+        valid = torch.zeros(w.nnz, dtype=torch.bool)
+        for b in range(B):
+            lo = int(w.indptr[b])
+            valid[lo:lo + w.n_pages(b)] = True
+        valid = valid.to(w.device)
+        assert torch.equal(fused.scores[:, valid], reb.scores[:, valid])
+        assert torch.equal(upd.scores[:, valid], reb.scores[:, valid])
+
+
+@pytest.mark.parametrize("k,n_sink,n_local", [(0, 1, 1), (3, 0, 0), (200, 1, 1), (5, 2, 0)])
+def test_budgets(k, n_sink, n_local):
+    w = on_gpu(W.make(SMALL["gqa_small"].replace(headroom_tokens=20), "cpu", seed=34))
+    step = DecodeStep(w, indexer="bounds", k=k, n_sink=n_sink, n_local=n_local)
+    step.rebuild_bounds()
+    w.append_token()
+    step.run()
+    T.sync()
+    assert check_against_oracle(w, step, range(w.batch)) <= max(1, w.batch // 20)
+
+
+def test_idle_and_single_token_sequences():
+    """seq_lens 0 (empty selection, zero output), one token, a page and a
+    token: against the oracle."""
+    lens = (0, 1, 16, 17, 0, 333)
+    sp = W.spec("gqa_bf16", batch=len(lens), lengths=("list", lens), headroom_tokens=16,
+                pool=("factor", 1.5))
+    w = on_gpu(W.make(sp, "cpu", seed=35))
+    step = DecodeStep(w, indexer="bounds")
+    step.out.fill_(1.0)
+    step.rebuild_bounds()
+    step.run()
+    T.sync()
+    for b, L in enumerate(w.seq_lens):
+        if L == 0:
+            assert (step.sel_count[b] == 0).all()
+            assert (step.out[b] == 0).all()
+            assert torch.isneginf(step.lse[b]).all()
+    assert check_against_oracle(w, step, [b for b, L in enumerate(w.seq_lens) if L]) == 0
+
+
+@pytest.mark.parametrize("name,sample", [("gqa_bf16", (0, 7, 31)), ("largebatch_bf16", (3, 200))])
+def test_full_size_sampled(name, sample):
+    """The shapes the step is timed at: sampled sequences against the oracle."""
+    w = W.make(W.spec(name, headroom_tokens=64), "cuda", seed=36)
+    step = DecodeStep(w, indexer="bounds")
+    step.rebuild_bounds()
+    w.append_token()
+    step.run()
+    T.sync()
+    assert check_against_oracle(w, step, sample) <= 1
+    del w, step
+    torch.cuda.empty_cache()

@@ -6,6 +6,8 @@ Tolerances (written here once, used by every parity test):
   mean of the page's valid keys; relative to the magnitude of what is summed);
 * scores: |s_gpu - s_ref| <= 1e-5 * scale * sum_h sum_d |q_hd c_d| (relative to
   the condition of the dot product; a plain |ds|/|s| is ill-posed near 0);
+  bound scores likewise with max(|lo_d|, |hi_d|) in place of |c_d|;
+* page bounds: exact (the minimum and maximum of KV-dtype values);
 * selection: bit-exact, except that a page may differ where the oracle's
   score lies within 1e-3 relative of the k-th ranked candidate score tau:
   |s(p) - tau| <= 1e-3 * max(|tau|, 1e-3 * max |s|);
@@ -32,7 +34,8 @@ def oracle_seq(w: W.Workload, step: DecodeStep, b: int, approx: bool = False) ->
                           n_sink=step.n_sink, n_local=step.n_local,
                           score_scale=step.score_scale, sm_scale=step.sm_scale, mla=s.mla,
                           head_dim_v=s.head_dim_v, approx=approx,
-                          score_dim=step.score_dim or None)
+                          score_dim=step.score_dim or None,
+                          indexer=getattr(step, "indexer", "centroid"))
     r["seq"] = seq
     return r
 
@@ -55,6 +58,37 @@ def check_centroids(w, step, b, ref):
         bound[p] = np.abs(seq["k"][p, :, :nv, :]).mean(axis=1)
     err = np.abs(got - ref["centroids"])
     assert np.all(err <= 1e-5 * bound + 1e-30), f"centroid err {err.max()} (b={b})"
+    return got
+
+
+def check_bounds(w, step, b, ref):
+    """The GPU's bounds rows of sequence b's pages in use equal the oracle's
+    (values compared, so -0.0 and +0.0 are alike)."""
+    n = ref["lo"].shape[0]
+    lo = int(w.indptr[b])
+    ids = torch.from_numpy(w.page_ids[lo:lo + n].astype(np.int64)).to(w.device)
+    got = step.bounds.index_select(0, ids).double().cpu().numpy()  # [n][Hkv][Dk/4][2][4]
+    n_, H, U = got.shape[:3]
+    np.testing.assert_array_equal(got[:, :, :, 0, :].reshape(n_, H, 4 * U), ref["lo"],
+                                  err_msg=f"lo b={b}")
+    np.testing.assert_array_equal(got[:, :, :, 1, :].reshape(n_, H, 4 * U), ref["hi"],
+                                  err_msg=f"hi b={b}")
+
+
+def check_bound_scores(w, step, b, ref):
+    s = w.spec
+    n = ref["lo"].shape[0]
+    lo = int(w.indptr[b])
+    got = step.scores[:, lo:lo + n].double().cpu().numpy()
+    q = ref["seq"]["q"]
+    G = s.num_q_heads // s.num_kv_heads
+    mag = np.maximum(np.abs(ref["lo"]), np.abs(ref["hi"]))  # [n][Hkv][Dk]
+    bound = np.zeros((s.num_kv_heads, n))
+    for g in range(s.num_kv_heads):
+        qa = np.abs(q[g * G:(g + 1) * G]).sum(axis=0)
+        bound[g] = step.score_scale * (mag[:, g, :] @ qa)
+    err = np.abs(got - ref["scores"])
+    assert np.all(err <= 1e-5 * bound + 1e-30), f"bound score err {err.max()} (b={b})"
     return got
 
 
