@@ -110,7 +110,7 @@ def cpu_baseline(w, step, seconds):
     s = w.spec
     done, t_total, seqs = 0, 0.0, {}
     try:
-        while t_total < seconds and done < 64 * s.batch:
+        while t_total < seconds and done < 1024 * s.batch:
             b = done % s.batch
             if b not in seqs:
                 seqs[b] = w.host_sequence(b)  # host copy, outside the timed part
