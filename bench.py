@@ -448,6 +448,7 @@ def main():
     # per-stage durations (each stage alone, graph replays of all replicas)
     if bounds:
         stages = {
+            "decode_step": lambda st: st.bound_step(),
             "indexer": lambda st: (st.bound_score(refresh=True), st.select()),
             "cache_refresh": lambda st: st.refresh_bounds(),
             "page_scores": lambda st: st.bound_score(),
@@ -493,7 +494,7 @@ def main():
     stage_bytes = {k: v for k, v in stage_bytes.items() if k in stage_us}
     # One kernel per step when the plan fuses it; otherwise the indexer and the
     # attention (+ merge) run in turn and the slower is dominant.
-    if plan["fused_step"] and not bounds:
+    if plan["fused_step"]:
         dom = "decode_step"
     else:
         dom = max(("indexer", "attention_merge"), key=lambda k: stage_us[k])
@@ -514,7 +515,7 @@ def main():
         "config": {"workload": f"{a.workload}: {DESCR[a.workload]}", "topk_mode": a.mode,
                    "indexer": a.indexer, "replicas": R, "hip_graph": True,
                    "num_splits": plan["num_splits"],
-                   "fused_step": bool(plan["fused_step"]) and not bounds},
+                   "fused_step": bool(plan["fused_step"])},
         "kv_tokens_per_s": kv_tokens_per_s,
         "step_bytes": total_b,
         "step_hbm_GBps": step_gbps,
@@ -524,7 +525,7 @@ def main():
         "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS,
-                     "traffic": None if bounds else measured_traffic(a.workload, dom),
+                     "traffic": measured_traffic(a.workload + ("_bounds" if bounds else ""), dom),
                      "kernel": dom,
                      "bytes_per_launch": stage_bytes[dom]},
     }

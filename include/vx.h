@@ -17,7 +17,8 @@
  * The Quest-style indexer the paper note measures against ("Paper context",
  * "Key results > User-side latency") is an alternative cache stage and
  * scorer: page bounds -> vx_bounds_update, bound scores -> vx_bound_scores;
- * its selection and attention are vx_topk_pages and vx_sparse_decode.
+ * its selection and attention are vx_topk_pages and vx_sparse_decode, and
+ * vx_bound_decode_step runs the whole step (one kernel where it fits).
  *
  * Conventions shared by every entry point
  *   - Every buffer argument is DEVICE memory owned by the caller, unless the
@@ -296,6 +297,29 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom,
                          int32_t* sel_count, float* out, float* lse,
                          int32_t num_splits, void* workspace,
                          size_t* workspace_bytes, hipStream_t stream);
+
+/* The whole step with the Quest-style indexer (GQA only; the mechanism is
+ * Quest's, the other baseline of the Vortex paper note, "Paper context" and
+ * "Key results > User-side latency"). Writes the same bits as
+ * vx_bound_scores (with refresh_newest), vx_topk_pages over those scores and
+ * vx_sparse_decode over that selection, in that order. When the plan has one
+ * split per (sequence, KV head) and the geometry is bf16, Dk = 128, with
+ * sel_stride <= 256 and max_pages <= 4096, it is one kernel per step, the
+ * same block-per-(sequence, KV head) kernel as vx_decode_step's with the
+ * bounds scorer in place of the centroid scorer. workspace == NULL: writes
+ * the bytes needed to *workspace_bytes (those of vx_sparse_decode) and
+ * returns VX_OK. */
+vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom,
+                               const void* q, const void* k_pool,
+                               const void* v_pool, void* bounds,
+                               int32_t refresh_newest, float score_scale,
+                               float sm_scale, int32_t k, int32_t n_sink,
+                               int32_t n_local, int32_t mode,
+                               const uint32_t* rand_u32, float* scores,
+                               int32_t* sel, int32_t sel_stride,
+                               int32_t* sel_count, float* out, float* lse,
+                               int32_t num_splits, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream);
 
 /* Workload planner (Vortex paper note, "System design > 3. Execution
  * backend": plan by batch size, sequence length, layout and operator).

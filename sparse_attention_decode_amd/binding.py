@@ -18,7 +18,7 @@ __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
     "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
     "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
-    "vx_bound_scores", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
+    "vx_bound_scores", "vx_bound_decode_step", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
 
@@ -26,7 +26,7 @@ VX_OK, VX_ERR_INVALID_ARG, VX_ERR_UNSUPPORTED, VX_ERR_WORKSPACE, VX_ERR_HIP = ra
 VX_F32, VX_BF16 = 0, 1
 VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
 ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-                "vx_bounds_update", "vx_bound_scores",
+                "vx_bounds_update", "vx_bound_scores", "vx_bound_decode_step",
                 "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
@@ -94,9 +94,14 @@ def load() -> ctypes.CDLL:
     lib.vx_bounds_update.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.vx_bound_scores.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_int32, c_float,
                                     c_void_p, c_void_p]
+    lib.vx_bound_decode_step.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                         c_float, c_float, c_int32, c_int32, c_int32, c_int32,
+                                         c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                         c_void_p, c_void_p, c_int32, c_void_p,
+                                         POINTER(c_size_t), c_void_p]
     for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
                  "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
-                 "vx_bound_scores"):
+                 "vx_bound_scores", "vx_bound_decode_step"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -227,6 +232,25 @@ def vx_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, centroids, c
                                  n_sink, n_local, mode, _ptr(rand_u32), _ptr(scores), _ptr(sel),
                                  sel_stride, _ptr(sel_count), _ptr(out), _ptr(lse), num_splits,
                                  _ptr(workspace), ctypes.byref(nbytes), _stream(stream)))
+    return nbytes.value
+
+
+def vx_bound_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, bounds,
+                         refresh_newest: bool, score_scale: float, sm_scale: float, k: int,
+                         n_sink: int, n_local: int, mode: int, rand_u32, scores, sel,
+                         sel_stride: int, sel_count, out, lse, num_splits: int = 0,
+                         workspace=None, workspace_bytes: Optional[int] = None,
+                         stream=None) -> int:
+    """The whole step with the bounds indexer; with workspace=None only
+    returns the bytes needed."""
+    nbytes = _nbytes(workspace, workspace_bytes)
+    _check(load().vx_bound_decode_step(ctypes.byref(pages), ctypes.byref(geom), _ptr(q),
+                                       _ptr(k_pool), _ptr(v_pool), _ptr(bounds),
+                                       int(refresh_newest), float(score_scale), float(sm_scale),
+                                       k, n_sink, n_local, mode, _ptr(rand_u32), _ptr(scores),
+                                       _ptr(sel), sel_stride, _ptr(sel_count), _ptr(out),
+                                       _ptr(lse), num_splits, _ptr(workspace),
+                                       ctypes.byref(nbytes), _stream(stream)))
     return nbytes.value
 
 

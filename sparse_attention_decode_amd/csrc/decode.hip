@@ -8,14 +8,15 @@
 // feeds only that segment's attention, so a block that has just selected
 // can attend at once: the chosen ids and the physical page of every entry
 // are already in its LDS (no kernel boundary, no reload of the selection or
-// of the page table).
+// of the page table). BOUNDS: the Quest-style indexer (page key bounds) in
+// place of the centroids.
 #include "attn_mfma.h"
 #include "index_seg.h"
 
 namespace vx {
 namespace {
 
-template <int G, int P, int NW>
+template <int G, int P, int NW, bool BOUNDS>
 __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                                                              const uint16_t* __restrict__ vp,
                                                              float qscale, float* __restrict__ out,
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
 
   const int seg = blockIdx.x;
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
-  index_segment<uint16_t, uint16_t, 128, G, NW>(a, seg, dyn, pid_l, sel_l, &cnt_l);
+  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l);
 
   const Meta& m = a.m;
   const int b = seg / a.hkv, g = seg % a.hkv;
@@ -50,31 +51,31 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                         qscale, 1, 0, out, lse, nullptr, nullptr);
 }
 
-template <int G, int P>
+template <int G, int P, bool BOUNDS>
 hipError_t launch_g(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
                     int max_pages, hipStream_t s) {
   dim3 grid(a.m.batch * a.hkv);
   const size_t lds = (size_t)(2 * a.cap_keys + kSelectExtraWords) * sizeof(uint32_t);
   if constexpr (G <= 4) {
     if (gqa_attn_waves(G, max_pages) == 16) {
-      hipLaunchKernelGGL((decode_seg_kernel<G, P, 16>), grid, dim3(1024), lds, s, a,
+      hipLaunchKernelGGL((decode_seg_kernel<G, P, 16, BOUNDS>), grid, dim3(1024), lds, s, a,
                          (const uint16_t*)v_pool, qscale, out, lse);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_seg_kernel<G, P, 8>), grid, dim3(512), lds, s, a,
+  hipLaunchKernelGGL((decode_seg_kernel<G, P, 8, BOUNDS>), grid, dim3(512), lds, s, a,
                      (const uint16_t*)v_pool, qscale, out, lse);
   return hipGetLastError();
 }
 
-template <int P>
+template <int P, bool BOUNDS>
 hipError_t launch_p(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
                     int max_pages, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_g<1, P>(a, v_pool, qscale, out, lse, max_pages, s);
-    case 2: return launch_g<2, P>(a, v_pool, qscale, out, lse, max_pages, s);
-    case 4: return launch_g<4, P>(a, v_pool, qscale, out, lse, max_pages, s);
-    case 8: return launch_g<8, P>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 1: return launch_g<1, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 2: return launch_g<2, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 4: return launch_g<4, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 8: return launch_g<8, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -90,7 +91,7 @@ bool decode_step_fusable(const vx_geom& g, int page_size, int max_pages, int sel
 
 hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q,
                                   const void* k_pool, const void* v_pool, float* cent,
-                                  uint16_t* cent_bf16, int refresh, float score_scale,
+                                  uint16_t* cent_bf16, void* bounds, int refresh, float score_scale,
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
@@ -104,6 +105,7 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
   a.kp = k_pool;
   a.cent = cent;
   a.cent_bf16 = cent_bf16;
+  a.bounds = bounds;
   a.refresh = refresh;
   a.scale = score_scale;
   a.scores = scores;
@@ -117,8 +119,12 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
   a.sel_count = sel_count;
   a.cap_keys = (max_pages + 63) / 64 * 64;
   const float qscale = sm_scale * kLog2e;
-  if (m.page_size == 16) return launch_p<16>(a, v_pool, qscale, out, lse, max_pages, s);
-  return launch_p<64>(a, v_pool, qscale, out, lse, max_pages, s);
+  if (bounds) {
+    if (m.page_size == 16) return launch_p<16, true>(a, v_pool, qscale, out, lse, max_pages, s);
+    return launch_p<64, true>(a, v_pool, qscale, out, lse, max_pages, s);
+  }
+  if (m.page_size == 16) return launch_p<16, false>(a, v_pool, qscale, out, lse, max_pages, s);
+  return launch_p<64, false>(a, v_pool, qscale, out, lse, max_pages, s);
 }
 
 }  // namespace vx

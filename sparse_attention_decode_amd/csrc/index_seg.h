@@ -20,8 +20,14 @@
 //     from its keys (fp32, token order, one IEEE divide: the cache stage's
 //     arithmetic) with up to 32 tokens in flight per lane, writes it back and
 //     scores it.
+//   - BOUNDS: the Quest-style indexer instead (bounds.h): a head's slice of a
+//     page's key bounds is as many bytes as its fp32 centroid slice (bf16
+//     minima and maxima, 16 bytes per lane), scored with the stand-alone
+//     bound scorer's arithmetic; the refresh recomputes the newest page's
+//     bounds.
 #pragma once
 
+#include "bounds.h"
 #include "topk_wave.h"
 
 namespace vx {
@@ -35,6 +41,7 @@ struct SegArgs {
   const void* kp;
   float* cent;
   uint16_t* cent_bf16;
+  void* bounds;  // Quest-style indexer: [pool][Hkv][Dk/4][2][4] bf16
   int refresh;
   float scale;
   float* scores;
@@ -51,7 +58,7 @@ struct SegArgs {
 // receives the physical page of every entry in use; sel_lds / count_lds
 // (nullable) a copy of the selection. Ends after the selection is written;
 // its LDS copies are visible to the block after a barrier.
-template <typename QT, typename KV, int DK, int GG, int NW>
+template <typename QT, typename KV, int DK, int GG, int NW, bool BOUNDS = false>
 VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_lds,
                           int32_t* sel_lds, int32_t* count_lds) {
   constexpr int W = DK / 4;    // lanes per row slice
@@ -59,6 +66,7 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   constexpr int kChunk = kSegChunk * PPI;
   static_assert(kChunk <= 64, "one page id per lane");
   static_assert(NW <= 16, "block select reduction words");
+  static_assert(!BOUNDS || sizeof(KV) == 2, "bounds slices are 16 bytes per lane for bf16 keys");
 
   const Meta& m = a.m;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -97,12 +105,22 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   const int rw = refresh ? NW - 1 : NW;
   float* scores = a.scores + (size_t)g * m.nnz + row0;
 
-  auto emit = [&](int p, float4 r, bool ok) {
-    float sc = qs.x * r.x;
-    sc = fmaf(qs.y, r.y, sc);
-    sc = fmaf(qs.z, r.z, sc);
-    sc = fmaf(qs.w, r.w, sc);
-    sc = group_sum<W>(sc);
+  // this lane's share of a page's score, from its 16 bytes of the row slice
+  auto lane_part = [&](const u32x4& raw) {
+    if constexpr (BOUNDS) {
+      float lo[4], hi[4];
+      Unit<uint16_t>::widen(raw, lo, hi);
+      return unit_bound(qs, lo, hi);
+    } else {
+      float sc = qs.x * __uint_as_float(raw.x);
+      sc = fmaf(qs.y, __uint_as_float(raw.y), sc);
+      sc = fmaf(qs.z, __uint_as_float(raw.z), sc);
+      sc = fmaf(qs.w, __uint_as_float(raw.w), sc);
+      return sc;
+    }
+  };
+  auto emit = [&](int p, float part, bool ok) {
+    const float sc = group_sum<W>(part);
     if (ok && dl == 0) {
       scores[p] = sc;
       keys[p] = (p < a.n_sink || p >= n - a.n_local) ? 0u : topk_detail::score_key(sc);
@@ -115,23 +133,22 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
       const bool mine = cb + lane < pw1 && lane < kChunk;
       const int my_pid = mine ? phys_page(m, row0 + cb + lane) : 0;
       if (pid_lds && mine) pid_lds[cb + lane] = my_pid;
-      float4 r[kSegChunk];
+      u32x4 r[kSegChunk];
 #pragma unroll
       for (int t = 0; t < kSegChunk; ++t) {
         const int p = cb + t * PPI + sub;
         const int pid = __shfl(my_pid, t * PPI + sub);
-        // centroid rows are streamed once per step: non-temporal loads
-        const u32x4 raw =
-            p < pw1 ? __builtin_nontemporal_load(
-                          (const u32x4*)(a.cent + ((size_t)pid * a.hkv + g) * DK + 4 * dl))
-                    : u32x4{0u, 0u, 0u, 0u};
-        r[t] = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
-                           __uint_as_float(raw.w));
+        // rows are streamed once per step: non-temporal loads
+        const u32x4* src =
+            BOUNDS ? (const u32x4*)((const uint16_t*)a.bounds +
+                                    (((size_t)pid * a.hkv + g) * W + dl) * 8)
+                   : (const u32x4*)(a.cent + ((size_t)pid * a.hkv + g) * DK + 4 * dl);
+        r[t] = p < pw1 ? __builtin_nontemporal_load(src) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int t = 0; t < kSegChunk; ++t) {
         const int p = cb + t * PPI + sub;
-        emit(p, r[t], p < pw1);
+        emit(p, lane_part(r[t]), p < pw1);
       }
     }
   } else if (refresh) {
@@ -141,33 +158,48 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
     const int pid = phys_page(m, row0 + p);
     if (pid_lds && lane == 0) pid_lds[p] = pid;
     const bool own = sub == 0;
-    const KV* col = (const KV*)a.kp + ((size_t)pid * a.hkv + g) * P * DK + 4 * dl;
-    constexpr int kTok = sizeof(KV) == 2 ? 32 : 16;
-    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t0 = 0; t0 < nv; t0 += kTok) {
-      typename Quad<KV>::raw x[kTok];
-#pragma unroll
-      for (int t = 0; t < kTok; ++t)
-        if (own && t0 + t < nv) x[t] = Quad<KV>::load(col + (size_t)(t0 + t) * DK);
-#pragma unroll
-      for (int t = 0; t < kTok; ++t)
-        if (own && t0 + t < nv) {
-          const float4 v = Quad<KV>::widen(x[t]);
-          s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
-        }
-    }
-    const float fn = (float)nv;
-    const float4 c4 = make_float4(s4.x / fn, s4.y / fn, s4.z / fn, s4.w / fn);
-    if (own) {
-      const size_t o = ((size_t)pid * a.hkv + g) * DK + 4 * dl;
-      *(float4*)(a.cent + o) = c4;
-      if (a.cent_bf16) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(c4.x) | ((uint32_t)f32_to_bf16(c4.y) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(c4.z) | ((uint32_t)f32_to_bf16(c4.w) << 16);
-        *(uint2*)(a.cent_bf16 + o) = make_uint2(lo, hi);
+    if constexpr (BOUNDS) {
+      float part = 0.f;
+      if (own) {
+        float lo[4], hi[4];
+        unit_bounds<uint16_t>((const uint16_t*)a.kp, (uint16_t*)a.bounds, P, a.hkv, DK, pid, nv,
+                              g * W + dl, lo, hi);
+        part = unit_bound(qs, lo, hi);
       }
+      emit(p, part, own);
+    } else {
+      const KV* col = (const KV*)a.kp + ((size_t)pid * a.hkv + g) * P * DK + 4 * dl;
+      constexpr int kTok = sizeof(KV) == 2 ? 32 : 16;
+      float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int t0 = 0; t0 < nv; t0 += kTok) {
+        typename Quad<KV>::raw x[kTok];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+          if (own && t0 + t < nv) x[t] = Quad<KV>::load(col + (size_t)(t0 + t) * DK);
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+          if (own && t0 + t < nv) {
+            const float4 v = Quad<KV>::widen(x[t]);
+            s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
+          }
+      }
+      const float fn = (float)nv;
+      const float4 c4 = make_float4(s4.x / fn, s4.y / fn, s4.z / fn, s4.w / fn);
+      if (own) {
+        const size_t o = ((size_t)pid * a.hkv + g) * DK + 4 * dl;
+        *(float4*)(a.cent + o) = c4;
+        if (a.cent_bf16) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(c4.x) | ((uint32_t)f32_to_bf16(c4.y) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(c4.z) | ((uint32_t)f32_to_bf16(c4.w) << 16);
+          *(uint2*)(a.cent_bf16 + o) = make_uint2(lo, hi);
+        }
+      }
+      float part = qs.x * c4.x;
+      part = fmaf(qs.y, c4.y, part);
+      part = fmaf(qs.z, c4.z, part);
+      part = fmaf(qs.w, c4.w, part);
+      emit(p, part, own);
     }
-    emit(p, c4, own);
   }
   __syncthreads();  // every key of the segment is in LDS
   const uint32_t rnd = a.mode == VX_TOPK_APPROX ? a.rnd[seg] : 0u;

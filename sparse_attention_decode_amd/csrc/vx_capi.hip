@@ -243,7 +243,7 @@ void split_buffers(const vx_pages* p, const vx_geom* g, int S, void* ws, float**
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 3; }
+int32_t vx_abi_version(void) { return 4; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {
@@ -484,7 +484,8 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
   if (plan.num_splits == 1 && pages->total_pages > 0 &&
       vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride)) {
     const hipError_t e = vx::launch_decode_step_gqa(
-        meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, refresh_newest,
+        meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, nullptr,
+        refresh_newest,
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
         sel_count, out, lse, pages->max_pages, stream);
     return hip_status(e, "decode step kernel launch");
@@ -515,6 +516,61 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
   if ((st = vx_index_pages(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
                            score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,
                            sel_stride, sel_count, stream)) != VX_OK)
+    return st;
+  return vx_sparse_decode(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                          out, lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom, const void* q,
+                               const void* k_pool, const void* v_pool, void* bounds,
+                               int32_t refresh_newest, float score_scale, float sm_scale,
+                               int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
+                               const uint32_t* rand_u32, float* scores, int32_t* sel,
+                               int32_t sel_stride, int32_t* sel_count, float* out, float* lse,
+                               int32_t num_splits, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  VX_CHECK(!geom->mla, VX_ERR_UNSUPPORTED, "page bounds are implemented for GQA only");
+  VX_CHECK(workspace_bytes, VX_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  if ((st = check_decode_args(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                              out, workspace != nullptr)) != VX_OK)
+    return st;
+  if (workspace) {
+    VX_CHECK(refresh_newest == 0 || refresh_newest == 1, VX_ERR_INVALID_ARG,
+             "refresh_newest must be 0 or 1");
+    VX_CHECK(std::isfinite(score_scale), VX_ERR_INVALID_ARG, "score_scale not finite");
+    if ((st = check_topk(pages, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
+                         sel_count)) != VX_OK)
+      return st;
+    VX_CHECK(pages->total_pages == 0 || (bounds && scores), VX_ERR_INVALID_ARG,
+             "bounds or scores is NULL");
+  }
+  int cus = 0;
+  if ((st = device_cus(&cus)) != VX_OK) return st;
+  vx_plan plan;
+  if ((st = make_plan(pages, geom, sel_stride, num_splits, cus, &plan)) != VX_OK) return st;
+  if (!workspace) {
+    *workspace_bytes = plan.workspace_bytes;
+    return VX_OK;
+  }
+  VX_CHECK(*workspace_bytes >= plan.workspace_bytes, VX_ERR_WORKSPACE,
+           "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
+  if (pages->batch == 0) return VX_OK;
+  if (plan.num_splits == 1 && pages->total_pages > 0 &&
+      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride)) {
+    const hipError_t e = vx::launch_decode_step_gqa(
+        meta_of(pages), *geom, q, k_pool, v_pool, nullptr, nullptr, bounds, refresh_newest,
+        score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
+        sel_count, out, lse, pages->max_pages, stream);
+    return hip_status(e, "decode step kernel launch");
+  }
+  if ((st = vx_bound_scores(pages, geom, q, k_pool, bounds, refresh_newest, score_scale, scores,
+                            stream)) != VX_OK)
+    return st;
+  if ((st = vx_topk_pages(pages, geom->num_kv_heads, scores, k, n_sink, n_local, mode, rand_u32,
+                          sel, sel_stride, sel_count, stream)) != VX_OK)
     return st;
   return vx_sparse_decode(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
                           out, lse, num_splits, workspace, workspace_bytes, stream);

@@ -135,15 +135,27 @@ class DecodeStep:
                          self.sel, self.k_out, self.sel_count, self.out, self.lse,
                          self.num_splits, self.workspace, self.workspace_bytes, stream)
 
+    def bound_step(self, refresh: bool = True, stream=None) -> None:
+        """vx_bound_decode_step: the bounds indexer and the attention in one call."""
+        w = self.w
+        V.vx_bound_decode_step(self.pages, self.geom, w.q, w.k_pool, w.v_pool, self.bounds,
+                               refresh, self.score_scale, self.sm_scale, self.k, self.n_sink,
+                               self.n_local, self.mode, w.d_rand_u32, self.scores, self.sel,
+                               self.k_out, self.sel_count, self.out, self.lse, self.num_splits,
+                               self.workspace, self.workspace_bytes, stream)
+
     def plan(self) -> dict:
         return V.vx_plan_decode(self.pages, self.geom, self.k_out, self.num_splits)
 
     def run(self, stream=None) -> None:
         """The whole step: cache refresh, scoring, selection, attention."""
         if self.indexer == "bounds":
-            self.bound_score(refresh=True, stream=stream)
-            self.select(stream=stream)
-            self.attend(stream=stream)
+            if self.fused:
+                self.bound_step(stream=stream)
+            else:
+                self.bound_score(refresh=True, stream=stream)
+                self.select(stream=stream)
+                self.attend(stream=stream)
         elif self.fused:
             self.step(stream=stream)
         else:

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 3
+    assert lib.vx_abi_version() == 4
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -267,3 +267,31 @@ def test_bounds_argument_checks():
     empty = V.make_pages(0, 16, 0, 0, 0, None, None, None)
     V.vx_bounds_update(empty, g, None, None, None, stream=0)
     V.vx_bound_scores(empty, g, None, None, None, True, 1.0, None, stream=0)
+
+
+def test_bound_decode_step_argument_checks():
+    p, g = pages(), geom()
+    ok = dict(q=BAD, k_pool=BAD, v_pool=BAD, bounds=BAD, refresh=1, sscale=1.0, smscale=1.0,
+              k=4, n_sink=1, n_local=1, mode=0, rand_u32=None, scores=BAD, sel=BAD, stride=6,
+              count=BAD, out=BAD, lse=None, splits=0, ws=BAD, ws_bytes=1 << 30, pages=p, geom=g)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return status_of(V.vx_bound_decode_step, a["pages"], a["geom"], a["q"], a["k_pool"],
+                         a["v_pool"], a["bounds"], a["refresh"], a["sscale"], a["smscale"],
+                         a["k"], a["n_sink"], a["n_local"], a["mode"], a["rand_u32"], a["scores"],
+                         a["sel"], a["stride"], a["count"], a["out"], a["lse"], a["splits"],
+                         a["ws"], a["ws_bytes"], stream=0)
+
+    assert call(geom=geom(hkv=1, mla=1, dk=576, dv=512, hq=32)) == V.VX_ERR_UNSUPPORTED
+    assert call(refresh=2) == V.VX_ERR_INVALID_ARG
+    assert call(sscale=float("nan")) == V.VX_ERR_INVALID_ARG
+    assert call(smscale=float("inf")) == V.VX_ERR_INVALID_ARG
+    assert call(stride=5) == V.VX_ERR_INVALID_ARG
+    assert call(mode=1) == V.VX_ERR_INVALID_ARG
+    assert call(v_pool=None) == V.VX_ERR_INVALID_ARG
+    assert call(out=None) == V.VX_ERR_INVALID_ARG
+    assert call(scores=None) == V.VX_ERR_INVALID_ARG
+    assert call(bounds=None) == V.VX_ERR_INVALID_ARG
+    assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
+    assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED

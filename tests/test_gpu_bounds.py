@@ -159,3 +159,60 @@ def test_full_size_sampled(name, sample):
     assert check_against_oracle(w, step, sample) <= 1
     del w, step
     torch.cuda.empty_cache()
+
+
+def bound_step_vs_calls(w, num_splits=0, appends=2, **kw):
+    """vx_bound_decode_step against vx_bound_scores + vx_topk_pages +
+    vx_sparse_decode on separate buffers: the same bits."""
+    sep = DecodeStep(w, indexer="bounds", fused=False, num_splits=num_splits, **kw)
+    one = DecodeStep(w, indexer="bounds", fused=True, num_splits=num_splits, **kw)
+    sep.rebuild_bounds()
+    one.rebuild_bounds()
+    ids = used(w)
+    for _ in range(appends):
+        if w.spec.headroom_tokens > 0:
+            w.append_token()
+        valid = torch.zeros(w.nnz, dtype=torch.bool)
+        for b in range(w.batch):
+            lo = int(w.indptr[b])
+            valid[lo:lo + w.n_pages(b)] = True
+        valid = valid.to(w.device)
+        sep.run()
+        one.run()
+        T.sync()
+        assert torch.equal(sep.bounds[ids], one.bounds[ids])
+        assert torch.equal(sep.scores[:, valid], one.scores[:, valid])
+        assert torch.equal(sep.sel_count, one.sel_count)
+        assert torch.equal(sep.sel, one.sel)
+        assert torch.equal(sep.out, one.out)
+        assert torch.equal(sep.lse, one.lse)
+    return one
+
+
+@pytest.mark.parametrize("num_splits", [0, 1])
+@pytest.mark.parametrize("name", GQA_SMALL)
+def test_small_bound_step_equals_calls(name, num_splits):
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=38))
+    one = bound_step_vs_calls(w, num_splits=num_splits)
+    spec = w.spec
+    fused = (num_splits == 1 and spec.kv_dtype == "bf16" and spec.head_dim_k == 128
+             and one.k_out <= 256)
+    assert one.plan()["fused_step"] == int(fused)
+
+
+@pytest.mark.parametrize("k,n_sink,n_local", [(0, 1, 1), (3, 0, 0), (200, 1, 1), (5, 0, 3)])
+def test_bound_step_budgets(k, n_sink, n_local):
+    """The whole-step kernel selects inside the attention kernel: other
+    budgets give the separate calls' bits and the oracle's attention."""
+    w = on_gpu(W.make(SMALL["gqa_small"].replace(headroom_tokens=20), "cpu", seed=39))
+    one = bound_step_vs_calls(w, num_splits=1, appends=1, k=k, n_sink=n_sink, n_local=n_local)
+    assert check_against_oracle(w, one, range(w.batch)) <= max(1, w.batch // 20)
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "largebatch_bf16", "longgen_bf16"])
+def test_full_size_bound_step_equals_calls(name):
+    w = W.make(W.spec(name, headroom_tokens=max(64, W.spec(name).headroom_tokens)), "cuda", seed=3)
+    one = bound_step_vs_calls(w)
+    assert one.plan()["fused_step"] == 1
+    del w, one
+    torch.cuda.empty_cache()
