@@ -22,11 +22,12 @@
 // past a short sequence's pages; every load instruction reads 1 KB of
 // contiguous bounds (bf16). W = Dk / 4 lanes cover a KV head and reduce with
 // DPP. A wave has several pages' rows in flight, issued as soon as their
-// page ids arrive, while it finds its first entry's sequence and sums that
-// sequence's query chunks into registers. With refresh on,
-// one extra block per sequence recomputes the newest page's bounds from its
-// keys, stores them and scores that page from the values it computed (same
-// arithmetic as the other blocks); the other blocks skip that page.
+// page ids arrive, while the block finds its first entry's sequence and sums
+// that sequence's query into LDS once. With refresh on, one extra block per
+// sequence recomputes the newest page's bounds from its keys, stores them
+// and scores that page from the values it computed (same arithmetic as the
+// other blocks); the other blocks skip that page. The whole-step kernel runs
+// the same arithmetic per (sequence, KV head) segment (index_seg.h).
 #include "bounds.h"
 
 namespace vx {
