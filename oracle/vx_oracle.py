@@ -57,7 +57,7 @@ import numpy as np
 __all__ = [
     "num_pages", "valid_tokens", "centroids", "round_to_bf16", "page_scores",
     "forced_pages", "topk_exact", "topk_approx", "approx_buckets",
-    "attention", "decode_sequence", "page_bounds", "bound_scores",
+    "attention", "decode_sequence", "page_bounds", "bound_scores", "centroids_fp32",
 ]
 
 
@@ -85,6 +85,24 @@ def centroids(k: np.ndarray, seq_len: int, page_size: int) -> np.ndarray:
     for p in range(n):
         nv = valid_tokens(seq_len, page_size, p)
         out[p] = k[p, :, :nv, :].astype(np.float64).sum(axis=1) / nv
+    return out
+
+
+def centroids_fp32(k: np.ndarray, seq_len: int, page_size: int) -> np.ndarray:
+    """The cache stage in the precision this project defines for it (the
+    pages fix none): per page and KV head, the valid keys added in token order
+    with every addition rounded to fp32, then one IEEE fp32 division by the
+    number of valid tokens. Keys must be fp32-representable (bf16 and fp32
+    keys are). Returns [n][Hkv][Dk] float32."""
+    n = num_pages(seq_len, page_size)
+    Hkv, Dk = k.shape[1], k.shape[3]
+    out = np.zeros((n, Hkv, Dk), dtype=np.float32)
+    for p in range(n):
+        nv = valid_tokens(seq_len, page_size, p)
+        acc = np.zeros((Hkv, Dk), dtype=np.float32)
+        for t in range(nv):
+            acc = acc + k[p, :, t, :].astype(np.float32)  # float32 + float32: rounded
+        out[p] = acc / np.float32(nv)
     return out
 
 

@@ -437,3 +437,30 @@ def test_decode_sequence_bounds_indexer():
     assert list(cent["sel"][0]) == [0]
     assert list(bnd["sel"][0]) == [1]
     np.testing.assert_allclose(bnd["scores"][0], [1, 3, 0])
+
+
+# ------------------------------------------- the cache stage's fp32 definition
+
+def test_centroids_fp32_token_order():
+    """Addition in token order with fp32 rounding after each step: keys
+    2**24, 1, 1 sum to 2**24 (each +1 rounds away: ties to even), while any
+    order that adds the ones first gives 2**24 + 2; the mean is then one fp32
+    division of 2**24 by 3."""
+    k = np.zeros((1, 1, 4, 1))
+    k[0, 0, :3, 0] = [2.0 ** 24, 1.0, 1.0]
+    c = O.centroids_fp32(k, 3, 4)
+    assert c.dtype == np.float32
+    assert c[0, 0, 0] == np.float32(2.0 ** 24) / np.float32(3)
+    assert c[0, 0, 0] != np.float32((2.0 ** 24 + 2) / 3)
+
+
+def test_centroids_fp32_matches_fp64_when_exact():
+    """Small integer keys sum exactly in fp32, so the fp32 centroid is the
+    fp64 one rounded once; a partial last page divides by its own count."""
+    rng = np.random.default_rng(11)
+    P, L = 16, 45
+    k = rng.integers(-50, 51, size=(4, 2, P, 8)).astype(np.float64)
+    c32 = O.centroids_fp32(k, L, P)
+    c64 = O.centroids(k, L, P)
+    np.testing.assert_array_equal(c32, c64.astype(np.float32))
+    assert c32.shape == (3, 2, 8)
