@@ -216,3 +216,49 @@ def test_full_size_bound_step_equals_calls(name):
     assert one.plan()["fused_step"] == 1
     del w, one
     torch.cuda.empty_cache()
+
+
+# (Hq, Hkv, Dk, dtype): units per row C = Hkv * Dk / 4 of 512 (8 per lane), 128 (2), 64 and 32
+# (1, lanes idle); group sizes 3 (no compiled group size), 2, 1 and 8.
+GEOMETRIES = [(48, 16, 128, "bf16"), (8, 4, 128, "bf16"), (4, 4, 64, "bf16"), (16, 2, 64, "f32")]
+
+
+@pytest.mark.parametrize("hq,hkv,dk,dt", GEOMETRIES)
+def test_geometries(hq, hkv, dk, dt):
+    """Other row widths and group sizes: bounds exact and scores within
+    tolerance after appends; the whole step against the oracle where the
+    attention takes the group size (a group of 3 runs the cache stage and the
+    scorer only, through the C ABI directly)."""
+    from types import SimpleNamespace
+    from sparse_attention_decode_amd import binding as V
+    sp = W.spec("gqa_bf16", batch=4, num_q_heads=hq, num_kv_heads=hkv, head_dim_k=dk,
+                head_dim_v=dk, kv_dtype=dt, q_dtype=dt, lengths=("list", (100, 333, 17, 1)),
+                headroom_tokens=24)
+    w = on_gpu(W.make(sp, "cpu", seed=40))
+    if hq // hkv in (1, 2, 4, 8):
+        step = DecodeStep(w, indexer="bounds")
+        step.rebuild_bounds()
+        for _ in range(3):
+            w.append_token()
+            step.run()
+        T.sync()
+        assert check_against_oracle(w, step, range(w.batch)) <= 1
+        return
+    score_scale, sm_scale = sp.scales()
+    pages = V.make_pages(sp.batch, sp.page_size, w.pool_pages, w.nnz, w.max_pages, w.d_indptr,
+                         w.d_page_ids, w.d_seq_lens)
+    geom = V.make_geom(hq, hkv, dk, dk, 0, w.q.dtype, w.k_pool.dtype, 0)
+    st = SimpleNamespace(k=sp.topk, n_sink=sp.n_sink, n_local=sp.n_local, score_scale=score_scale,
+                         sm_scale=sm_scale, score_dim=0, indexer="bounds",
+                         bounds=torch.zeros((w.pool_pages, hkv, dk // 4, 2, 4), dtype=w.k_pool.dtype,
+                                            device=w.device),
+                         scores=torch.zeros((hkv, w.nnz), dtype=torch.float32, device=w.device))
+    V.vx_bounds_update(pages, geom, w.k_pool, None, st.bounds)
+    for _ in range(3):
+        w.append_token()
+        V.vx_bound_scores(pages, geom, w.q, w.k_pool, st.bounds, True, score_scale, st.scores)
+    T.sync()
+    for b in range(w.batch):
+        r = T.oracle_seq(w, st, b)
+        T.check_bounds(w, st, b, r)
+        T.check_bound_scores(w, st, b, r)
