@@ -190,8 +190,12 @@ constexpr int kScorePagesPerWave = 8;
 // one sequence for MLA, with its waves splitting that selection's chunks;
 // when the batch alone gives fewer blocks than compute units, each selection
 // is cut into S balanced splits (merged afterwards by log-sum-exp) so that
-// about one block runs per compute unit. No split holds more than
-// kMaxPagesPerSplit pages.
+// about one block runs per compute unit, but no split streams less than
+// kMinSplitBytes of keys and values (below that the merge launch costs more
+// than the parallelism gains). No split holds more than kMaxPagesPerSplit
+// pages.
+constexpr long kMinSplitBytes = 128 * 1024;
+
 vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num_splits,
                     int num_cus, vx_plan* out) {
   *out = vx_plan{};
@@ -203,6 +207,10 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
     S = num_splits;
   } else {
     long s = items0 > 0 ? (num_cus + items0 - 1) / items0 : 1;
+    const long elt = g->kv_dtype == VX_F32 ? 4 : 2;
+    const long row = (g->mla ? g->head_dim_k : g->head_dim_k + g->head_dim_v) * elt;
+    const long most = (long)stride * p->page_size * row / kMinSplitBytes;  // a full selection
+    if (s > most) s = most;
     S = (int)(s < 1 ? 1 : s);
   }
   if (S > stride) S = stride;

@@ -134,17 +134,28 @@ def test_planner_splits_and_workspace():
     # 32 sequences x 8 KV heads already give one block per compute unit: no split
     plan = V.vx_plan_decode(pages(batch=32, nnz=6144, pool=7680, maxp=256), g, 18, 0, 256)
     assert plan["num_splits"] == 1 and plan["workspace_bytes"] == 0
-    # a small batch is split so that about one block runs per compute unit
-    plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 0, 256)
+    # a small batch is split so that about one block runs per compute unit, each split
+    # streaming at least 128 KB: 18 pages x 64 tokens x 512 B = 576 KB -> 4 splits
+    plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20, page_size=64), g, 18, 0, 256)
     S, pps = plan["num_splits"], plan["pages_per_split"]
-    assert S == 16 and pps == 2
+    assert S == 4 and pps == 5
     assert plan["workspace_bytes"] >= 2 * 16 * S * (128 + 2) * 4
+    # 18 pages x 16 tokens x 512 B = 144 KB: one split, no merge
+    plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 0, 256)
+    assert plan["num_splits"] == 1 and plan["workspace_bytes"] == 0
     # an explicit split count is honoured (balanced splits, largest one reported)
     plan = V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 7, 256)
     assert plan["num_splits"] == 7 and plan["pages_per_split"] == 3
     # never more splits than selected pages, never more than 256 pages per split
-    plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64), g.__class__(2, 1, 64, 64, 0, 0, 0), 9, 0, 256)
+    tiny = g.__class__(2, 1, 64, 64, 0, 0, 0)
+    plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64), tiny, 9, 50, 256)
     assert plan["num_splits"] == 9
+    # 9 pages x 16 tokens x 512 B (fp32, D = 64) = 72 KB: one split
+    plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64), tiny, 9, 0, 256)
+    assert plan["num_splits"] == 1
+    # at 64-token pages 288 KB: two splits
+    plan = V.vx_plan_decode(pages(batch=1, nnz=64, pool=128, maxp=64, page_size=64), tiny, 9, 0, 256)
+    assert plan["num_splits"] == 2
     plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=200), g, 131, 1, 256)
     assert plan["pages_per_split"] == 131 and plan["num_splits"] == 1
     plan = V.vx_plan_decode(pages(batch=4096, nnz=500000, pool=500000, maxp=300), g, 260, 1, 256)
@@ -231,9 +242,11 @@ def test_plan_reports_the_whole_step_kernel():
     assert V.vx_plan_decode(big, geom(qd=V.VX_F32, kvd=V.VX_F32), 18, 0, 256)["fused_step"] == 0
     huge = pages(batch=32, nnz=200000, pool=200000, maxp=5000)
     assert V.vx_plan_decode(huge, g, 18, 0, 256)["fused_step"] == 0  # capacity > 4096 pages
-    small = pages(batch=2, nnz=40, pool=40, maxp=20)
+    small = pages(batch=2, nnz=40, pool=40, maxp=20, page_size=64)
     assert V.vx_plan_decode(small, g, 18, 0, 256)["fused_step"] == 0  # planner splits
     assert V.vx_plan_decode(small, g, 18, 1, 256)["fused_step"] == 1
+    # 144 KB per selection at 16-token pages: too little to split, one kernel
+    assert V.vx_plan_decode(pages(batch=2, nnz=40, pool=40, maxp=20), g, 18, 0, 256)["fused_step"] == 1
 
 
 def test_bounds_argument_checks():

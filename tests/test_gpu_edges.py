@@ -56,10 +56,11 @@ def test_zero_query_selects_lowest_indices():
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
-@pytest.mark.parametrize("base", ["longgen_bf16", "mla_bf16"])
+@pytest.mark.parametrize("base", ["longgen_bf16", "mla_bf16", "tiny_fp32"])
 def test_split_count_invariance(base, splits):
-    lens = ("uniform", 2500, 3000) if base == "longgen_bf16" else ("uniform", 4000, 5000)
-    sp = W.spec(base, batch=3, lengths=lens, headroom_tokens=0)
+    lens = {"longgen_bf16": ("uniform", 2500, 3000), "mla_bf16": ("uniform", 4000, 5000),
+            "tiny_fp32": ("uniform", 500, 1000)}[base]
+    sp = W.spec(base, batch=3, lengths=lens, headroom_tokens=0, pool=("factor", 1.25))
     w = on_gpu(W.make(sp, "cpu", seed=6))
     pipeline_check(w, range(3), DecodeStep(w, num_splits=splits))
 
