@@ -276,9 +276,10 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom,
  * backend": sequence-local fusion). Writes the same bits as vx_index_pages
  * followed by vx_sparse_decode with the same arguments (the latter's sel /
  * sel_count being the former's outputs). When the plan has one split per
- * (sequence, KV head) and the geometry is GQA, bf16, Dk = 128 with
+ * (sequence, KV head) and the geometry is GQA (group of 1, 2, 4 or 8) with
  * sel_stride <= 256 and max_pages <= 4096, it is one kernel with a block per
- * (sequence, KV head) that indexes and then attends over its own selection.
+ * (sequence, KV head) that indexes and then attends over its own selection
+ * (on the matrix cores for bf16 with Dk = 128, else on the vector ALUs).
  * MLA: the scorer, then one kernel in which every split block selects its
  * sequence's pages from the scores (the first split writes sel / sel_count)
  * and attends over its share, then the split merge. Otherwise the two calls'
@@ -303,10 +304,10 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom,
  * "Key results > User-side latency"). Writes the same bits as
  * vx_bound_scores (with refresh_newest), vx_topk_pages over those scores and
  * vx_sparse_decode over that selection, in that order. When the plan has one
- * split per (sequence, KV head) and the geometry is bf16, Dk = 128, with
- * sel_stride <= 256 and max_pages <= 4096, it is one kernel per step, the
- * same block-per-(sequence, KV head) kernel as vx_decode_step's with the
- * bounds scorer in place of the centroid scorer. workspace == NULL: writes
+ * split per (sequence, KV head), the keys are bf16 and sel_stride <= 256,
+ * max_pages <= 4096, it is one kernel per step, the same
+ * block-per-(sequence, KV head) kernel as vx_decode_step's with the bounds
+ * scorer in place of the centroid scorer. workspace == NULL: writes
  * the bytes needed to *workspace_bytes (those of vx_sparse_decode) and
  * returns VX_OK. */
 vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom,

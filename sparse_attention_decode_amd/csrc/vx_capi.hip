@@ -230,7 +230,7 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   }
   out->workspace_bytes = ws;
   out->fused_step = S == 1 && p->total_pages > 0 &&
-                    vx::decode_step_fusable(*g, p->page_size, p->max_pages, sel_stride);
+                    vx::decode_step_fusable(*g, p->page_size, p->max_pages, sel_stride, false);
   return VX_OK;
 }
 
@@ -490,7 +490,7 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
            "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
   if (pages->batch == 0) return VX_OK;
   if (plan.num_splits == 1 && pages->total_pages > 0 &&
-      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride)) {
+      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride, false)) {
     const hipError_t e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, nullptr,
         refresh_newest,
@@ -567,7 +567,7 @@ vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom, const
            "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
   if (pages->batch == 0) return VX_OK;
   if (plan.num_splits == 1 && pages->total_pages > 0 &&
-      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride)) {
+      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride, true)) {
     const hipError_t e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, nullptr, nullptr, bounds, refresh_newest,
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,

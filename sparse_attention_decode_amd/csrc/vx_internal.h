@@ -168,10 +168,12 @@ hipError_t launch_index_gqa(const Meta& m, const vx_geom& g, const void* q, cons
                             float* scores, int k, int n_sink, int n_local, int mode,
                             const uint32_t* rnd, int32_t* sel, int stride, int32_t* sel_count,
                             int max_pages, hipStream_t s);
-// Whole step per (sequence, KV head) in one kernel (GQA, bf16, Dk = 128, one
-// split): index_segment then mfma_attend. bounds != NULL: the Quest-style
-// indexer on those page bounds (cent and cent_bf16 unused).
-bool decode_step_fusable(const vx_geom& g, int page_size, int max_pages, int sel_stride);
+// Whole step per (sequence, KV head) in one kernel (GQA, one split):
+// index_segment then mfma_attend (bf16, Dk = 128) or vec_attend (fp32 keys or
+// Dk = 64). bounds != NULL: the Quest-style indexer on those page bounds
+// (cent and cent_bf16 unused; bf16 keys only).
+bool decode_step_fusable(const vx_geom& g, int page_size, int max_pages, int sel_stride,
+                         bool bounds);
 hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q,
                                   const void* k_pool, const void* v_pool, float* cent,
                                   uint16_t* cent_bf16, void* bounds, int refresh, float score_scale,

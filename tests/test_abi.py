@@ -239,7 +239,9 @@ def test_plan_reports_the_whole_step_kernel():
     assert V.vx_plan_decode(big, g, 18, 2, 256)["fused_step"] == 0  # two splits
     assert V.vx_plan_decode(big, g, 131, 0, 256)["fused_step"] == 1
     assert V.vx_plan_decode(big, g, 257, 0, 256)["fused_step"] == 0  # selection > 256 pages
-    assert V.vx_plan_decode(big, geom(qd=V.VX_F32, kvd=V.VX_F32), 18, 0, 256)["fused_step"] == 0
+    assert V.vx_plan_decode(big, geom(qd=V.VX_F32, kvd=V.VX_F32), 18, 0, 256)["fused_step"] == 1
+    assert V.vx_plan_decode(big, geom(dk=64, dv=64), 18, 0, 256)["fused_step"] == 1
+    assert V.vx_plan_decode(big, geom(hq=24, hkv=8), 18, 0, 256)["fused_step"] == 0  # group of 3
     huge = pages(batch=32, nnz=200000, pool=200000, maxp=5000)
     assert V.vx_plan_decode(huge, g, 18, 0, 256)["fused_step"] == 0  # capacity > 4096 pages
     small = pages(batch=2, nnz=40, pool=40, maxp=20, page_size=64)

@@ -195,9 +195,8 @@ def test_small_bound_step_equals_calls(name, num_splits):
     w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=38))
     one = bound_step_vs_calls(w, num_splits=num_splits)
     spec = w.spec
-    fused = (one.plan()["num_splits"] == 1 and spec.kv_dtype == "bf16" and spec.head_dim_k == 128
-             and one.k_out <= 256)
-    assert one.plan()["fused_step"] == int(fused)
+    fused = one.plan()["num_splits"] == 1 and one.k_out <= 256
+    assert one.plan()["fused_step"] == int(fused)  # the centroid step's plan; bounds: bf16 only
 
 
 @pytest.mark.parametrize("k,n_sink,n_local", [(0, 1, 1), (3, 0, 0), (200, 1, 1), (5, 0, 3)])
