@@ -95,26 +95,57 @@ __global__ __launch_bounds__(64 * NW) void attn_gqa_mfma_kernel(
 
 // out[b][h] = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m).
 // One block per (sequence, head), one thread per 4 value columns.
+// Up to kMergeBatch splits have every load in flight at once (their (m, l)
+// and this thread's 4 values of each partial output); the arithmetic and
+// its order are the same for any S.
+constexpr int kMergeBatch = 16;
+
 __global__ __launch_bounds__(128) void merge_kernel(int S, int dv, const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse) {
   const int bh = blockIdx.x;
   const float* ml = part_ml + (size_t)bh * S * 2;
-  float mmax = kNegBig;
-  for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, ml[2 * s]);
   const int d = 4 * threadIdx.x;
+  const float* po = part_o + (size_t)bh * S * dv + d;
+  float mmax = kNegBig;
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* po = part_o + (size_t)bh * S * dv + d;
+  if (S <= kMergeBatch) {
+    float2 mlv[kMergeBatch];
+    float4 x[kMergeBatch];
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s < S) {
+        mlv[s] = *(const float2*)(ml + 2 * s);
+        if (d < dv) x[s] = *(const float4*)(po + (size_t)s * dv);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s)
+      if (s < S) mmax = fmaxf(mmax, mlv[s].x);
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s < S) {
+        const float wt = __builtin_amdgcn_exp2f(mlv[s].x - mmax);
+        wsum = fmaf(mlv[s].y, wt, wsum);
+        if (d < dv) {
+          acc.x = fmaf(x[s].x, wt, acc.x); acc.y = fmaf(x[s].y, wt, acc.y);
+          acc.z = fmaf(x[s].z, wt, acc.z); acc.w = fmaf(x[s].w, wt, acc.w);
+        }
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, ml[2 * s]);
 #pragma unroll 4
-  for (int s = 0; s < S; ++s) {
-    const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
-    wsum = fmaf(ml[2 * s + 1], wt, wsum);
-    if (d < dv) {
-      const float4 x = *(const float4*)(po + (size_t)s * dv);
-      acc.x = fmaf(x.x, wt, acc.x); acc.y = fmaf(x.y, wt, acc.y);
-      acc.z = fmaf(x.z, wt, acc.z); acc.w = fmaf(x.w, wt, acc.w);
+    for (int s = 0; s < S; ++s) {
+      const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
+      wsum = fmaf(ml[2 * s + 1], wt, wsum);
+      if (d < dv) {
+        const float4 xs = *(const float4*)(po + (size_t)s * dv);
+        acc.x = fmaf(xs.x, wt, acc.x); acc.y = fmaf(xs.y, wt, acc.y);
+        acc.z = fmaf(xs.z, wt, acc.z); acc.w = fmaf(xs.w, wt, acc.w);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
