@@ -1,0 +1,81 @@
+"""Host logic of bench.py (no GPU): the algorithmic byte count, the
+selection overlap (recall@k), and the source hash that keys the HBM traffic
+table (comments do not change it, code does)."""
+
+import importlib.util
+import os
+import shutil
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+from sparse_attention_decode_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def small_workload():
+    sp = W.spec("gqa_bf16", batch=2, num_q_heads=4, num_kv_heads=2,
+                lengths=("list", (40, 17)))  # pages 3 (last holds 8) and 2 (last holds 1)
+    return W.make(sp, "cpu", seed=3)
+
+
+def fake_step(w, sel, indexer="centroid", k=2, n_sink=0, n_local=1):
+    sel = torch.tensor(sel, dtype=torch.int32)
+    cnt = (sel >= 0).sum(-1).to(torch.int32)
+    return SimpleNamespace(sel=sel, sel_count=cnt, indexer=indexer, k=k, n_sink=n_sink,
+                           n_local=n_local)
+
+
+def test_step_bytes_counts_valid_tokens_and_index_rows():
+    B = load_bench()
+    w = small_workload()
+    # sequence 0 selects pages 0 and 2 (16 + 8 tokens), sequence 1 page 1 (1 token), per KV head
+    step = fake_step(w, [[[0, 2, -1], [0, 2, -1]], [[1, -1, -1], [1, -1, -1]]])
+    cent, kv, tokens = B.step_bytes(w, step)
+    assert tokens == 2 * (16 + 8) + 2 * 1
+    assert kv == tokens * (128 + 128) * 2
+    assert cent == (3 + 2) * 2 * 128 * 4  # fp32 centroid rows of every page in use
+    bcent, _, _ = B.step_bytes(w, fake_step(w, step.sel.tolist(), indexer="bounds"))
+    assert bcent == (3 + 2) * 2 * 128 * 2 * 2  # bf16 minima and maxima
+
+
+def test_overlap_is_recall_without_forced_pages():
+    B = load_bench()
+    w = small_workload()
+    a = fake_step(w, [[[0, 1, 2], [0, 1, 2]], [[0, 1, -1], [0, 1, -1]]])
+    same = B.overlap(w, a, a.sel, a.sel_count, a.sel, a.sel_count)
+    assert same["mean"] == 1.0 and same["min"] == 1.0
+    # sequence 0: forced = last page (2); candidates 0, 1 both wanted (k = 2); the other
+    # selection keeps page 0 only -> recall 1/2 on both heads; sequence 1: 1 candidate
+    b = fake_step(w, [[[0, 2, -1], [0, 2, -1]], [[0, 1, -1], [0, 1, -1]]])
+    r = B.overlap(w, a, b.sel, b.sel_count, a.sel, a.sel_count)
+    assert r["min"] == 0.5 and np.isclose(r["mean"], (0.5 + 0.5 + 1 + 1) / 4)
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    B = load_bench()
+    src = os.path.join(ROOT, "sparse_attention_decode_amd", "csrc")
+    copy = tmp_path / "sparse_attention_decode_amd" / "csrc"
+    shutil.copytree(src, copy, ignore=shutil.ignore_patterns("*.o", "*.hipfb"))
+    monkeypatch.setattr(B, "ROOT", str(tmp_path))
+    h0 = B.sources_hash()
+    f = copy / "bounds.h"
+    text = f.read_text()
+    f.write_text("// a new comment line\n" + text.replace("#pragma once", "#pragma once  /* x */"))
+    assert B.sources_hash() == h0
+    f.write_text(text + "\nconstexpr int vx_extra = 1;\n")
+    assert B.sources_hash() != h0
+
+
+def test_measured_traffic_unknown_workload_is_none():
+    B = load_bench()
+    assert B.measured_traffic("no_such_workload", "decode_step") is None
