@@ -253,3 +253,25 @@ def test_step_selection_budgets(name, k, n_sink, n_local):
     w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=20), "cpu", seed=23))
     one = step_vs_calls(w, appends=1, k=k, n_sink=n_sink, n_local=n_local)
     assert check_step_against_oracle(w, one, range(w.batch)) <= max(1, w.batch // 20)
+
+
+@pytest.mark.parametrize("indexer", ["centroid", "bounds"])
+def test_selection_beyond_one_split(indexer):
+    """More than 256 selected pages per segment (k = 300): the plan needs two
+    or more attention splits, so the step runs as separate kernels with the
+    split merge; same bits as the separate calls, and the oracle."""
+    sp = W.spec("gqa_bf16", batch=2, num_q_heads=4, num_kv_heads=2,
+                lengths=("list", (6000, 9000)), headroom_tokens=16)
+    w = W.make(sp, "cuda", seed=24)
+    kw = dict(k=300, n_sink=1, n_local=1)
+    if indexer == "bounds":
+        from test_gpu_bounds import bound_step_vs_calls, check_against_oracle as check_bounds_step
+        one = bound_step_vs_calls(w, appends=1, **kw)
+        assert one.plan()["num_splits"] >= 2 and one.plan()["fused_step"] == 0
+        assert check_bounds_step(w, one, range(2)) == 0
+    else:
+        one = step_vs_calls(w, appends=1, **kw)
+        assert one.plan()["num_splits"] >= 2 and one.plan()["fused_step"] == 0
+        assert check_step_against_oracle(w, one, range(2)) == 0
+    del w, one
+    torch.cuda.empty_cache()
