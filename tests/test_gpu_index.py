@@ -275,3 +275,16 @@ def test_selection_beyond_one_split(indexer):
         assert check_step_against_oracle(w, one, range(2)) == 0
     del w, one
     torch.cuda.empty_cache()
+
+
+def test_mla_selection_beyond_one_split():
+    """MLA with more than 256 selected pages per sequence: the select +
+    attention kernel runs several splits of one selection and the merge; same
+    bits as the separate calls, and the oracle."""
+    sp = W.spec("mla_bf16", batch=2, lengths=("list", (20000, 30000)), headroom_tokens=64)
+    w = W.make(sp, "cuda", seed=25)
+    one = step_vs_calls(w, appends=1, k=300, n_sink=1, n_local=1)
+    assert one.plan()["num_splits"] >= 2
+    assert check_step_against_oracle(w, one, range(2)) == 0
+    del w, one
+    torch.cuda.empty_cache()
