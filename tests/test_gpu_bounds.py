@@ -261,3 +261,26 @@ def test_geometries(hq, hkv, dk, dt):
         r = T.oracle_seq(w, st, b)
         T.check_bounds(w, st, b, r)
         T.check_bound_scores(w, st, b, r)
+
+
+@pytest.mark.parametrize("name", ["gqa_small", "large_small"])
+def test_bound_step_approx_topk_equals_calls(name):
+    """The approximate top-k inside the whole-step kernel gives the separate
+    calls' bits on bound scores too."""
+    from sparse_attention_decode_amd import binding as V
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=20), "cpu", seed=42))
+    bound_step_vs_calls(w, num_splits=1, appends=2, mode=V.VX_TOPK_APPROX)
+
+
+def test_bound_step_very_large_capacity():
+    """Page capacity beyond the whole-step kernel's 4096 pages: the separate
+    kernels run, and match the oracle."""
+    sp = W.spec("gqa_bf16", batch=2, num_q_heads=4, num_kv_heads=2,
+                lengths=("list", (3000, 70)), headroom_tokens=130000)
+    w = W.make(sp, "cuda", seed=43)
+    assert w.max_pages > 8000
+    one = bound_step_vs_calls(w, appends=1)
+    assert one.plan()["fused_step"] == 0
+    assert check_against_oracle(w, one, range(2)) == 0
+    del w, one
+    torch.cuda.empty_cache()
