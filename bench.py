@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="only write profiles/<workload>_step.md and profiles/traffic.json from "
+                         "the rocprofv3 runs under DIR (see profile_commands)")
     ap.add_argument("--dense-compare", action="store_true",
                     help="sparse vs dense decode attention at a 32-query / 8-KV-head, D=128, "
                          "batch 16, 32K-token shape (prints its own JSON line)")
@@ -168,6 +171,172 @@ def measured_traffic(workload, stage):
     if not e or e.get("sources_sha256") != sources_hash() or stage not in e.get("stages", {}):
         return None
     return e["stages"][stage]["hbm_bytes_per_launch"]
+
+
+# Kernels whose HBM bytes make up each stage bench.py can report as dominant,
+# per profiled run (workload, or workload + "_bounds" for --indexer bounds).
+PROFILE_STAGES = {
+    "gqa_bf16": {"decode_step": ["decode_seg_kernel"], "indexer": ["index_seg_kernel"],
+                 "attention_merge": ["attn_gqa_mfma_kernel"]},
+    "largebatch_bf16": {"decode_step": ["decode_seg_kernel"], "indexer": ["index_seg_kernel"],
+                        "attention_merge": ["attn_gqa_mfma_kernel"]},
+    "longgen_bf16": {"decode_step": ["decode_seg_kernel"], "indexer": ["index_seg_kernel"],
+                     "attention_merge": ["attn_gqa_mfma_kernel"]},
+    "mla_bf16": {"indexer": ["scores_mla_kernel", "topk"],
+                 "attention_merge": ["attn_mla_kernel", "merge_kernel"]},
+    "tiny_fp32": {"decode_step": ["decode_seg_vec_kernel"], "indexer": ["index_seg_kernel"],
+                  "attention_merge": ["attn_gqa_kernel"]},
+    "gqa_bf16_bounds": {"decode_step": ["decode_seg_kernel"]},
+    "largebatch_bf16_bounds": {"decode_step": ["decode_seg_kernel"]},
+    "longgen_bf16_bounds": {"decode_step": ["decode_seg_kernel"]},
+}
+
+
+def profile_commands(run):
+    """The rocprofv3 runs a profiled run `run` (a PROFILE_STAGES key) needs,
+    with their outputs under $OUT: a kernel trace, then one pass per HBM
+    counter; the copy calibration passes run once for all."""
+    bounds = run.endswith("_bounds")
+    wl = run[:-len("_bounds")] if bounds else run
+    flags = f"--workload {wl}{' --indexer bounds' if bounds else ''}"
+    cmds = [f"rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{run}_trace -o run -- "
+            f"python3 $R/bench.py {flags} --steps 50 --warmup 5 --stage-reps 5 --no-cpu-baseline"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d $OUT/{run}_{c} -o run "
+                    f"-- python3 $R/bench.py {flags} --steps 8 --warmup 2 --stage-reps 1 --no-cpu-baseline")
+    return cmds
+
+
+def summarize_profiles(out, commit):
+    """Writes profiles/<run>_step.md for every run profiled under `out` and
+    profiles/traffic.json: per stage, the calibrated HBM bytes per launch
+    (FETCH_SIZE and WRITE_SIZE scaled by what they read for a plain 1 GiB
+    copy), keyed on sources_hash()."""
+    import collections
+    import csv
+    import re
+    import statistics
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "").replace("void ", "").replace("vx::", "")
+        return re.sub(r"\(.*", "", n).replace("unsigned short", "bf16")
+
+    def durations(d):
+        agg = collections.defaultdict(list)
+        with open(os.path.join(d, "run_kernel_trace.csv")) as f:
+            for r in csv.DictReader(f):
+                agg[short(r["Kernel_Name"])].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        return agg
+
+    def counters(d, name):
+        agg = collections.defaultdict(list)
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == name:
+                    agg[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return ({k: statistics.mean(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()})
+
+    cf, _ = counters(os.path.join(out, "copy_FETCH_SIZE"), "FETCH_SIZE")
+    cw, _ = counters(os.path.join(out, "copy_WRITE_SIZE"), "WRITE_SIZE")
+    copy_kernel = max(cf, key=lambda k: cf[k])
+    kib = (1 << 30) / 1024
+    ff, wf = kib / cf[copy_kernel], kib / cw[copy_kernel]
+    sha = sources_hash()
+    traffic = {"calibration": {"copy_kernel": copy_kernel, "bytes_read_and_written": 1 << 30,
+                               "fetch_size_kib": cf[copy_kernel], "write_size_kib": cw[copy_kernel],
+                               "fetch_factor": ff, "write_factor": wf},
+               "commit_profiled": commit, "workloads": {}}
+    for run, stages in PROFILE_STAGES.items():
+        if not os.path.isdir(os.path.join(out, run + "_trace")):
+            continue
+        bounds = run.endswith("_bounds")
+        wl = run[:-len("_bounds")] if bounds else run
+        dur = durations(os.path.join(out, run + "_trace"))
+        fe, nf = counters(os.path.join(out, run + "_FETCH_SIZE"), "FETCH_SIZE")
+        wr, _ = counters(os.path.join(out, run + "_WRITE_SIZE"), "WRITE_SIZE")
+        with open(os.path.join(out, run + "_trace.log")) as f:
+            text = f.read()
+        tot, cent, kv = (float(x) for x in re.search(
+            r"step touches ([\d.]+) MB \(centroids ([\d.]+), selected KV ([\d.]+)\)", text).groups())
+        step_us = re.search(r"\d+ steps: ([\d.]+) us/step", text).group(1)
+        stage_line = re.search(r"stage us: (.*)", text).group(1)
+        title = f"{wl} with the Quest-style bounds indexer" if bounds else wl
+        lines = [f"# {title}: one decode step, kernel durations and HBM traffic", "",
+                 f"Profiled at commit `{commit}` on one MI355X. Algorithmic bytes per step: {tot:.1f} MB "
+                 f"({'page bounds' if bounds else 'centroids'} {cent:.1f} MB + selected valid KV "
+                 f"{kv:.1f} MB).", "",
+                 "Commands (`cd /tmp && export TMPDIR=/tmp` first; `$R` = the repository, `$OUT` = the "
+                 "output directory), then `python3 $R/bench.py --summarize-profiles $OUT`:", "", "```",
+                 *profile_commands(run), "```", "",
+                 f"Same-run bench (under the profiler): {step_us} us/step; stages (each alone) "
+                 f"{stage_line}.", "",
+                 "| kernel | dispatches | mean us | median us | min us | FETCH_SIZE KiB | WRITE_SIZE KiB "
+                 "| HBM MB (calibrated) |", "|---|---|---|---|---|---|---|---|"]
+        for k, v in sorted(dur.items(), key=lambda kv_: -statistics.mean(kv_[1]) * len(kv_[1])):
+            if not k.startswith(("decode_seg", "decode_mla", "index_", "attn_", "merge", "scores_",
+                                 "topk", "centroid_", "bound")):
+                continue
+            f_, w_ = fe.get(k), wr.get(k)
+            hb = "" if f_ is None or w_ is None else round((f_ * ff + w_ * wf) * 1024 / 1e6, 2)
+            lines.append(f"| `{k}` | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} "
+                         f"| {min(v):.2f} | {f_ if f_ is None else round(f_, 1)} | "
+                         f"{w_ if w_ is None else round(w_, 1)} | {hb} |")
+        entry = {"sources_sha256": sha, "stages": {}}
+        for st, pats in stages.items():
+            parts, total = [], 0.0
+            for pat in pats:
+                match = [k for k in fe if pat in k and (not pat.startswith("decode_seg")
+                                                        or k.endswith("true>") == bounds)]
+                if not match:
+                    raise SystemExit(f"{run}: no counters for {pat}")
+                k = max(match, key=lambda x: nf[x])  # the stage's instantiation: most dispatches
+                b = (fe[k] * ff + wr.get(k, 0.0) * wf) * 1024
+                total += b
+                parts.append({"kernel": k, "fetch_size_kib": fe[k], "write_size_kib": wr.get(k, 0.0),
+                              "hbm_bytes": b})
+            entry["stages"][st] = {"kernels": parts, "hbm_bytes_per_launch": total}
+        traffic["workloads"][run] = entry
+        lines += ["", f"Calibration (`bench.py --copy-calibration`, a torch elementwise copy reading and "
+                      f"writing 1 GiB): FETCH_SIZE {cf[copy_kernel]:.1f} KiB and WRITE_SIZE "
+                      f"{cw[copy_kernel]:.1f} KiB per dispatch, so FETCH_SIZE is scaled by {ff:.3f} and "
+                      f"WRITE_SIZE by {wf:.3f}.", "",
+                  "HBM bytes per launch of the stages bench.py can report as dominant:", ""]
+        for st, e in entry["stages"].items():
+            lines.append(f"- `{st}`: {e['hbm_bytes_per_launch'] / 1e6:.2f} MB "
+                         f"({', '.join(p_['kernel'] for p_ in e['kernels'])})")
+        mf = os.path.join(out, run + "_MFMA")
+        if os.path.isdir(mf):
+            vals = collections.defaultdict(lambda: collections.defaultdict(list))
+            with open(os.path.join(mf, "run_counter_collection.csv")) as f:
+                for r in csv.DictReader(f):
+                    vals[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            mdur = durations(mf)
+            lines += ["", "## MFMA use (MLA kernels)", "", "```",
+                      f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES "
+                      f"SQ_INSTS_MFMA --kernel-trace --output-format csv -d $OUT/{run}_MFMA -o run -- "
+                      f"python3 $R/bench.py --workload {wl} --steps 8 --warmup 2 --stage-reps 1 "
+                      f"--no-cpu-baseline", "```", "",
+                      "| kernel | mean us (under counters) | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES "
+                      "| SQ_BUSY_CU_CYCLES | MFMA busy / CU busy |", "|---|---|---|---|---|---|"]
+            for k in sorted(vals):
+                if not k.startswith(("scores_mla", "attn_mla", "decode_mla")):
+                    continue
+                v = {c: statistics.mean(x) for c, x in vals[k].items()}
+                busy, cu = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("SQ_BUSY_CU_CYCLES", 0.0)
+                lines.append(f"| `{k}` | {statistics.mean(mdur[k]):.2f} | {v.get('SQ_INSTS_MFMA', 0):.0f} "
+                             f"| {busy:.0f} | {cu:.0f} | {100 * busy / cu if cu else 0:.1f} % |")
+            lines += ["", "By flops the scorer's [32 x 576] x [576 x pages] contraction is about 0.76 "
+                          "GFLOP per step and the", "attention's q.k^T and P.V about 9.7 GFLOP (32 heads "
+                          "x 2176 tokens x (576 + 512) x 2 x 32", "sequences); both read far more bytes "
+                          "per flop than the matrix cores' ridge, so HBM and",
+                      "latency bound them, and the MFMA busy fraction stays low."]
+        with open(os.path.join(ROOT, "profiles", f"{run}_step.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"wrote profiles/{run}_step.md")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    log("wrote profiles/traffic.json")
 
 
 def overlap(w, step, sel_a, cnt_a, sel_b, cnt_b):
@@ -344,6 +513,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.summarize_profiles:
+        import subprocess
+        commit = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
+                                capture_output=True, text=True).stdout.strip() or "unknown"
+        summarize_profiles(a.summarize_profiles, os.environ.get("PROFILED_COMMIT") or commit)
+        return
     if a.copy_calibration:
         copy_calibration()
         return

@@ -79,3 +79,50 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
 def test_measured_traffic_unknown_workload_is_none():
     B = load_bench()
     assert B.measured_traffic("no_such_workload", "decode_step") is None
+
+
+def _csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write(",".join(header) + "\n")
+        for r in rows:
+            f.write(",".join(str(x) for x in r) + "\n")
+
+
+def test_summarize_profiles_calibrates_counters(tmp_path, monkeypatch):
+    """Counters of a synthetic profiled run: FETCH_SIZE is scaled by what it
+    reads for the 1 GiB copy (here half of it: factor 2), WRITE_SIZE likewise
+    (factor 1); the stage's bytes per launch are the scaled sum."""
+    B = load_bench()
+    out = tmp_path / "prof"
+    copy = "void at::native::copy_kernel(float)"
+    kern = "void vx::(anonymous namespace)::decode_seg_kernel<2, 16, 16, false>(vx::SegArgs)"
+    cc = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    _csv(str(out / "copy_FETCH_SIZE" / "run_counter_collection.csv"), cc,
+         [[f'"{copy}"', "FETCH_SIZE", 524288.0]])
+    _csv(str(out / "copy_WRITE_SIZE" / "run_counter_collection.csv"), cc,
+         [[f'"{copy}"', "WRITE_SIZE", 1048576.0]])
+    _csv(str(out / "gqa_bf16_FETCH_SIZE" / "run_counter_collection.csv"), cc,
+         [[f'"{kern}"', "FETCH_SIZE", 1000.0], [f'"{kern}"', "FETCH_SIZE", 1000.0]])
+    _csv(str(out / "gqa_bf16_WRITE_SIZE" / "run_counter_collection.csv"), cc,
+         [[f'"{kern}"', "WRITE_SIZE", 10.0]])
+    _csv(str(out / "gqa_bf16_trace" / "run_kernel_trace.csv"),
+         ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+         [[f'"{kern}"', 1000, 19000], [f'"{kern}"', 50000, 68000]])
+    with open(out / "gqa_bf16_trace.log", "w") as f:
+        f.write("[bench] step touches 62.4 MB (centroids 25.7, selected KV 36.7); 16 replica(s)\n"
+                "[bench] 50 steps: 18.50 us/step (host wall 18.70 us)\n"
+                "[bench] stage us: decode_step 18.20\n")
+    os.makedirs(tmp_path / "profiles")
+    monkeypatch.setattr(B, "ROOT", str(tmp_path))
+    monkeypatch.setattr(B, "sources_hash", lambda: "h")
+    monkeypatch.setattr(B, "PROFILE_STAGES", {"gqa_bf16": {"decode_step": ["decode_seg_kernel"]}})
+    B.summarize_profiles(str(out), "abc1234")
+    import json
+    t = json.load(open(tmp_path / "profiles" / "traffic.json"))
+    assert t["calibration"]["fetch_factor"] == 2.0 and t["calibration"]["write_factor"] == 1.0
+    st = t["workloads"]["gqa_bf16"]["stages"]["decode_step"]
+    assert st["hbm_bytes_per_launch"] == (1000.0 * 2 + 10.0) * 1024
+    md = (tmp_path / "profiles" / "gqa_bf16_step.md").read_text()
+    assert "| `decode_seg_kernel<2, 16, 16, false>` | 2 | 18.00 |" in md
+    assert "abc1234" in md
