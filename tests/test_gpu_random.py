@@ -72,3 +72,41 @@ def test_random_configuration(seed):
             else:
                 differing += 1
     assert differing <= 1
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_mla_configuration(seed):
+    rng = np.random.default_rng(2000 + seed)
+    batch = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(1, 9000, size=batch)]
+    if batch > 2:
+        lens[int(rng.integers(batch))] = 0
+    hq = int(rng.choice([16, 32]))
+    sp = W.spec("mla_bf16", batch=batch, num_q_heads=hq, lengths=("list", tuple(lens)),
+                headroom_tokens=int(rng.integers(0, 70)), pool=("factor", 1.5))
+    kw = dict(k=int(rng.integers(0, 40)), n_sink=int(rng.integers(0, 3)),
+              n_local=int(rng.integers(0, 3)), num_splits=int(rng.choice([0, 0, 1, 5])),
+              score_dim=int(rng.choice([0, 512])))
+    w = on_gpu(W.make(sp, "cpu", seed=seed))
+    step = DecodeStep(w, **kw)
+    step.rebuild()
+    step.run()
+    for _ in range(min(int(rng.integers(0, 3)), sp.headroom_tokens)):
+        w.append_token()
+        step.run()
+    T.sync()
+    out = step.out.cpu().double().numpy()
+    lse = step.lse.cpu().double().numpy()
+    differing = 0
+    for b in range(batch):
+        if int(w.seq_lens[b]) == 0:
+            assert (step.out[b] == 0).all() and (step.sel_count[b] == 0).all()
+            continue
+        r = T.oracle_seq(w, step, b)
+        T.check_centroids(w, step, b, r)
+        T.check_scores(w, step, b, r)
+        if T.check_selection(w, step, b, r)[0]:
+            T.check_attention(w, out[b], lse[b], r["out"], r["lse"], tag=f"seed={seed} b={b}")
+        else:
+            differing += 1
+    assert differing <= 1
