@@ -284,3 +284,22 @@ def test_bound_step_very_large_capacity():
     assert check_against_oracle(w, one, range(2)) == 0
     del w, one
     torch.cuda.empty_cache()
+
+
+def test_zero_query_selects_lowest_indices():
+    """q = 0: every bound score is a (signed) zero, all rank equal, and the
+    tie-break keeps the lowest logical pages besides the forced ones."""
+    sp = W.spec("gqa_bf16", batch=3, lengths=("list", (300, 517, 64)))
+    w = on_gpu(W.make(sp, "cpu", seed=5))
+    w.q.zero_()
+    step = DecodeStep(w, indexer="bounds")
+    step.rebuild_bounds()
+    step.run()
+    T.sync()
+    assert check_against_oracle(w, step, range(3)) == 0
+    sel = step.sel.cpu().numpy()
+    for b in range(3):
+        n = w.n_pages(b)
+        for g in range(w.spec.num_kv_heads):
+            want = sorted(set(range(min(n, 1 + 16))) | {n - 1})
+            assert list(sel[b, g][:len(want)]) == want
