@@ -192,8 +192,8 @@ constexpr int kScorePagesPerWave = 8;
 // is cut into S balanced splits (merged afterwards by log-sum-exp) so that
 // about one block runs per compute unit, but no split streams less than
 // kMinSplitBytes of keys and values (below that the merge launch costs more
-// than the parallelism gains). No split holds more than kMaxPagesPerSplit
-// pages.
+// than the parallelism gains), and no more splits are used than the largest
+// split's size needs. No split holds more than kMaxPagesPerSplit pages.
 constexpr long kMinSplitBytes = 128 * 1024;
 
 vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num_splits,
@@ -212,6 +212,12 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
     const long most = (long)stride * p->page_size * row / kMinSplitBytes;  // a full selection
     if (s > most) s = most;
     S = (int)(s < 1 ? 1 : s);
+    if (S > stride) S = stride;
+    // The largest split sets the time; use no more splits than that size
+    // needs (fewer partials to write and merge, fewer blocks repeating
+    // per-sequence work).
+    const int pps = (stride + S - 1) / S;
+    S = (stride + pps - 1) / pps;
   }
   if (S > stride) S = stride;
   const int min_splits = (stride + vx::kMaxPagesPerSplit - 1) / vx::kMaxPagesPerSplit;

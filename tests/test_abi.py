@@ -165,7 +165,7 @@ def test_planner_splits_and_workspace():
     # MLA: one block per sequence and split
     mla = V.make_geom(32, 1, 576, 512, 1, V.VX_BF16, V.VX_BF16)
     plan = V.vx_plan_decode(pages(batch=32, nnz=20480, pool=25600, maxp=1024, page_size=64), mla, 34, 0, 256)
-    assert plan["num_splits"] == 8
+    assert plan["num_splits"] == 7 and plan["pages_per_split"] == 5  # 8 splits would also take 5
 
 
 def test_index_pages_argument_checks():
