@@ -233,7 +233,6 @@ hipError_t launch_t(const Meta& m, const vx_geom& geo, const void* q, const void
   if (dk == 64 && P == 64)
     return launch_g<QT, KV, 64, 64>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, pps,
                                     out, lse, po, pml, st);
-#ifndef VX_GQA_FORCE_VALU
   if constexpr (sizeof(KV) == 2) {
     if (dk == 128 && P == 16)
       return launch_mfma<16>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out, lse,
@@ -242,7 +241,6 @@ hipError_t launch_t(const Meta& m, const vx_geom& geo, const void* q, const void
       return launch_mfma<64>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, out, lse,
                              po, pml, max_pages, st);
   }
-#endif
   if (dk == 128 && P == 16)
     return launch_g<QT, KV, 128, 16>(m, geo, q, k_pool, v_pool, sel, stride, cnt, qscale, S, pps,
                                      out, lse, po, pml, st);

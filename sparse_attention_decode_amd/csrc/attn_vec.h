@@ -37,14 +37,8 @@ template <> struct KVTraits<uint16_t> {
   }
 };
 
-#ifndef VX_ATTN_WAVES
-#define VX_ATTN_WAVES 8
-#endif
-constexpr int kVecWaves = VX_ATTN_WAVES;  // waves per vector attention block
-#ifndef VX_ATTN_BATCH
-#define VX_ATTN_BATCH 1
-#endif
-constexpr int kVecBatch = VX_ATTN_BATCH;  // chunks in flight per wave (short rows)
+constexpr int kVecWaves = 8;  // waves per vector attention block
+constexpr int kVecBatch = 1;  // chunks in flight per wave (short rows)
 
 template <typename QT, typename KV, int G>
 struct VecQuery {

@@ -29,14 +29,8 @@
 namespace vx {
 namespace {
 
-#ifndef VX_SCORE_PPW
-#define VX_SCORE_PPW 4
-#endif
-#ifndef VX_INDEX_WAVES
-#define VX_INDEX_WAVES 8
-#endif
-constexpr int kPPW = VX_SCORE_PPW;      // pages per wave, all rows in flight at once
-constexpr int kWaves = VX_INDEX_WAVES;  // waves per block
+constexpr int kPPW = 4;    // pages per wave, all rows in flight at once
+constexpr int kWaves = 8;  // waves per block
 constexpr int kSpan = kWaves * kPPW;    // entries per block
 
 template <typename T>
