@@ -34,13 +34,30 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   static_assert(kMaxPagesPerSplit <= 64 * NW, "one page-list entry per thread");
 
   const int seg = blockIdx.x;
+  const int b = seg / a.hkv, g = seg % a.hkv;
+  const uint16_t* kp = (const uint16_t*)a.kp;
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
-  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l);
+  u32x4 qa[4];
+  MfmaState st;
+  st.init();
+  // With a forced sink and newest page, the first and last page of the
+  // selection are pages 0 and n-1 whatever the scores: while wave 0 selects,
+  // the waves that the chunk deal gives their chunks attend them.
+  bool q_loaded = false, ends_done = false;
+  auto idle = [&](int n, int L) {
+    mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
+    q_loaded = true;
+    if (a.n_sink >= 1 && a.n_local >= 1 && n >= 1) {
+      const ChunkDeal<P / 16> d(n >= 2 ? 2 : 1);
+      mfma_end_chunks<G, P, NW>(sm, st, d, pid_l[0], min(P, L), pid_l[n - 1],
+                                min(P, L - (n - 1) * P), g, a.hkv, qa, kp, vp, qscale);
+      ends_done = true;
+    }
+  };
+  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, idle);
 
   const Meta& m = a.m;
-  const int b = seg / a.hkv, g = seg % a.hkv;
-  u32x4 qa[4];
-  mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
+  if (!q_loaded) mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
   __syncthreads();  // selection and page ids visible to the block
   const int count = min(cnt_l, kMaxPagesPerSplit);
   const int L = seq_len_clamped(m, b);
@@ -50,8 +67,12 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
     pg_nv[threadIdx.x] = max(0, min(P, L - lp * P));
   }
   __syncthreads();  // page list ready
-  mfma_attend<G, P, NW>(sm, pg_phys, pg_nv, count, b, g, a.hkv, qa, (const uint16_t*)a.kp, vp,
-                        qscale, 1, 0, out, lse, nullptr, nullptr);
+  const ChunkDeal<P / 16> d(count);
+  if (!ends_done && count > 0)
+    mfma_end_chunks<G, P, NW>(sm, st, d, pg_phys[0], pg_nv[0], pg_phys[count - 1],
+                              pg_nv[count - 1], g, a.hkv, qa, kp, vp, qscale);
+  mfma_mid_chunks<G, P, NW>(sm, st, d, pg_phys, pg_nv, g, a.hkv, qa, kp, vp, qscale);
+  mfma_finish<G, NW>(sm, st, b, g, a.hkv, 1, 0, out, lse, nullptr, nullptr);
 }
 
 template <typename KV, int G, int DK, int P, bool BOUNDS>

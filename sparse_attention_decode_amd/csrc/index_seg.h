@@ -53,14 +53,24 @@ struct SegArgs {
   int cap_keys;
 };
 
+// What the waves other than wave 0 do while wave 0 selects: nothing.
+struct NoIdle {
+  VX_DEV void operator()(int, int) const {}
+};
+
 // The index of segment seg = b * Hkv + g by a block of NW waves (NW <= 16).
 // keys: LDS, cap_keys + kSelectExtraWords words (16-byte aligned). pid_lds (nullable, cap_keys ints)
 // receives the physical page of every entry in use; sel_lds / count_lds
 // (nullable) a copy of the selection. Ends after the selection is written;
-// its LDS copies are visible to the block after a barrier.
-template <typename QT, typename KV, int DK, int GG, int NW, bool BOUNDS = false>
+// its LDS copies are visible to the block after a barrier. When one wave
+// selects (segments of up to kBlockSelectMin pages), the other waves call
+// idle(n, L) meanwhile (n pages in use, L tokens; the keys and pid_lds are
+// then visible); a longer segment is selected by every wave and idle is not
+// called.
+template <typename QT, typename KV, int DK, int GG, int NW, bool BOUNDS = false,
+          typename Idle = NoIdle>
 VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_lds,
-                          int32_t* sel_lds, int32_t* count_lds) {
+                          int32_t* sel_lds, int32_t* count_lds, Idle idle = Idle{}) {
   constexpr int W = DK / 4;    // lanes per row slice
   constexpr int PPI = 64 / W;  // pages per load instruction
   constexpr int kChunk = kSegChunk * PPI;
@@ -208,9 +218,11 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
                           a.n_local, a.mode, rnd, a.sel + (size_t)seg * a.stride, a.stride,
                           a.sel_count + seg, sel_lds, count_lds);
   else if (w == 0)
-    wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd,
+    wave_select_keys(keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd,
                      a.sel + (size_t)seg * a.stride, a.stride, a.sel_count + seg, lane, sel_lds,
                      count_lds);
+  else
+    idle(n, L);
 }
 
 }  // namespace vx

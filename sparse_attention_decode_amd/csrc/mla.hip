@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256 * MT) void decode_mla_kernel(MlaStepArgs a) {
     block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + kSelectHistWords, n, a.k, a.n_sink,
                           a.n_local, a.mode, rnd, gsel, a.stride, gcnt, sel_l, &cnt_l);
   else if (w == 0)
-    wave_select_keys(keys, keys + a.cap_keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd, gsel,
+    wave_select_keys(keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd, gsel,
                      a.stride, gcnt, lane, sel_l, &cnt_l);
   __syncthreads();  // selection in LDS
   int p0, p1;

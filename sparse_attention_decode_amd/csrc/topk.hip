@@ -15,16 +15,16 @@ __global__ __launch_bounds__(256) void topk_kernel(Meta m, int hkv, const float*
                                                    int32_t* __restrict__ sel_count, int cap_keys) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int seg = blockIdx.x * (blockDim.x >> 6) + w;
   if (seg >= m.batch * hkv) return;  // whole wave; no block barrier below
-  uint32_t* keys = lds + w * (cap_keys + 256);
+  uint32_t* keys = lds + w * cap_keys;
   const int b = seg / hkv, g = seg % hkv;
   const int row0 = m.indptr[b];
   const int cap = m.indptr[b + 1] - row0;
   int n = (seq_len_clamped(m, b) + m.page_size - 1) / m.page_size;
   n = n > cap ? cap : n;
-  wave_select(keys, keys + cap_keys, cap_keys, scores + (size_t)g * m.nnz + row0, n, k, n_sink,
+  wave_select(keys, cap_keys, scores + (size_t)g * m.nnz + row0, n, k, n_sink,
               n_local, mode, mode == VX_TOPK_APPROX ? rnd[seg] : 0u, sel + (size_t)seg * stride,
               stride, sel_count + seg, lane);
 }
@@ -69,7 +69,7 @@ hipError_t launch_topk_sized(const Meta& m, int hkv, const float* scores, int k,
                        cap_keys);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)waves_per_block * (cap_keys + 256) * sizeof(uint32_t);
+  const size_t lds = (size_t)waves_per_block * cap_keys * sizeof(uint32_t);
   dim3 block(64 * waves_per_block), grid((segs + waves_per_block - 1) / waves_per_block);
   hipLaunchKernelGGL(topk_kernel, grid, block, lds, s, m, hkv, scores, k, n_sink, n_local, mode,
                      rand_u32, sel, sel_stride, sel_count, cap_keys);

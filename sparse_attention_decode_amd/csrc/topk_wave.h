@@ -1,22 +1,36 @@
-// Wave-level radix top-k over one (sequence, KV head) segment of page scores.
+// Radix top-k over one (sequence, KV head) segment of page scores.
 //
 // Vortex paper note, "System design > 1. vFlow": keep the top-k blocks by
 // score; "System design > 3. Execution backend": top-k is the indexer's
 // bottleneck, served by a radix top-k with an approximate mode (stochastic
 // early termination and remapping) when recall can be traded for time.
 //
-// One wave per segment. Scores become order-preserving 32-bit keys in LDS
-// (forced pages get key 0 and never compete). Exact mode runs 8-bit digit
-// passes, most significant first, starting at the first byte where the
-// smallest and largest candidate keys differ: an LDS histogram of the digit
-// among keys that still match the chosen prefix, a DPP scan across the wave
-// to find the digit where the count from the top reaches the remaining need
-// r, and an early exit when that bucket holds exactly r keys. The
-// survivors are then compacted in index order with ballot + mbcnt prefix
-// sums, which yields ascending page ids and the lower-index tie-break.
-// Approximate mode maps candidate scores affinely onto 256 buckets, runs one
-// pass and fills the r remaining places from the boundary bucket cyclically
-// from a random offset.
+// Scores become order-preserving 32-bit keys in LDS (forced pages get key 0
+// and never compete). The selection rule has one answer: the forced pages
+// plus the kk best candidates by (score desc, page index asc).
+//
+// Register select (segments of up to 256 keys, one wave): each lane holds
+// its keys in registers and a threshold tau is searched two bits per step,
+// most significant first: per step, three ballot counts (one ballot per key
+// register) tell how many keys reach each of the three candidate values, so
+// no LDS round trip or barrier is needed, and the search stops as soon as
+// exactly kk keys reach tau. Keys above tau are taken, and the first
+// kk - count(> tau) keys equal to tau in index order; a ballot + mbcnt
+// compaction writes the survivors in ascending page order. The approximate
+// mode first maps the candidates' scores affinely onto 256 buckets (the
+// remap) and runs the same search over the 9-bit bucket codes only (the
+// early termination); the places left in the boundary bucket are filled
+// cyclically from a random offset (the stochastic part).
+//
+// Block select (longer segments, exact mode, small k): every wave selects
+// the local top kk of a contiguous range of the keys in registers; the
+// union of the local lists holds the global top kk (a key outside its
+// range's top kk has kk better keys in the same order), so one wave then
+// selects from at most NW * kk candidates the same way. Otherwise (large k,
+// very long segments, approximate mode) the block runs 8-bit digit passes:
+// LDS histograms shared by the waves, a DPP wave scan to find the digit, an
+// early exit when the boundary bucket is exactly needed, then an ordered
+// compaction by all waves.
 #pragma once
 
 #include "vx_internal.h"
@@ -107,35 +121,71 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t r, in
   return out;
 }
 
-// Ordered compaction (ascending page index) of the survivors: forced pages,
-// candidates with (key & mask) > prefix, and r of those with (key & mask) ==
-// prefix taken in index order from offset `off`, cyclic over the `members`
-// of that tie group. One wave; ballot + mbcnt ranks keep the order. out /
-// count_out (global) and out_lds / count_lds may each be null.
-__device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, int n, int n_sink,
-                                             int n_local, uint32_t prefix, uint32_t mask,
-                                             uint32_t r, uint32_t off, uint32_t members,
-                                             int32_t* __restrict__ out, int stride,
-                                             int32_t* __restrict__ count_out, int lane,
-                                             int32_t* __restrict__ out_lds,
-                                             int32_t* __restrict__ count_lds) {
-  uint32_t written = 0, tie_seen = 0;
-  for (int base0 = 0; base0 < n; base0 += 64 * kU) {
-    uint32_t kvs[kU];
+// Number of the wave's register keys >= t (R registers, the first ru used).
+// ru and t must be wave-uniform (they are kept in scalar registers, so the
+// loop has no divergent branch and the count stays scalar).
+template <int R>
+__device__ __forceinline__ uint32_t count_ge(const uint32_t (&kv)[R], int ru, uint32_t t) {
+  uint32_t c = 0;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = base0 + 64 * u + lane;
-      kvs[u] = i < n ? keys[i] : 0u;
-    }
+  for (int u = 0; u < R; ++u)
+    if (u < ru) c += (uint32_t)__popcll(__ballot(kv[u] >= t));
+  return __builtin_amdgcn_readfirstlane(c);
+}
+
+// A threshold for the kk best of the wave's register keys (1 <= kk <= number
+// of nonzero keys, keys below 2^(top+1), top odd): the largest tau with
+// count_ge(tau) >= kk, decided two bits per step from the top (three
+// independent counts per step), or an earlier tau with count_ge(tau) == kk
+// exactly, where the keys >= tau already are the kk best. Either way the
+// kk best are the keys > tau plus the first kk - count_ge(tau + 1) keys
+// equal to tau.
+template <int R>
+__device__ __forceinline__ uint32_t select_threshold(const uint32_t (&kv)[R], int ru, uint32_t kk,
+                                                     int top) {
+  ru = __builtin_amdgcn_readfirstlane(ru);
+  kk = __builtin_amdgcn_readfirstlane(kk);
+  uint32_t tau = 0;
+  for (int bit = __builtin_amdgcn_readfirstlane(top) - 1; bit >= 0; bit -= 2) {
+    const uint32_t t1 = tau | (1u << bit), t2 = tau | (2u << bit), t3 = tau | (3u << bit);
+    const uint32_t c1 = count_ge<R>(kv, ru, t1);
+    const uint32_t c2 = count_ge<R>(kv, ru, t2);
+    const uint32_t c3 = count_ge<R>(kv, ru, t3);
+    uint32_t c;
+    if (c3 >= kk) { tau = t3; c = c3; }
+    else if (c2 >= kk) { tau = t2; c = c2; }
+    else if (c1 >= kk) { tau = t1; c = c1; }
+    else { c = 0; }
+    if (c == kk) break;
+  }
+  return __builtin_amdgcn_readfirstlane(tau);
+}
+
+// Ordered compaction from registers: lane key u is element i0 + 64 u + lane
+// (code 0 = not a candidate). Survivors: forced pages (i < n_sink or
+// i >= n - n_local), codes > tau, and r of the codes == tau taken in index
+// order cyclically from offset `off` over their `members`. Writes
+// out[o0 + rank] (global) and out_lds[o0 + rank] (each nullable); returns the
+// number written.
+template <int R>
+__device__ __forceinline__ uint32_t reg_compact(const uint32_t (&code)[R], const int32_t (&idx)[R],
+                                                int ru, int n, int n_sink, int n_local,
+                                                uint32_t tau, uint32_t r, uint32_t off,
+                                                uint32_t members, int32_t* __restrict__ out,
+                                                int32_t* __restrict__ out_lds, uint32_t o0) {
+  ru = __builtin_amdgcn_readfirstlane(ru);
+  tau = __builtin_amdgcn_readfirstlane(tau);
+  r = __builtin_amdgcn_readfirstlane(r);
+  off = __builtin_amdgcn_readfirstlane(off);
+  members = __builtin_amdgcn_readfirstlane(members);
+  uint32_t written = __builtin_amdgcn_readfirstlane(o0), tie_seen = 0;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-    const int i = base0 + 64 * u + lane;
-    const bool in = i < n;
-    const uint32_t kv = kvs[u];
-    const bool forced = in && (i < n_sink || i >= n - n_local);
-    const bool cand = kv != 0u;
-    const bool above = cand && (kv & mask) > prefix;
-    const bool tie = cand && (kv & mask) == prefix;
+  for (int u = 0; u < R; ++u) {
+    if (u >= ru) break;
+    const int i = idx[u];
+    const bool forced = i >= 0 && i < n && (i < n_sink || i >= n - n_local);
+    const bool above = code[u] > tau;
+    const bool tie = code[u] != 0u && code[u] == tau;
     const unsigned long long tmask = __ballot(tie);
     const uint32_t trank = tie_seen + rank_below(tmask);
     tie_seen += (uint32_t)__popcll(tmask);
@@ -152,13 +202,76 @@ __device__ __forceinline__ void wave_compact(const uint32_t* __restrict__ keys, 
       if (out_lds) out_lds[written + rank_below(smask)] = i;
     }
     written += (uint32_t)__popcll(smask);
-    }
   }
+  return written - o0;
+}
+
+// Register select of one segment of n <= 64 R keys by one wave (see the top
+// of the file). keys: the segment's keys in LDS.
+template <int R>
+__device__ __forceinline__ void wave_select_reg(const uint32_t* __restrict__ keys, int n, int k,
+                                                int n_sink, int n_local, int mode,
+                                                uint32_t rnd_word, int32_t* __restrict__ out,
+                                                int stride, int32_t* __restrict__ count_out,
+                                                int lane, int32_t* __restrict__ out_lds,
+                                                int32_t* __restrict__ count_lds) {
+  n = __builtin_amdgcn_readfirstlane(min(n, 64 * R));
+  k = __builtin_amdgcn_readfirstlane(k);
+  n_sink = __builtin_amdgcn_readfirstlane(n_sink);
+  n_local = __builtin_amdgcn_readfirstlane(n_local);
+  mode = __builtin_amdgcn_readfirstlane(mode);
+  const int nf = min(n, n_sink + n_local);  // forced: a prefix and a suffix of [0, n)
+  const int nc = n - nf;
+  const int kk = min(k, nc);
+  constexpr int ru = R;  // keys past n are 0: below every threshold, never counted
+  uint32_t code[R];
+  int32_t idx[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int i = 64 * u + lane;
+    idx[u] = i;
+    code[u] = i < n ? keys[i] : 0u;
+  }
+  // Defaults: kk == nc takes every candidate (codes > 0), kk == 0 none.
+  uint32_t tau = kk == nc ? 0u : 0xffffffffu, r = 0, off = 0, members = 0;
+  if (kk > 0 && kk < nc) {
+    int top = 31;  // odd: two bits per search step
+    if (mode == VX_TOPK_APPROX) {
+      // remap: candidates' scores onto 256 buckets, code = bucket + 1
+      uint32_t kmax = 0u, kminc = 0u;  // kminc: max of ~key, so min = ~kminc
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (code[u]) { kmax = max(kmax, code[u]); kminc = max(kminc, ~code[u]); }
+      const float mx = key_score(wave_max(kmax)), mn = key_score(~wave_max(kminc));
+      const float wdt = __fsub_rn(mx, mn);
+      const bool spread = wdt > 0.f;
+      const float inv = spread ? __fdiv_rn(256.f, wdt) : 0.f;
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        if (code[u]) {
+          uint32_t bk = 0;
+          if (spread) {
+            const float t = floorf(__fmul_rn(__fsub_rn(key_score(code[u]), mn), inv));
+            bk = t >= 255.f ? 255u : (uint32_t)t;
+          }
+          code[u] = bk + 1u;
+        }
+      }
+      top = 9;
+    }
+    tau = select_threshold<R>(code, ru, (uint32_t)kk, top);
+    const uint32_t above = count_ge<R>(code, ru, tau + 1u);
+    members = count_ge<R>(code, ru, tau) - above;
+    r = (uint32_t)kk - above;
+    off = (mode == VX_TOPK_APPROX && members) ? rnd_word % members : 0u;
+  }
+  const uint32_t total = reg_compact<R>(code, idx, ru, n, n_sink, n_local, tau, r, off, members,
+                                        out, out_lds, 0u);
   if (out)
-    for (int i = (int)written + lane; i < stride; i += 64) out[i] = -1;
+    for (int i = (int)total + lane; i < stride; i += 64) out[i] = -1;
   if (lane == 0) {
-    if (count_out) *count_out = (int32_t)written;
-    if (count_lds) *count_lds = (int32_t)written;
+    if (count_out) *count_out = (int32_t)total;
+    if (count_lds) *count_lds = (int32_t)total;
   }
 }
 
@@ -250,114 +363,96 @@ __device__ __forceinline__ void block_compact(const uint32_t* __restrict__ keys,
 
 }  // namespace topk_detail
 
-// Select for one segment whose n keys are already in this wave's LDS
-// (keys[i] = 0 for a forced page, else score_key of its score); `hist` is
-// 256 words of LDS. Writes out[0..stride) and *count_out, and, when given,
-// the chosen ids to out_lds[0..count) and the count to *count_lds.
-__device__ __forceinline__ void wave_select_keys(uint32_t* __restrict__ keys,
-                                                 uint32_t* __restrict__ hist, int n, int k,
+// Select for one segment of n <= kBlockSelectMin keys already in this
+// wave's LDS (keys[i] = 0 for a forced page, else score_key of its score).
+// Writes out[0..stride) and *count_out, and, when given, the chosen ids to
+// out_lds[0..count) and the count to *count_lds.
+__device__ __forceinline__ void wave_select_keys(const uint32_t* __restrict__ keys, int n, int k,
                                                  int n_sink, int n_local, int mode,
                                                  uint32_t rnd_word, int32_t* __restrict__ out,
                                                  int stride, int32_t* __restrict__ count_out,
                                                  int lane, int32_t* __restrict__ out_lds = nullptr,
                                                  int32_t* __restrict__ count_lds = nullptr) {
+  static_assert(kBlockSelectMin == 256, "four register keys per lane");
+  topk_detail::wave_select_reg<4>(keys, n, k, n_sink, n_local, mode, rnd_word, out, stride,
+                                  count_out, lane, out_lds, count_lds);
+}
+
+// Exact block select by local top-kk lists (see the top of the file): wave
+// w selects the kk best keys of its range of ceil(n / NW) <= 64 R1 keys, then
+// wave 0 selects kk of the NW kk <= 64 R2 candidates. hist: LDS for the
+// candidate ids. Called by every thread with 0 < kk < the candidate count.
+template <int NW, int R1, int R2>
+__device__ __forceinline__ void block_union_select(const uint32_t* __restrict__ keys,
+                                                   uint32_t* __restrict__ hist, int n, int kk,
+                                                   int n_sink, int n_local,
+                                                   int32_t* __restrict__ out, int stride,
+                                                   int32_t* __restrict__ count_out,
+                                                   int32_t* __restrict__ out_lds,
+                                                   int32_t* __restrict__ count_lds) {
   using namespace topk_detail;
-  const int nf = min(n, n_sink + n_local);  // forced: a prefix and a suffix of [0, n)
-  const int nc = n - nf;
-  const int kk = min(k, nc);
-
-  // Survivors: candidates with (key & mask) > prefix, plus `r` of those with
-  // (key & mask) == prefix taken in index order from offset `off` (cyclic
-  // over the `members` of that tie group).
-  uint32_t prefix = 0, mask = 0, r = (uint32_t)kk, off = 0, members = (uint32_t)nc;
-  if (kk > 0 && kk < nc) {
-    // smallest and largest candidate key (forced pages hold 0 and are skipped)
-    uint32_t kmax = 0u, kminc = 0u;  // kminc: max of ~key, so min = ~kminc
-    for (int base = 0; base < n; base += 64 * kU) {
-      uint32_t kv[kU];
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nf = min(n, n_sink + n_local);
+  const int per = (n + NW - 1) / NW;
+  // Local top kk of wave w's range [lo, hi): candidate ids to cand[w kk ..
+  // (w + 1) kk), in index order, -1 after the last.
+  int32_t* cand = (int32_t*)hist;
+  const int lo = min(n, w * per), hi = min(n, lo + per);
+  const int ru1 = R1 <= 2 ? R1 : (hi - lo + 63) / 64;  // keys past hi are 0, never counted
+  uint32_t kv[R1];
+  int32_t ix[R1];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i = base + 64 * u + lane;
-        kv[u] = i < n ? keys[i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (kv[u]) { kmax = max(kmax, kv[u]); kminc = max(kminc, ~kv[u]); }
-    }
-    kmax = wave_max(kmax);
-    const uint32_t kmin = ~wave_max(kminc);
-    if (mode == VX_TOPK_APPROX) {
-      const float mn = key_score(kmin), mx = key_score(kmax);
-      const float wdt = __fsub_rn(mx, mn);
-      const bool spread = wdt > 0.f;
-      const float inv = spread ? __fdiv_rn(256.f, wdt) : 0.f;
-      *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
-      wave_sync();
-      for (int base = 0; base < n; base += 64 * kU) {
-        uint32_t kv[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int i = base + 64 * u + lane;
-          kv[u] = i < n ? keys[i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int i = base + 64 * u + lane;
-          if (kv[u]) {
-            uint32_t bk = 0;
-            if (spread) {
-              const float t = floorf(__fmul_rn(__fsub_rn(key_score(kv[u]), mn), inv));
-              bk = t >= 255.f ? 255u : (uint32_t)t;
-            }
-            keys[i] = (bk << 24) | 1u;  // nonzero; digit 3 is the bucket
-            atomicAdd(&hist[bk], 1u);
-          }
-        }
-      }
-      wave_sync();
-      const Digit dg = find_digit(hist, r, lane);
-      prefix = dg.d << 24;
-      mask = 0xff000000u;
-      r -= dg.above;
-      members = dg.count;
-      off = members ? rnd_word % members : 0u;
-    } else if (kmin == kmax) {
-      prefix = kmin;  // every candidate ties: index order decides
-      mask = 0xffffffffu;
-    } else {
-      // Bytes every candidate shares need no pass: start at the first byte
-      // where the smallest and largest keys differ.
-      const int top = __clz(kmin ^ kmax) / 8;
-      mask = top ? 0xffffffffu << (32 - 8 * top) : 0u;
-      prefix = kmin & mask;
-      for (int shift = 24 - 8 * top; shift >= 0; shift -= 8) {
-        *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
-        wave_sync();
-        for (int base = 0; base < n; base += 64 * kU) {
-          uint32_t kv[kU];
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int i = base + 64 * u + lane;
-            kv[u] = i < n ? keys[i] : 0u;
-          }
-#pragma unroll
-          for (int u = 0; u < kU; ++u)
-            if (kv[u] && (kv[u] & mask) == prefix) atomicAdd(&hist[(kv[u] >> shift) & 255u], 1u);
-        }
-        wave_sync();
-        const Digit dg = find_digit(hist, r, lane);
-        prefix |= dg.d << shift;
-        mask |= 255u << shift;
-        r -= dg.above;
-        members = dg.count;
-        wave_sync();
-        if (dg.count == r) break;  // the whole bucket is needed: exact already
-      }
-    }
+  for (int u = 0; u < R1; ++u) {
+    const int i = lo + 64 * u + lane;
+    ix[u] = i;
+    kv[u] = (u < ru1 && i < hi) ? keys[i] : 0u;
   }
-
-  topk_detail::wave_compact(keys, n, n_sink, n_local, prefix, mask, r, off, members, out, stride,
-                            count_out, lane, out_lds, count_lds);
+  uint32_t tau = 0, rr = 0, mem = 0;  // fewer than kk candidates: take them all
+  if (count_ge<R1>(kv, ru1, 1u) > (uint32_t)kk) {
+    tau = select_threshold<R1>(kv, ru1, (uint32_t)kk, 31);
+    const uint32_t above = count_ge<R1>(kv, ru1, tau + 1u);
+    mem = count_ge<R1>(kv, ru1, tau) - above;
+    rr = (uint32_t)kk - above;
+  }
+  const uint32_t c = reg_compact<R1>(kv, ix, ru1, n, 0, 0, tau, rr, 0u, mem, nullptr,
+                                     cand + w * kk, 0u);
+  for (int j = (int)c + lane; j < kk; j += 64) cand[w * kk + j] = -1;
+  __syncthreads();
+  if (w != 0) return;
+  // One wave selects kk of the candidates; slot order is index order. The
+  // forced prefix [0, ns) and suffix [ss, n) frame them in the output.
+  const int nsl = NW * kk, ru2 = R2 <= 4 ? R2 : (nsl + 63) / 64;
+  uint32_t cv[R2];
+  int32_t cx[R2];
+#pragma unroll
+  for (int u = 0; u < R2; ++u) {
+    const int j = 64 * u + lane;
+    const int id = (u < ru2 && j < nsl) ? cand[j] : -1;
+    cx[u] = id;
+    cv[u] = id >= 0 ? keys[id] : 0u;
+  }
+  const uint32_t tau2 = select_threshold<R2>(cv, ru2, (uint32_t)kk, 31);
+  const uint32_t above2 = count_ge<R2>(cv, ru2, tau2 + 1u);
+  const uint32_t mem2 = count_ge<R2>(cv, ru2, tau2) - above2;
+  const int ns = min(n_sink, n), ss = max(ns, n - n_local);
+  reg_compact<R2>(cv, cx, ru2, n, 0, 0, tau2, (uint32_t)kk - above2, 0u, mem2, out, out_lds,
+                  (uint32_t)ns);
+  for (int i = lane; i < ns; i += 64) {
+    if (out) out[i] = i;
+    if (out_lds) out_lds[i] = i;
+  }
+  for (int i = ss + lane; i < n; i += 64) {
+    const int o = ns + kk + (i - ss);
+    if (out) out[o] = i;
+    if (out_lds) out_lds[o] = i;
+  }
+  const int total = nf + kk;
+  if (out)
+    for (int i = total + lane; i < stride; i += 64) out[i] = -1;
+  if (lane == 0) {
+    if (count_out) *count_out = (int32_t)total;
+    if (count_lds) *count_lds = (int32_t)total;
+  }
 }
 
 // Select for one segment with all NW waves of a block (every thread calls
@@ -376,10 +471,25 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
                                                   int32_t* __restrict__ out_lds = nullptr,
                                                   int32_t* __restrict__ count_lds = nullptr) {
   using namespace topk_detail;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  n = __builtin_amdgcn_readfirstlane(n);
+  k = __builtin_amdgcn_readfirstlane(k);
+  n_sink = __builtin_amdgcn_readfirstlane(n_sink);
+  n_local = __builtin_amdgcn_readfirstlane(n_local);
+  mode = __builtin_amdgcn_readfirstlane(mode);
   const int nf = min(n, n_sink + n_local);
   const int nc = n - nf;
   const int kk = min(k, nc);
+  const int per = (n + NW - 1) / NW;
+  if (mode == VX_TOPK_EXACT && kk > 0 && kk < nc && per <= 512 && NW * kk <= kSelectHistWords) {
+    if (per <= 128 && NW * kk <= 256)
+      block_union_select<NW, 2, 4>(keys, hist, n, kk, n_sink, n_local, out, stride, count_out,
+                                   out_lds, count_lds);
+    else
+      block_union_select<NW, 8, kSelectHistWords / 64>(keys, hist, n, kk, n_sink, n_local, out,
+                                                       stride, count_out, out_lds, count_lds);
+    return;
+  }
   uint32_t prefix = 0, mask = 0, r = (uint32_t)kk, off = 0, members = (uint32_t)nc;
   if (kk > 0 && kk < nc) {
     uint32_t kmax = 0u, kminc = 0u;
@@ -453,31 +563,29 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
                     count_out, out_lds, count_lds, red);
 }
 
-// Select for one segment: `sc` points at its n scores, `keys` / `hist` at
-// this wave's LDS (cap_keys + 256 words). Writes out[0..stride) and *count_out.
-__device__ __forceinline__ void wave_select(uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
-                                            int cap_keys, const float* __restrict__ sc, int n, int k,
-                                            int n_sink, int n_local, int mode, uint32_t rnd_word,
+// Select for one segment: `sc` points at its n scores, `keys` at this
+// wave's LDS (cap_keys words, cap_keys <= kBlockSelectMin). Writes
+// out[0..stride) and *count_out.
+__device__ __forceinline__ void wave_select(uint32_t* __restrict__ keys, int cap_keys,
+                                            const float* __restrict__ sc, int n, int k, int n_sink,
+                                            int n_local, int mode, uint32_t rnd_word,
                                             int32_t* __restrict__ out, int stride,
                                             int32_t* __restrict__ count_out, int lane) {
   using namespace topk_detail;
   n = n > cap_keys ? cap_keys : n;  // a wrong host max_pages must not overrun LDS
-  // Load the segment 8 elements per lane at a time (all loads in flight).
-  for (int base = 0; base < n; base += 64 * kU) {
-    float v[kU];
+  float v[kBlockSelectMin / 64];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = base + 64 * u + lane;
-      v[u] = i < n ? sc[i] : 0.f;
-    }
+  for (int u = 0; u < kBlockSelectMin / 64; ++u) {
+    const int i = 64 * u + lane;
+    v[u] = i < n ? sc[i] : 0.f;
+  }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = base + 64 * u + lane;
-      if (i < n) keys[i] = (i < n_sink || i >= n - n_local) ? 0u : score_key(v[u]);
-    }
+  for (int u = 0; u < kBlockSelectMin / 64; ++u) {
+    const int i = 64 * u + lane;
+    if (i < n) keys[i] = (i < n_sink || i >= n - n_local) ? 0u : score_key(v[u]);
   }
   wave_sync();
-  wave_select_keys(keys, hist, n, k, n_sink, n_local, mode, rnd_word, out, stride, count_out, lane);
+  wave_select_keys(keys, n, k, n_sink, n_local, mode, rnd_word, out, stride, count_out, lane);
 }
 
 }  // namespace vx

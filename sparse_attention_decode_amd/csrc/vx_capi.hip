@@ -100,7 +100,7 @@ vx_status check_topk(const vx_pages* p, int32_t k, int32_t n_sink, int32_t n_loc
 // segments as fit 64 KB, at most 4.
 int topk_waves(int max_pages) {
   const int cap_keys = (max_pages + 63) / 64 * 64;
-  const int wpb = (int)(65536 / ((size_t)(cap_keys + 256) * 4));
+  const int wpb = (int)(65536 / ((size_t)cap_keys * 4));
   return wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
 }
 

@@ -69,11 +69,15 @@ def run_topk(ns, scores, hkv, k, n_sink, n_local, mode, rnd):
 
 
 @pytest.mark.parametrize("k,n_sink,n_local", [(16, 1, 1), (8, 0, 1), (128, 1, 2), (64, 0, 0),
-                                              (0, 1, 1), (1, 0, 0), (5, 3, 3)])
+                                              (0, 1, 1), (1, 0, 0), (5, 3, 3), (96, 2, 2)])
 @pytest.mark.parametrize("mode", [V.VX_TOPK_EXACT, V.VX_TOPK_APPROX])
-def test_topk_bit_exact(k, n_sink, n_local, mode):
+@pytest.mark.parametrize("max_n", [250, 2100])
+def test_topk_bit_exact(k, n_sink, n_local, mode, max_n):
+    """max_n 250: one wave per segment (register select); 2100: one block per
+    segment (local top-k per wave then one wave over the candidates for
+    k <= 96, digit passes for k = 128)."""
     hkv, batch = 3, 9
-    ns, scores = segments(1000 + k, batch, hkv, max_n=2100)
+    ns, scores = segments(1000 + k + max_n, batch, hkv, max_n=max_n)
     rnd = np.random.default_rng(k).integers(0, 2**32, size=(batch, hkv), dtype=np.uint64).astype(np.uint32)
     sel, cnt = run_topk(ns, scores, hkv, k, n_sink, n_local, mode, rnd)
     for b in range(batch):
@@ -90,11 +94,14 @@ def test_topk_bit_exact(k, n_sink, n_local, mode):
             assert cnt[b, g] == int((want >= 0).sum())
 
 
-def test_topk_large_segments():
-    """Long segments (one block per segment) next to a 3-page one."""
+@pytest.mark.parametrize("ns", [(5000, 3, 4100), (4000, 3, 2900)])
+def test_topk_large_segments(ns):
+    """Long segments (one block per segment) next to a 3-page one; up to 4096
+    pages the waves' ranges fit their registers (local top-k then one wave
+    over the candidates), beyond that the digit passes run."""
     hkv, batch = 2, 3
     rng = np.random.default_rng(5)
-    ns = np.array([5000, 3, 4100])
+    ns = np.array(ns)
     scores = [rng.standard_normal(ns[b]).astype(np.float32) for b in range(batch) for _ in range(hkv)]
     rnd = np.zeros((batch, hkv), dtype=np.uint32)
     sel, cnt = run_topk(ns, scores, hkv, 64, 1, 1, V.VX_TOPK_EXACT, rnd)
