@@ -9,6 +9,7 @@
  *                  top-k pages per (sequence, KV head)        -> vx_topk_pages
  *                  both, fused with the newest-page refresh   -> vx_index_pages
  *   whole step     indexer + attention, fused where possible  -> vx_decode_step
+ *                  the same, without a workspace argument     -> vx_decode_step_static
  *   attention      exact softmax over the selected pages      -> vx_sparse_decode
  * Section "System design > 2. vTensor" gives the paged layout (a tensor with
  * batch size, a pointer array and a page-index structure): vx_pages below.
@@ -298,6 +299,30 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom,
                          int32_t* sel_count, float* out, float* lse,
                          int32_t num_splits, void* workspace,
                          size_t* workspace_bytes, hipStream_t stream);
+
+/* vx_decode_step for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments and results (the same kernels and bits) as vx_decode_step, with
+ * no workspace argument: the split partials live in a 16 MiB scratch array
+ * inside the library, one per device, which each device holds until the
+ * process ends. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that
+ * device's scratch address. A step whose partials need more than 16 MiB
+ * (batch * num_q_heads * splits * (head_dim_v + 2) * 4 bytes, split steps
+ * only) returns VX_ERR_WORKSPACE before any launch. Every call on one device
+ * shares its scratch, so calls that overlap on one device (different streams
+ * or threads) race; calls ordered on one stream do not. The scratch needs
+ * no setup: a call writes every partial it reads. */
+vx_status vx_decode_step_static(const vx_pages* pages, const vx_geom* geom,
+                                const void* q, const void* k_pool,
+                                const void* v_pool, float* centroids,
+                                void* cent_bf16, int32_t refresh_newest,
+                                float score_scale, float sm_scale, int32_t k,
+                                int32_t n_sink, int32_t n_local, int32_t mode,
+                                const uint32_t* rand_u32, float* scores,
+                                int32_t* sel, int32_t sel_stride,
+                                int32_t* sel_count, float* out, float* lse,
+                                int32_t num_splits, hipStream_t stream);
 
 /* The whole step with the Quest-style indexer (GQA only; the mechanism is
  * Quest's, the other baseline of the Vortex paper note, "Paper context" and

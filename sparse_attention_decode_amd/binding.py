@@ -18,7 +18,7 @@ __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
     "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
     "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
-    "vx_bound_scores", "vx_bound_decode_step", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
+    "vx_bound_scores", "vx_bound_decode_step", "vx_decode_step_static", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
 
@@ -27,7 +27,8 @@ VX_F32, VX_BF16 = 0, 1
 VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
 ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
                 "vx_bounds_update", "vx_bound_scores", "vx_bound_decode_step",
-                "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_status_string", "vx_last_error", "vx_abi_version")
+                "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static", "vx_plan_decode",
+                "vx_status_string", "vx_last_error", "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
 
@@ -90,6 +91,11 @@ def load() -> ctypes.CDLL:
                                    c_float, c_float, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                    c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                    c_int32, c_void_p, POINTER(c_size_t), c_void_p]
+    lib.vx_decode_step_static.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_int32, c_float, c_float, c_int32, c_int32,
+                                          c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                          c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                          c_void_p]
     lib.vx_plan_decode.argtypes = [P, G, c_int32, c_int32, c_int32, POINTER(VxPlan)]
     lib.vx_bounds_update.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.vx_bound_scores.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_int32, c_float,
@@ -100,8 +106,8 @@ def load() -> ctypes.CDLL:
                                          c_void_p, c_void_p, c_int32, c_void_p,
                                          POINTER(c_size_t), c_void_p]
     for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-                 "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
-                 "vx_bound_scores", "vx_bound_decode_step"):
+                 "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static", "vx_plan_decode",
+                 "vx_bounds_update", "vx_bound_scores", "vx_bound_decode_step"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -233,6 +239,21 @@ def vx_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, centroids, c
                                  sel_stride, _ptr(sel_count), _ptr(out), _ptr(lse), num_splits,
                                  _ptr(workspace), ctypes.byref(nbytes), _stream(stream)))
     return nbytes.value
+
+
+def vx_decode_step_static(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, centroids, cent_bf16,
+                          refresh_newest: bool, score_scale: float, sm_scale: float, k: int,
+                          n_sink: int, n_local: int, mode: int, rand_u32, scores, sel,
+                          sel_stride: int, sel_count, out, lse, num_splits: int = 0,
+                          stream=None) -> None:
+    """vx_decode_step with the library's own scratch (no workspace argument)."""
+    _check(load().vx_decode_step_static(ctypes.byref(pages), ctypes.byref(geom), _ptr(q),
+                                        _ptr(k_pool), _ptr(v_pool), _ptr(centroids),
+                                        _ptr(cent_bf16), int(refresh_newest), float(score_scale),
+                                        float(sm_scale), k, n_sink, n_local, mode,
+                                        _ptr(rand_u32), _ptr(scores), _ptr(sel), sel_stride,
+                                        _ptr(sel_count), _ptr(out), _ptr(lse), num_splits,
+                                        _stream(stream)))
 
 
 def vx_bound_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, bounds,

@@ -253,11 +253,37 @@ void split_buffers(const vx_pages* p, const vx_geom* g, int S, void* ws, float**
                                            256));
 }
 
+// Scratch memory of vx_decode_step_static: the split partials of a step,
+// in a file-scope device array instead of a caller's workspace. Each device
+// that loads the library holds its own copy until the process ends. Host
+// code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and kept per device.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+void* g_scratch[64];  // per-device address of `scratch`, null until looked up
+
+vx_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  VX_CHECK(dev >= 0 && dev < 64, VX_ERR_UNSUPPORTED, "device %d (supported: 0..63)", dev);
+  void* p = __atomic_load_n(&g_scratch[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    VX_CHECK(p, VX_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    __atomic_store_n(&g_scratch[dev], p, __ATOMIC_RELEASE);
+  }
+  *out = p;
+  return VX_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 4; }
+int32_t vx_abi_version(void) { return 5; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {
@@ -533,6 +559,43 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
     return st;
   return vx_sparse_decode(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
                           out, lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+vx_status vx_decode_step_static(const vx_pages* pages, const vx_geom* geom, const void* q,
+                                const void* k_pool, const void* v_pool, float* centroids,
+                                void* cent_bf16, int32_t refresh_newest, float score_scale,
+                                float sm_scale, int32_t k, int32_t n_sink, int32_t n_local,
+                                int32_t mode, const uint32_t* rand_u32, float* scores,
+                                int32_t* sel, int32_t sel_stride, int32_t* sel_count, float* out,
+                                float* lse, int32_t num_splits, hipStream_t stream) {
+  vx_status st;
+  // Every argument check of a launching vx_decode_step, before any HIP call.
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  if ((st = check_geom(geom)) != VX_OK) return st;
+  if ((st = check_decode_args(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
+                              out, true)) != VX_OK)
+    return st;
+  if ((st = check_index_args(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
+                             score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,
+                             sel_stride, sel_count)) != VX_OK)
+    return st;
+  size_t need = 0;
+  // Size query of the same call (host only, no launch), then the limit.
+  if ((st = vx_decode_step(pages, geom, q, k_pool, v_pool, centroids, cent_bf16, refresh_newest,
+                           score_scale, sm_scale, k, n_sink, n_local, mode, rand_u32, scores,
+                           sel, sel_stride, sel_count, out, lse, num_splits, nullptr, &need,
+                           stream)) != VX_OK)
+    return st;
+  VX_CHECK(need <= kStaticScratchBytes, VX_ERR_WORKSPACE,
+           "this step needs %zu bytes of scratch; the static scratch holds %zu (fewer splits or "
+           "a smaller batch fit, or call vx_decode_step with a workspace)",
+           need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != VX_OK) return st;
+  size_t have = kStaticScratchBytes;
+  return vx_decode_step(pages, geom, q, k_pool, v_pool, centroids, cent_bf16, refresh_newest,
+                        score_scale, sm_scale, k, n_sink, n_local, mode, rand_u32, scores, sel,
+                        sel_stride, sel_count, out, lse, num_splits, ws, &have, stream);
 }
 
 vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom, const void* q,

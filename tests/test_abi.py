@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 4
+    assert lib.vx_abi_version() == 5
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -228,6 +228,33 @@ def test_decode_step_argument_checks():
     assert call(out=None) == V.VX_ERR_INVALID_ARG
     assert call(scores=None) == V.VX_ERR_INVALID_ARG
     assert call(centroids=None) == V.VX_ERR_INVALID_ARG
+    assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
+    assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
+
+
+def test_static_decode_step_argument_checks():
+    """vx_decode_step_static runs vx_decode_step's checks before any HIP call
+    (it has no workspace to query or check)."""
+    p, g = pages(), geom()
+    ok = dict(q=BAD, k_pool=BAD, v_pool=BAD, centroids=BAD, cent_bf16=None, refresh=1, sscale=1.0,
+              smscale=1.0, k=4, n_sink=1, n_local=1, mode=0, rand_u32=None, scores=BAD, sel=BAD,
+              stride=6, count=BAD, out=BAD, lse=None, splits=0, pages=p, geom=g)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return status_of(V.vx_decode_step_static, a["pages"], a["geom"], a["q"], a["k_pool"],
+                         a["v_pool"], a["centroids"], a["cent_bf16"], a["refresh"], a["sscale"],
+                         a["smscale"], a["k"], a["n_sink"], a["n_local"], a["mode"],
+                         a["rand_u32"], a["scores"], a["sel"], a["stride"], a["count"], a["out"],
+                         a["lse"], a["splits"], stream=0)
+
+    assert call(refresh=2) == V.VX_ERR_INVALID_ARG
+    assert call(sscale=float("nan")) == V.VX_ERR_INVALID_ARG
+    assert call(stride=5) == V.VX_ERR_INVALID_ARG
+    assert call(mode=1) == V.VX_ERR_INVALID_ARG
+    assert call(v_pool=None) == V.VX_ERR_INVALID_ARG
+    assert call(out=None) == V.VX_ERR_INVALID_ARG
+    assert call(scores=None) == V.VX_ERR_INVALID_ARG
     assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
     assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
 
