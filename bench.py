@@ -53,8 +53,11 @@ def parse():
                     help="bounds: the Quest-style page-bounds indexer (GQA workloads)")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 1 GB touched")
     ap.add_argument("--stage-reps", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="measure only --workload (by default the other workloads are measured "
+                         "in the same run and reported under \"workloads\")")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -101,41 +104,102 @@ def refresh_bytes(w):
     return int(sum(nv)) * s.num_kv_heads * s.head_dim_k * kv_elt
 
 
-def cpu_baseline(w, step, seconds):
-    """The oracle as it stands, single-threaded, on whole sequences of the same
-    workload, passing over the batch until `seconds` of CPU work have run."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_worker(args):
+    """One CPU worker (a fresh process): the oracle's whole step over the
+    sequences stored under `d`, round-robin from `first`, until `seconds`
+    of work have run. Returns (sequence-steps, KV tokens attended, seconds)."""
+    d, names, first, seconds, kw = args
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from threadpoolctl import threadpool_limits
+    sys.path.insert(0, ROOT)
     from oracle import vx_oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover
-        limiter = None
-    s = w.spec
-    done, t_total, seqs = 0, 0.0, {}
-    try:
-        while t_total < seconds and done < 1024 * s.batch:
-            b = done % s.batch
-            if b not in seqs:
-                seqs[b] = w.host_sequence(b)  # host copy, outside the timed part
+    seqs = []
+    for n in names:
+        z = np.load(os.path.join(d, n + ".npz"))
+        seqs.append({"q": z["q"].astype(np.float64), "k": z["k"].astype(np.float64),
+                     "v": z["v"].astype(np.float64) if z["v"].size else None,
+                     "seq_len": int(z["seq_len"]), "rand_u32": z["rand_u32"]})
+    P, H = kw["page_size"], kw["num_kv_heads"]
+    done, tokens, busy = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        i = first
+        while busy < seconds:
+            seq = seqs[i % len(seqs)]
             t0 = time.perf_counter()
-            O.decode_sequence(seqs[b], page_size=s.page_size, num_kv_heads=s.num_kv_heads,
-                              k=step.k, n_sink=step.n_sink, n_local=step.n_local,
-                              score_scale=step.score_scale, sm_scale=step.sm_scale, mla=s.mla,
-                              head_dim_v=s.head_dim_v, approx=step.mode == 1,
-                              indexer=step.indexer)
-            t_total += time.perf_counter() - t0
+            r = O.decode_sequence(seq, **kw)
+            busy += time.perf_counter() - t0
+            L = seq["seq_len"]
+            ids = r["sel"][r["sel"] >= 0].astype(np.int64)
+            tokens += int(np.clip(L - ids * P, 0, P).sum())
             done += 1
-            if len(seqs) > 8:
-                seqs.pop(next(iter(seqs)))
+            i += 1
+    return done, tokens / H, busy
+
+
+def cpu_baseline(w, step, seconds):
+    """The oracle as it stands (oracle/vx_oracle.py, numpy fp64) on the host
+    cores, over whole sequences of the same workload: first one worker per
+    host core the process may use (at most 16, the host share of one GPU),
+    then a single worker, each for about `seconds` of work. Each
+    sequence-step is the oracle's decode_sequence: it rebuilds the centroid
+    of every page of the sequence (the GPU step refreshes only the newest
+    page's), then scores, selects and attends."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    s = w.spec
+    nseq = min(s.batch, 8)
+    d = tempfile.mkdtemp(prefix="vx_cpu_")
+    try:
+        names = []
+        for b in range(nseq):
+            q = w.host_sequence(b)
+            np.savez(os.path.join(d, f"s{b}.npz"), q=q["q"].astype(np.float32),
+                     k=q["k"].astype(np.float32),
+                     v=(q["v"].astype(np.float32) if q["v"] is not None else np.zeros(0)),
+                     seq_len=q["seq_len"], rand_u32=q["rand_u32"])
+            names.append(f"s{b}")
+        kw = dict(page_size=s.page_size, num_kv_heads=s.num_kv_heads, k=step.k,
+                  n_sink=step.n_sink, n_local=step.n_local, score_scale=step.score_scale,
+                  sm_scale=step.sm_scale, mla=s.mla, head_dim_v=s.head_dim_v,
+                  approx=step.mode == 1, indexer=step.indexer)
+        cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+        ctx = mp.get_context("spawn")  # no fork of a process that holds the GPU
+        res = {}
+        for label, nw in (("all", cores), ("one", 1)):
+            with ctx.Pool(nw) as pool:
+                out = pool.map(_oracle_worker,
+                               [(d, names, i, seconds, kw) for i in range(nw)])
+            done = sum(o[0] for o in out)
+            res[label] = {"seqs_per_s": sum(o[0] / o[2] for o in out),
+                          "kv_tokens_per_s": sum(o[1] / o[2] for o in out),
+                          "sequence_steps": done, "workers": nw}
     finally:
-        if limiter is not None:
-            limiter.restore_original_limits()
-    distinct = min(done, s.batch)
-    return {"value": done / t_total, "unit": "seqs/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence-steps over {distinct} distinct sequences of the same "
-                      f"workload (whole step each: {'page bounds' if step.indexer == 'bounds' else 'centroids'}, "
-                      f"scores, selection, attention), "
-                      f"numpy fp64, one thread, {t_total:.1f} s"}
+        shutil.rmtree(d, ignore_errors=True)
+    one = res["one"]
+    return {"value": res["all"]["seqs_per_s"], "unit": "seqs/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "kv_tokens_per_s": res["all"]["kv_tokens_per_s"],
+            "one_core": {"value": one["seqs_per_s"], "unit": "seqs/s", "cores": 1,
+                         "kv_tokens_per_s": one["kv_tokens_per_s"]},
+            "sample": f"{res['all']['sequence_steps']} sequence-steps on {cores} worker processes "
+                      f"(one numpy thread each, about {seconds:.0f} s of work per worker), then "
+                      f"{one['sequence_steps']} on one, over the first {nseq} sequences of the same "
+                      f"workload; each sequence-step is the oracle's whole step: the "
+                      f"{'page bounds' if step.indexer == 'bounds' else 'centroids'} of every page "
+                      f"rebuilt (the GPU step refreshes only the newest page's), then scores, "
+                      f"selection and attention, in fp64"}
 
 
 def sources_hash():
@@ -200,10 +264,10 @@ def profile_commands(run):
     wl = run[:-len("_bounds")] if bounds else run
     flags = f"--workload {wl}{' --indexer bounds' if bounds else ''}"
     cmds = [f"rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{run}_trace -o run -- "
-            f"python3 $R/bench.py {flags} --steps 50 --warmup 5 --stage-reps 5 --no-cpu-baseline"]
+            f"python3 $R/bench.py {flags} --steps 50 --warmup 5 --stage-reps 5 --no-cpu-baseline --no-extras"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d $OUT/{run}_{c} -o run "
-                    f"-- python3 $R/bench.py {flags} --steps 8 --warmup 2 --stage-reps 1 --no-cpu-baseline")
+                    f"-- python3 $R/bench.py {flags} --steps 8 --warmup 2 --stage-reps 1 --no-cpu-baseline --no-extras")
     return cmds
 
 
@@ -316,7 +380,7 @@ def summarize_profiles(out, commit):
                       f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES "
                       f"SQ_INSTS_MFMA --kernel-trace --output-format csv -d $OUT/{run}_MFMA -o run -- "
                       f"python3 $R/bench.py --workload {wl} --steps 8 --warmup 2 --stage-reps 1 "
-                      f"--no-cpu-baseline", "```", "",
+                      f"--no-cpu-baseline --no-extras", "```", "",
                       "| kernel | mean us (under counters) | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES "
                       "| SQ_BUSY_CU_CYCLES | MFMA busy / CU busy |", "|---|---|---|---|---|---|"]
             for k in sorted(vals):
@@ -505,6 +569,204 @@ def dense_compare(a):
     print(json.dumps(res), flush=True)
 
 
+# The workload each default run also measures beside the headline one, so
+# every configuration's step is timed in the same run; the long-generation
+# workload's step appends a token (K/V slot write + that page's centroid),
+# and the two large ones also report the indexer in exact and approximate
+# top-k mode.
+EXTRA_WORKLOADS = ("mla_bf16", "longgen_bf16", "largebatch_bf16", "tiny_fp32")
+APPEND_WORKLOADS = ("longgen_bf16",)
+INDEX_MODE_WORKLOADS = ("longgen_bf16", "largebatch_bf16")
+
+
+class Bench:
+    """The replicas of one workload, their step graphs and timings."""
+
+    def __init__(self, name, mode, indexer, replicas, append):
+        import torch
+        from sparse_attention_decode_amd import workloads as W
+        from sparse_attention_decode_amd.step import DecodeStep
+        self.name, self.mode, self.indexer, self.append = name, mode, indexer, append
+        sp = W.spec(name)
+        self.spec = sp
+        log(f"workload {name}: generating on cuda:0")
+        w0 = W.make(sp, "cuda", seed=0)
+        base = DecodeStep(w0, mode=mode, indexer=indexer)
+        base.rebuild()
+        self.run_fn = (lambda st: st.run_append()) if append else (lambda st: st.run())
+        self.run_fn(base)
+        torch.cuda.synchronize()
+        self.w0, self.base = w0, base
+        self.cent_b, self.kv_b, self.tokens = step_bytes(w0, base)
+        self.plan = base.plan()
+        total = self.cent_b + self.kv_b
+        self.R = replicas or max(1, min(16, math.ceil(1.0e9 / total)))
+        log(f"step touches {total / 1e6:.1f} MB (centroids {self.cent_b / 1e6:.1f}, selected KV "
+            f"{self.kv_b / 1e6:.1f}); {self.R} replica(s)")
+        self.ws, self.steps = [w0], [base]
+        for _ in range(self.R - 1):
+            w = w0.replicate()
+            st = DecodeStep(w, mode=mode, indexer=indexer)
+            st.rebuild()
+            self.ws.append(w)
+            self.steps.append(st)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.Stream()
+        self.stream.wait_stream(torch.cuda.current_stream())
+
+    def capture(self, fn):
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            for st in self.steps:  # one eager pass before capture
+                fn(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=self.stream, capture_error_mode="thread_local"):
+            for st in self.steps:
+                fn(st)
+        torch.cuda.synchronize()
+        return g
+
+    def time_step(self, steps, warmup):
+        """us per step over `steps` steps (graph replays of all replicas, then
+        single-replica graphs for the remainder), timed with HIP events on
+        the replay stream between two synchronisations."""
+        import torch
+        g_step = self.capture(self.run_fn)
+        singles = []
+        for st in self.steps:
+            g1 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1, stream=self.stream, capture_error_mode="thread_local"):
+                self.run_fn(st)
+            singles.append(g1)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            for _ in range(max(1, warmup // self.R)):
+                g_step.replay()
+        torch.cuda.synchronize()
+        full, rem = divmod(steps, self.R)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.stream):
+            ev0.record(self.stream)
+            for _ in range(full):
+                g_step.replay()
+            for i in range(rem):
+                singles[i].replay()
+            ev1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        us = ev0.elapsed_time(ev1) * 1e3 / steps
+        log(f"{self.name}: {steps} steps: {us:.2f} us/step (host wall {wall * 1e6 / steps:.2f} us)")
+        return us
+
+    def time_stage(self, fn, reps):
+        """us per call of fn (graph replays of every replica, HIP events on the
+        replay stream)."""
+        import torch
+        g = self.capture(fn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            g.replay()
+            e0.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * self.R)
+
+    def stages(self, full):
+        """The stage functions to time: every stage for the headline workload,
+        otherwise those the roofline needs."""
+        if self.indexer == "bounds":
+            st = {"decode_step": lambda x: x.bound_step(),
+                  "indexer": lambda x: (x.bound_score(refresh=True), x.select()),
+                  "attention_merge": lambda x: x.attend()}
+            if full:
+                st.update({"cache_refresh": lambda x: x.refresh_bounds(),
+                           "page_scores": lambda x: x.bound_score(),
+                           "bound_scores_refresh": lambda x: x.bound_score(refresh=True),
+                           "topk": lambda x: x.select()})
+            return st
+        refresh = not self.append
+        st = {"decode_step": lambda x: x.step(refresh=refresh),
+              "indexer": lambda x: x.index(refresh=refresh),
+              "attention_merge": lambda x: x.attend()}
+        if self.append:
+            st["append_kv"] = lambda x: x.append_kv()
+        if full:
+            st.update({"cache_refresh": lambda x: x.refresh_centroids(),
+                       "page_scores": lambda x: x.score(),
+                       "topk": lambda x: x.select()})
+        return st
+
+    def record(self, a, full):
+        """One workload's measurements: the step, its stages and the roofline
+        of its dominant kernel stage."""
+        us = self.time_step(a.steps, a.warmup)
+        stage_us = {k: self.time_stage(fn, a.stage_reps) for k, fn in self.stages(full).items()}
+        log(f"{self.name}: stage us: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+        s = self.spec
+        t_step = us * 1e-6
+        total = self.cent_b + self.kv_b
+        ref_b = 0 if self.append else refresh_bytes(self.w0)
+        stage_bytes = {"decode_step": self.cent_b + ref_b + self.kv_b,
+                       "indexer": self.cent_b + ref_b, "page_scores": self.cent_b,
+                       "bound_scores_refresh": self.cent_b + refresh_bytes(self.w0),
+                       "attention_merge": self.kv_b}
+        stage_bytes = {k: v for k, v in stage_bytes.items() if k in stage_us}
+        # One kernel per step when the plan fuses it; otherwise the indexer and
+        # the attention (+ merge) run in turn and the slower is dominant.
+        if self.plan["fused_step"]:
+            dom = "decode_step"
+        else:
+            dom = max(("indexer", "attention_merge"), key=lambda k: stage_us[k])
+        achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+        run = self.name + ("_bounds" if self.indexer == "bounds" else "")
+        rec = {"workload": f"{self.name}: {DESCR[self.name]}",
+               "ms_per_step": us / 1e3, "seqs_per_s": s.batch / t_step,
+               "kv_tokens_per_s": self.tokens / s.num_kv_heads / t_step,
+               "step_bytes": total, "step_hbm_GBps": total / t_step / 1e9,
+               "step_frac_of_peak": total / t_step / 1e9 / PEAK_GBPS,
+               "replicas": self.R, "num_splits": self.plan["num_splits"],
+               "fused_step": bool(self.plan["fused_step"]), "appends_token": self.append,
+               "stage_us": stage_us,
+               "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
+               "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS,
+                            "unit": "GB/s", "frac": achieved / PEAK_GBPS,
+                            "traffic": measured_traffic(run, dom), "kernel": dom,
+                            "bytes_per_launch": stage_bytes[dom]}}
+        return rec
+
+    def free(self):
+        import torch
+        del self.steps, self.ws, self.base, self.w0
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def index_modes(name, a):
+    """The indexer stage (vx_index_pages) in exact and in approximate top-k
+    mode on the same workload, with the approximate selection's recall@k
+    against the exact one on the same scores."""
+    from sparse_attention_decode_amd import binding as V
+    out = {}
+    for label, mode in (("exact", V.VX_TOPK_EXACT), ("approx", V.VX_TOPK_APPROX)):
+        b = Bench(name, mode, "centroid", a.replicas, False)
+        out[f"indexer_us_{label}"] = b.time_stage(lambda x: x.index(), a.stage_reps)
+        out[f"topk_us_{label}"] = b.time_stage(lambda x: x.select(), a.stage_reps)
+        if mode == V.VX_TOPK_APPROX:
+            out["approx_recall_at_k"] = approx_recall(b.w0, b.base)
+        b.free()
+    out["indexer_speedup_approx"] = out["indexer_us_exact"] / out["indexer_us_approx"]
+    out["topk_speedup_approx"] = out["topk_us_exact"] / out["topk_us_approx"]
+    log(f"{name}: indexer exact {out['indexer_us_exact']:.2f} us, approx "
+        f"{out['indexer_us_approx']:.2f} us; top-k alone {out['topk_us_exact']:.2f} / "
+        f"{out['topk_us_approx']:.2f} us; recall@k {out['approx_recall_at_k']['mean']:.4f}")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -527,24 +789,18 @@ def main():
         return
 
     from sparse_attention_decode_amd import binding as V
-    from sparse_attention_decode_amd import workloads as W
-    from sparse_attention_decode_amd.step import DecodeStep
 
     torch.cuda.set_device(0)
     mode = V.VX_TOPK_APPROX if a.mode == "approx" else V.VX_TOPK_EXACT
+    from sparse_attention_decode_amd import workloads as W
     sp = W.spec(a.workload)
     bounds = a.indexer == "bounds"
     if bounds and sp.mla:
         print("the bounds indexer is implemented for GQA workloads only", file=sys.stderr)
         sys.exit(2)
-    log(f"workload {a.workload}: generating on cuda:0")
-    w0 = W.make(sp, "cuda", seed=0)
-    base = DecodeStep(w0, mode=mode, indexer=a.indexer)
-    base.rebuild()
-    base.run()
-    torch.cuda.synchronize()
-    cent_b, kv_b, tokens = step_bytes(w0, base)
-    plan = base.plan()
+    append = a.workload in APPEND_WORKLOADS and not bounds
+    main_b = Bench(a.workload, mode, a.indexer, a.replicas, append)
+    w0, base = main_b.w0, main_b.base
     recall = approx_recall(w0, base) if mode == V.VX_TOPK_APPROX else None
     if recall:
         log(f"approximate top-k recall@k: mean {recall['mean']:.4f}, min {recall['min']:.4f} "
@@ -555,6 +811,7 @@ def main():
             f"min {rope['min']:.4f}")
     quality = None
     if bounds:
+        from sparse_attention_decode_amd.step import DecodeStep
         cent = DecodeStep(w0, mode=mode)
         cent.rebuild()
         cent.run()
@@ -568,147 +825,35 @@ def main():
             f"{quality['attention_mass_centroid']['mean']:.4f}; selection overlap "
             f"{quality['overlap_with_centroid']['mean']:.4f}")
         del cent
-    total_b = cent_b + kv_b
-    R = a.replicas or max(1, min(16, math.ceil(1.0e9 / total_b)))
-    log(f"step touches {total_b / 1e6:.1f} MB (centroids {cent_b / 1e6:.1f}, selected KV "
-        f"{kv_b / 1e6:.1f}); {R} replica(s)")
-    ws, steps = [w0], [base]
-    for _ in range(R - 1):
-        w = w0.replicate()
-        st = DecodeStep(w, mode=mode, indexer=a.indexer)
-        st.rebuild()
-        ws.append(w)
-        steps.append(st)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-
-    def capture(fn_per_replica):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for st in steps:  # one eager pass before capture
-                fn_per_replica(st)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=stream, capture_error_mode="thread_local"):
-            for st in steps:
-                fn_per_replica(st)
-        torch.cuda.synchronize()
-        return g
-
-    g_step = capture(lambda st: st.run())
-    # single-replica graphs for a remainder of K not divisible by R
-    singles = []
-    for st in steps:
-        g1 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g1, stream=stream, capture_error_mode="thread_local"):
-            st.run()
-        singles.append(g1)
-    torch.cuda.synchronize()
-
-    with torch.cuda.stream(stream):
-        for i in range(max(1, a.warmup // R)):
-            g_step.replay()
-    torch.cuda.synchronize()
-    full, rem = divmod(a.steps, R)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for i in range(full):
-            g_step.replay()
-        for i in range(rem):
-            singles[i].replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / a.steps
-    log(f"{a.steps} steps: {ms_step * 1e3:.2f} us/step (host wall {wall * 1e3 / a.steps * 1e3:.2f} us)")
-
-    # per-stage durations (each stage alone, graph replays of all replicas)
-    if bounds:
-        stages = {
-            "decode_step": lambda st: st.bound_step(),
-            "indexer": lambda st: (st.bound_score(refresh=True), st.select()),
-            "cache_refresh": lambda st: st.refresh_bounds(),
-            "page_scores": lambda st: st.bound_score(),
-            "bound_scores_refresh": lambda st: st.bound_score(refresh=True),
-            "topk": lambda st: st.select(),
-            "attention_merge": lambda st: st.attend(),
-        }
-    else:
-        stages = {
-            "decode_step": lambda st: st.step(),
-            "indexer": lambda st: st.index(),
-            "cache_refresh": lambda st: st.refresh_centroids(),
-            "page_scores": lambda st: st.score(),
-            "topk": lambda st: st.select(),
-            "attention_merge": lambda st: st.attend(),
-        }
-    stage_us = {}
-    for name, fn in stages.items():
-        g = capture(fn)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            g.replay()
-            e0.record(stream)
-            for _ in range(a.stage_reps):
-                g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        stage_us[name] = e0.elapsed_time(e1) * 1e3 / (a.stage_reps * R)
-        del g
-    log("stage us: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
-
+    rec = main_b.record(a, full=True)
     copy_gbps = stream_copy_GBps()
     log(f"streaming copy of 1 GiB: {copy_gbps:.0f} GB/s (read + write)")
-    t_step = ms_step / 1e3
     s = sp
-    seqs_per_s = s.batch / t_step
-    kv_tokens_per_s = tokens / s.num_kv_heads / t_step
-    step_gbps = total_b / t_step / 1e9
-    ref_b = refresh_bytes(w0)
-    stage_bytes = {"decode_step": cent_b + ref_b + kv_b, "indexer": cent_b + ref_b,
-                   "page_scores": cent_b, "bound_scores_refresh": cent_b + ref_b,
-                   "attention_merge": kv_b}
-    stage_bytes = {k: v for k, v in stage_bytes.items() if k in stage_us}
-    # One kernel per step when the plan fuses it; otherwise the indexer and the
-    # attention (+ merge) run in turn and the slower is dominant.
-    if plan["fused_step"]:
-        dom = "decode_step"
-    else:
-        dom = max(("indexer", "attention_merge"), key=lambda k: stage_us[k])
-    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     result = {
         "metric": METRIC,
-        "value": seqs_per_s,
+        "value": rec["seqs_per_s"],
         "unit": "seqs/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if s.kv_dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{a.workload}: {DESCR[a.workload]}", "topk_mode": a.mode,
-                   "indexer": a.indexer, "replicas": R, "hip_graph": True,
-                   "num_splits": plan["num_splits"],
-                   "fused_step": bool(plan["fused_step"])},
-        "kv_tokens_per_s": kv_tokens_per_s,
-        "step_bytes": total_b,
-        "step_hbm_GBps": step_gbps,
-        "step_frac_of_peak": step_gbps / PEAK_GBPS,
+        "config": {"workload": rec["workload"], "topk_mode": a.mode,
+                   "indexer": a.indexer, "replicas": rec["replicas"], "hip_graph": True,
+                   "num_splits": rec["num_splits"], "fused_step": rec["fused_step"],
+                   "appends_token": rec["appends_token"]},
+        "kv_tokens_per_s": rec["kv_tokens_per_s"],
+        "step_bytes": rec["step_bytes"],
+        "step_hbm_GBps": rec["step_hbm_GBps"],
+        "step_frac_of_peak": rec["step_frac_of_peak"],
         "stream_copy_GBps": copy_gbps,
-        "stage_us": stage_us,
-        "stage_GBps": {k: stage_bytes[k] / (stage_us[k] * 1e-6) / 1e9 for k in stage_bytes},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBPS,
-                     "traffic": measured_traffic(a.workload + ("_bounds" if bounds else ""), dom),
-                     "kernel": dom,
-                     "bytes_per_launch": stage_bytes[dom]},
+        "stage_us": rec["stage_us"],
+        "stage_GBps": rec["stage_GBps"],
+        "roofline": rec["roofline"],
     }
     if recall:
         result["approx_recall_at_k"] = recall
@@ -716,9 +861,26 @@ def main():
         result["mla_rope_unaware_recall_at_k"] = rope
     if quality:
         result["selection_quality"] = quality
+    if not a.no_extras and not bounds and mode == V.VX_TOPK_EXACT:
+        # The other workloads, each measured in this same run.
+        main_b.free()
+        result["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            if name == a.workload:
+                continue
+            b = Bench(name, mode, "centroid", a.replicas, name in APPEND_WORKLOADS)
+            r = b.record(a, full=False)
+            b.free()
+            if name in INDEX_MODE_WORKLOADS:
+                r["topk_modes"] = index_modes(name, a)
+            result["workloads"][name] = r
+        # the headline workload's CPU baseline needs its inputs again
+        main_b = None
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w0, base, a.cpu_seconds)
+        if main_b is None:
+            main_b = Bench(a.workload, mode, a.indexer, 1, append)
+        result["cpu_baseline"] = cpu_baseline(main_b.w0, main_b.base, a.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

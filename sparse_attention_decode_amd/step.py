@@ -68,6 +68,7 @@ class DecodeStep:
                                     None, self.sm_scale, None, None, num_splits)
         self.workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
         self.workspace_bytes = nbytes
+        self.k_new = self.v_new = None  # appended token's K/V (append_kv draws them)
 
     # -- stages ---------------------------------------------------------
     def rebuild_centroids(self, stream=None) -> None:
@@ -143,6 +144,35 @@ class DecodeStep:
                                self.n_local, self.mode, w.d_rand_u32, self.scores, self.sel,
                                self.k_out, self.sel_count, self.out, self.lse, self.num_splits,
                                self.workspace, self.workspace_bytes, stream)
+
+    def append_kv(self, stream=None) -> None:
+        """Cache stage of an appending decode step: write each sequence's new
+        token's K/V (self.k_new / self.v_new) into the slot of its newest
+        token and recompute that page's centroid (vx_centroid_update with
+        first_token = -1, k_new and v_new)."""
+        w = self.w
+        if self.k_new is None:
+            s = w.spec
+            g = torch.Generator(device=w.device)
+            g.manual_seed(12345)
+            shape = (s.batch, s.num_kv_heads)
+            self.k_new = torch.randn(shape + (s.head_dim_k,), generator=g, device=w.device).to(
+                w.k_pool.dtype)
+            if not s.mla:
+                self.v_new = torch.randn(shape + (s.head_dim_v,), generator=g,
+                                         device=w.device).to(w.k_pool.dtype)
+        V.vx_centroid_update(self.pages, self.geom, w.k_pool,
+                             None if w.spec.mla else w.v_pool, self.newest, self.k_new,
+                             self.v_new, self.centroids, self.cent_bf16, stream)
+
+    def run_append(self, stream=None) -> None:
+        """An appending decode step: the new token's K/V slot write and its
+        page's centroid (append_kv), then the indexer and attention without a
+        second refresh."""
+        self.append_kv(stream)
+        if self.indexer == "bounds":
+            raise ValueError("the appending step is built for the centroid indexer")
+        self.step(refresh=False, stream=stream)
 
     def plan(self) -> dict:
         return V.vx_plan_decode(self.pages, self.geom, self.k_out, self.num_splits)
