@@ -43,6 +43,8 @@ def check_against_oracle(w, step, sample, selection=True):
                                   heads=range(g * G, (g + 1) * G), tag=f"b={b} g={g}")
             else:
                 differing += 1
+                T.check_attention_on_gpu_selection(w, step, b, r, out[b], lse[b], g,
+                                                   tag=f"b={b} g={g}")
     return differing
 
 

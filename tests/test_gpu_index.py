@@ -120,6 +120,8 @@ def check_step_against_oracle(w, step, sample):
                                   heads=range(g * G, (g + 1) * G), tag=f"b={b} g={g}")
             else:
                 differing += 1
+                T.check_attention_on_gpu_selection(w, step, b, r, out[b], lse[b], g,
+                                                   tag=f"b={b} g={g}")
     return differing
 
 

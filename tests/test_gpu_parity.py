@@ -52,6 +52,8 @@ def pipeline_check(w, sample, step=None):
                                   heads=range(g * G, (g + 1) * G), tag=f"b={b} g={g}")
             else:
                 differing += 1
+                T.check_attention_on_gpu_selection(w, step, b, r, out[b], lse[b], g,
+                                                   tag=f"b={b} g={g}")
     # attention on exactly the oracle's selection, every head
     sel, cnt = T.sel_tensor_from_oracle(w, step, refs)
     step.attend(sel=sel, sel_count=cnt)
@@ -86,4 +88,35 @@ def test_full_size_workloads_sampled(name, sample):
     _, _, differing = pipeline_check(w, sample)
     assert differing <= max(1, len(sample) * w.spec.num_kv_heads // 20)
     del w
+    torch.cuda.empty_cache()
+
+
+def test_full_size_approximate_selection_on_gpu_scores():
+    """The large-batch workload in approximate top-k mode, at full size in the
+    benchmarked launch (one kernel per step): for sampled sequences, every KV
+    head's selection equals the oracle's approximate selection run on the
+    GPU's own fp32 scores, bit for bit (the same remap, boundary bucket and
+    random window)."""
+    from oracle import vx_oracle as O
+    from sparse_attention_decode_amd import binding as V
+    s = W.spec("largebatch_bf16")
+    w = W.make(s, "cuda", seed=0)
+    step = DecodeStep(w, mode=V.VX_TOPK_APPROX)
+    step.rebuild()
+    step.run()
+    T.sync()
+    assert step.plan()["fused_step"]
+    scores = step.scores.cpu().numpy()
+    sel = step.sel.cpu().numpy()
+    cnt = step.sel_count.cpu().numpy()
+    for b in (0, 37, 100, 181, 255):
+        lo, n = int(w.indptr[b]), w.n_pages(b)
+        for g in range(s.num_kv_heads):
+            want = O.topk_approx(scores[g, lo:lo + n], step.k, step.n_sink, step.n_local,
+                                 int(w.rand_u32[b, g]))
+            full = np.full(step.k_out, -1)
+            full[:len(want)] = want
+            np.testing.assert_array_equal(sel[b, g], full, err_msg=f"b={b} g={g} n={n}")
+            assert cnt[b, g] == int((want >= 0).sum())
+    del w, step
     torch.cuda.empty_cache()

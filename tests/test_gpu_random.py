@@ -71,6 +71,8 @@ def test_random_configuration(seed):
                                   heads=range(g * G, (g + 1) * G), tag=f"seed={seed} b={b} g={g}")
             else:
                 differing += 1
+                T.check_attention_on_gpu_selection(w, step, b, r, out[b], lse[b], g,
+                                                   tag=f"seed={seed} b={b} g={g}")
     assert differing <= 1
 
 
@@ -109,4 +111,6 @@ def test_random_mla_configuration(seed):
             T.check_attention(w, out[b], lse[b], r["out"], r["lse"], tag=f"seed={seed} b={b}")
         else:
             differing += 1
+            T.check_attention_on_gpu_selection(w, step, b, r, out[b], lse[b],
+                                               tag=f"seed={seed} b={b}")
     assert differing <= 1

@@ -180,5 +180,21 @@ def oracle_attention_on(w, step, ref):
     return ref["out"], ref["lse"]
 
 
+def check_attention_on_gpu_selection(w, step, b, ref, out_b, lse_b, g=None, tag=""):
+    """Where a near tie made the GPU's selection differ from the oracle's,
+    the GPU's attention is still checked: against the oracle's attention on
+    the GPU's own selection (KV head g, or every head when g is None)."""
+    s = w.spec
+    seq = ref["seq"]
+    sel = step.sel[b].cpu().numpy().astype(np.int64)  # [Hkv][K_out], -1 padded
+    vv = seq["k"][..., :s.head_dim_v] if s.mla else seq["v"]
+    out_ref, lse_ref = O.attention(seq["q"], seq["k"], vv, seq["seq_len"], s.page_size, sel,
+                                   step.sm_scale, s.num_kv_heads)
+    G = s.num_q_heads // s.num_kv_heads
+    heads = None if g is None else range(g * G, (g + 1) * G)
+    check_attention(w, out_b, lse_b, out_ref, lse_ref, heads=heads,
+                    tag=f"{tag} (on the GPU's selection)")
+
+
 def sync():
     torch.cuda.synchronize()
