@@ -128,6 +128,10 @@ typedef struct vx_plan {
   int32_t num_cus;
   int32_t fused_step;        /* 1: vx_decode_step runs as one kernel */
   size_t workspace_bytes;    /* what vx_sparse_decode needs for this plan */
+  int32_t order_segments;    /* 1: vx_decode_step orders the sequences longest
+                                first on the device (segments span more than
+                                two rounds of blocks); its workspace then
+                                holds 4 more bytes per sequence */
 } vx_plan;
 
 /* Cache stage: refresh the key centroids of pages.
@@ -286,8 +290,9 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom,
  * and attends over its share, then the split merge. Otherwise the two calls'
  * kernels run in turn.
  * workspace == NULL: writes the bytes needed to *workspace_bytes (those of
- * vx_sparse_decode) and returns VX_OK; otherwise *workspace_bytes must be at
- * least that. */
+ * vx_sparse_decode, plus 4 per sequence when the plan orders the segments,
+ * see vx_plan_decode) and returns VX_OK; otherwise *workspace_bytes must be
+ * at least that. */
 vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom,
                          const void* q, const void* k_pool,
                          const void* v_pool, float* centroids,
@@ -333,7 +338,7 @@ vx_status vx_decode_step_static(const vx_pages* pages, const vx_geom* geom,
  * max_pages <= 4096, it is one kernel per step, the same
  * block-per-(sequence, KV head) kernel as vx_decode_step's with the bounds
  * scorer in place of the centroid scorer. workspace == NULL: writes
- * the bytes needed to *workspace_bytes (those of vx_sparse_decode) and
+ * the bytes needed to *workspace_bytes (as for vx_decode_step) and
  * returns VX_OK. */
 vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom,
                                const void* q, const void* k_pool,
@@ -350,7 +355,11 @@ vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom,
 /* Workload planner (Vortex paper note, "System design > 3. Execution
  * backend": plan by batch size, sequence length, layout and operator).
  * Host only: fills *plan from host sizes; num_cus <= 0 queries the current
- * device, num_splits <= 0 lets the planner choose. */
+ * device, num_splits <= 0 lets the planner choose. Sequence lengths live on
+ * the device, so the length-dependent part of the plan runs there: with
+ * order_segments, vx_decode_step first ranks the sequences by pages in use
+ * (a one-block kernel writing the order into its workspace) and the
+ * whole-step kernel's blocks take the longest segments first. */
 vx_status vx_plan_decode(const vx_pages* pages, const vx_geom* geom,
                          int32_t sel_stride, int32_t num_splits,
                          int32_t num_cus, vx_plan* plan);

@@ -19,6 +19,41 @@
 namespace vx {
 namespace {
 
+// The segment (sequence b, KV head g) = b * Hkv + g this block serves: block
+// row i = blockIdx.x / Hkv takes sequence order[i] when the planner ordered
+// the sequences (longest first), else sequence i.
+__device__ __forceinline__ int block_segment(const SegArgs& a) {
+  const int i = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+  if (!a.order) return blockIdx.x;
+  const int b = a.order[i];
+  return (b < 0 ? 0 : (b >= a.m.batch ? a.m.batch - 1 : b)) * a.hkv + g;
+}
+
+// Sequences ranked by pages in use, most first (ties: lower index first):
+// order[r] = the sequence of rank r, so the whole-step blocks that the GPU
+// dispatches first take the longest segments and the last ones the
+// shortest (the workload planning of the Vortex paper note, "System design >
+// 3. Execution backend": plan by batch size and sequence length). One block,
+// batch <= kMaxOrderedBatch.
+__global__ __launch_bounds__(1024) void rank_sequences_kernel(Meta m, int32_t* __restrict__ order) {
+  __shared__ int npg[kMaxOrderedBatch];
+  for (int b = threadIdx.x; b < m.batch; b += blockDim.x) {
+    const int cap = m.indptr[b + 1] - m.indptr[b];
+    const int L = seq_len_clamped(m, b);
+    npg[b] = min((L + m.page_size - 1) / m.page_size, cap);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < m.batch; b += blockDim.x) {
+    const int nb = npg[b];
+    int r = 0;
+    for (int j = 0; j < m.batch; ++j) {
+      const int nj = npg[j];
+      r += (nj > nb || (nj == nb && j < b)) ? 1 : 0;
+    }
+    order[r] = b;
+  }
+}
+
 template <int G, int P, int NW, bool BOUNDS>
 __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                                                              const uint16_t* __restrict__ vp,
@@ -33,7 +68,7 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   __shared__ MfmaShared<G, NW> sm;
   static_assert(kMaxPagesPerSplit <= 64 * NW, "one page-list entry per thread");
 
-  const int seg = blockIdx.x;
+  const int seg = block_segment(a);
   const int b = seg / a.hkv, g = seg % a.hkv;
   const uint16_t* kp = (const uint16_t*)a.kp;
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
@@ -90,7 +125,7 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs 
   __shared__ VecShared<G, DK> sm;
   static_assert(kMaxPagesPerSplit <= 64 * kVecWaves, "one page-list entry per thread");
 
-  const int seg = blockIdx.x;
+  const int seg = block_segment(a);
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
   index_segment<KV, KV, DK, G, kVecWaves, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l);
 
@@ -175,6 +210,13 @@ hipError_t launch_p(const SegArgs& a, const void* v_pool, float qscale, float* o
 
 }  // namespace
 
+hipError_t launch_rank_sequences(const Meta& m, int32_t* order, hipStream_t s) {
+  if (m.batch == 0) return hipSuccess;
+  if (m.batch > kMaxOrderedBatch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rank_sequences_kernel, dim3(1), dim3(1024), 0, s, m, order);
+  return hipGetLastError();
+}
+
 bool decode_step_fusable(const vx_geom& g, int page_size, int max_pages, int sel_stride,
                          bool bounds) {
   const int G = g.num_q_heads / g.num_kv_heads;
@@ -190,9 +232,10 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
-                                  hipStream_t s) {
+                                  const int32_t* order, hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   SegArgs a{};
+  a.order = order;
   a.m = m;
   a.hq = g.num_q_heads;
   a.hkv = g.num_kv_heads;

@@ -51,6 +51,7 @@ struct SegArgs {
   int stride;
   int32_t* sel_count;
   int cap_keys;
+  const int32_t* order;  // nullable: order[i] = the sequence block row i serves (whole step)
 };
 
 // What the waves other than wave 0 do while wave 0 selects: nothing.

@@ -237,7 +237,20 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   out->workspace_bytes = ws;
   out->fused_step = S == 1 && p->total_pages > 0 &&
                     vx::decode_step_fusable(*g, p->page_size, p->max_pages, sel_stride, false);
+  // The whole-step kernel takes one (sequence, KV head) segment per block.
+  // When the segments need more than two rounds of blocks over the compute
+  // units, the last blocks decide the step's end: order the sequences longest
+  // first, so the long segments start early and short ones fill the tail.
+  out->order_segments = out->fused_step && items0 > 2L * num_cus &&
+                        p->batch <= vx::kMaxOrderedBatch;
   return VX_OK;
+}
+
+// Workspace of a whole step: vx_sparse_decode's, then (ordered plans) the
+// sequence order, 4 bytes per sequence.
+size_t step_workspace_bytes(const vx_pages* p, const vx_plan& plan) {
+  return plan.workspace_bytes +
+         (plan.order_segments ? align_up((size_t)p->batch * sizeof(int32_t), 256) : 0);
 }
 
 // Per-split partial outputs and (m, l) pairs in the workspace (S > 1), laid
@@ -514,20 +527,28 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
   if ((st = device_cus(&cus)) != VX_OK) return st;
   vx_plan plan;
   if ((st = make_plan(pages, geom, sel_stride, num_splits, cus, &plan)) != VX_OK) return st;
+  const size_t need = step_workspace_bytes(pages, plan);
   if (!workspace) {
-    *workspace_bytes = plan.workspace_bytes;
+    *workspace_bytes = need;
     return VX_OK;
   }
-  VX_CHECK(*workspace_bytes >= plan.workspace_bytes, VX_ERR_WORKSPACE,
-           "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
+  VX_CHECK(*workspace_bytes >= need, VX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+           *workspace_bytes, need);
   if (pages->batch == 0) return VX_OK;
   if (plan.num_splits == 1 && pages->total_pages > 0 &&
       vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride, false)) {
-    const hipError_t e = vx::launch_decode_step_gqa(
+    int32_t* order = nullptr;
+    hipError_t e = hipSuccess;
+    if (plan.order_segments) {
+      order = (int32_t*)((char*)workspace + plan.workspace_bytes);
+      e = vx::launch_rank_sequences(meta_of(pages), order, stream);
+      if (e != hipSuccess) return hip_status(e, "sequence order kernel launch");
+    }
+    e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, nullptr,
         refresh_newest,
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
-        sel_count, out, lse, pages->max_pages, stream);
+        sel_count, out, lse, pages->max_pages, order, stream);
     return hip_status(e, "decode step kernel launch");
   }
   if (geom->mla && pages->total_pages > 0 &&
@@ -628,19 +649,30 @@ vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom, const
   if ((st = device_cus(&cus)) != VX_OK) return st;
   vx_plan plan;
   if ((st = make_plan(pages, geom, sel_stride, num_splits, cus, &plan)) != VX_OK) return st;
+  const bool fused = plan.num_splits == 1 && pages->total_pages > 0 &&
+                     vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages,
+                                             sel_stride, true);
+  plan.order_segments = plan.order_segments && fused;
+  const size_t need = step_workspace_bytes(pages, plan);
   if (!workspace) {
-    *workspace_bytes = plan.workspace_bytes;
+    *workspace_bytes = need;
     return VX_OK;
   }
-  VX_CHECK(*workspace_bytes >= plan.workspace_bytes, VX_ERR_WORKSPACE,
-           "workspace %zu bytes < %zu needed", *workspace_bytes, plan.workspace_bytes);
+  VX_CHECK(*workspace_bytes >= need, VX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+           *workspace_bytes, need);
   if (pages->batch == 0) return VX_OK;
-  if (plan.num_splits == 1 && pages->total_pages > 0 &&
-      vx::decode_step_fusable(*geom, pages->page_size, pages->max_pages, sel_stride, true)) {
-    const hipError_t e = vx::launch_decode_step_gqa(
+  if (fused) {
+    int32_t* order = nullptr;
+    hipError_t e = hipSuccess;
+    if (plan.order_segments) {
+      order = (int32_t*)((char*)workspace + plan.workspace_bytes);
+      e = vx::launch_rank_sequences(meta_of(pages), order, stream);
+      if (e != hipSuccess) return hip_status(e, "sequence order kernel launch");
+    }
+    e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, nullptr, nullptr, bounds, refresh_newest,
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
-        sel_count, out, lse, pages->max_pages, stream);
+        sel_count, out, lse, pages->max_pages, order, stream);
     return hip_status(e, "decode step kernel launch");
   }
   if ((st = vx_bound_scores(pages, geom, q, k_pool, bounds, refresh_newest, score_scale, scores,

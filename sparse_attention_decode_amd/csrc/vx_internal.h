@@ -180,7 +180,10 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
-                                  hipStream_t s);
+                                  const int32_t* order, hipStream_t s);
+// order[r] = the sequence with the r-th most pages in use (ties: lower index
+// first), for the whole-step kernel's block order. batch <= kMaxOrderedBatch.
+hipError_t launch_rank_sequences(const Meta& m, int32_t* order, hipStream_t s);
 // MLA scores on the bf16 centroids; refresh != 0 first recomputes each
 // sequence's newest page (fp32 centroid and its bf16 copy) from k_pool.
 hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,
@@ -245,6 +248,8 @@ constexpr int kSelectExtraWords = kSelectHistWords + 32;
 constexpr int kBlockSelectMin = 256;
 // Largest per-sequence page count the top-k supports (LDS resident keys).
 constexpr int kMaxTopkPages = 16000;
+// Largest batch whose sequences the planner orders longest first.
+constexpr int kMaxOrderedBatch = 1024;
 
 
 }  // namespace vx

@@ -64,8 +64,14 @@ class DecodeStep:
                     if with_lse else None)
         # -1: refresh the page holding each sequence's newest token
         self.newest = torch.full((s.batch,), -1, dtype=torch.int32, device=dev)
-        nbytes = V.vx_sparse_decode(self.pages, self.geom, None, None, None, None, self.k_out,
-                                    None, self.sm_scale, None, None, num_splits)
+        # the whole step's workspace covers the attention's (and, for ordered
+        # plans, the sequence order)
+        nbytes = max(
+            V.vx_sparse_decode(self.pages, self.geom, None, None, None, None, self.k_out,
+                               None, self.sm_scale, None, None, num_splits),
+            V.vx_decode_step(self.pages, self.geom, None, None, None, None, None, True,
+                             self.score_scale, self.sm_scale, self.k, self.n_sink, self.n_local,
+                             mode, None, None, None, self.k_out, None, None, None, num_splits))
         self.workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
         self.workspace_bytes = nbytes
         self.k_new = self.v_new = None  # appended token's K/V (append_kv draws them)

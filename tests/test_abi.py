@@ -168,6 +168,29 @@ def test_planner_splits_and_workspace():
     assert plan["num_splits"] == 7 and plan["pages_per_split"] == 5  # 8 splits would also take 5
 
 
+def test_planner_orders_long_batches():
+    """Sequence lengths are device data, so the planner's length-dependent part
+    runs on the device: when the whole step's segments span more than two
+    rounds of blocks it asks vx_decode_step to rank the sequences longest first,
+    and the step's workspace grows by 4 bytes per sequence."""
+    g = geom(hq=64, hkv=8)
+    # the large-batch shape: 256 sequences x 8 KV heads = 2048 segments > 2 x 256
+    big = pages(batch=256, nnz=81600, pool=102000, maxp=1024, page_size=64)
+    plan = V.vx_plan_decode(big, g, 64, 0, 256)
+    assert plan["fused_step"] == 1 and plan["order_segments"] == 1
+    assert plan["workspace_bytes"] == 0  # vx_decode_step adds 256 x 4 bytes for the order
+    # one round (the long-generation shape, 512 segments): no ordering, no workspace
+    plan = V.vx_plan_decode(pages(batch=64, nnz=81920, pool=102400, maxp=2052), geom(hq=32), 131,
+                            0, 256)
+    assert plan["fused_step"] == 1 and plan["order_segments"] == 0
+    # split plans are not whole-step kernels: never ordered
+    plan = V.vx_plan_decode(big, g, 64, 3, 256)
+    assert plan["order_segments"] == 0
+    # beyond the largest ordered batch
+    plan = V.vx_plan_decode(pages(batch=2048, nnz=2048 * 20, pool=2048 * 25, maxp=20), g, 18, 0, 256)
+    assert plan["order_segments"] == 0
+
+
 def test_index_pages_argument_checks():
     p, g = pages(), geom()
     ok = dict(q=BAD, k_pool=BAD, centroids=BAD, cent_bf16=None, refresh=1, scale=1.0, scores=BAD,
