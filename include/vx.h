@@ -308,11 +308,11 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom,
 /* vx_decode_step for callers that cannot allocate: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. Same
  * arguments and results (the same kernels and bits) as vx_decode_step, with
- * no workspace argument: the split partials live in a 16 MiB scratch array
+ * no workspace argument: the split partials live in a 32 MiB scratch array
  * inside the library, one per device, which each device holds until the
  * process ends. The call allocates nothing (no hipMalloc, hipFree or
  * allocating library routine); its first call on a device looks up that
- * device's scratch address. A step whose partials need more than 16 MiB
+ * device's scratch address. A step whose partials need more than 32 MiB
  * (batch * num_q_heads * splits * (head_dim_v + 2) * 4 bytes, split steps
  * only) returns VX_ERR_WORKSPACE before any launch. Every call on one device
  * shares its scratch, so calls that overlap on one device (different streams

@@ -202,6 +202,8 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   out->num_cus = num_cus;
   const int stride = sel_stride < 1 ? 1 : sel_stride;
   const long items0 = (long)p->batch * (g->mla ? 1 : g->num_kv_heads);
+  const int units = stride;  // pages
+  const int unit_cap = vx::kMaxPagesPerSplit;
   int S;
   if (num_splits > 0) {
     S = num_splits;
@@ -212,19 +214,19 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
     const long most = (long)stride * p->page_size * row / kMinSplitBytes;  // a full selection
     if (s > most) s = most;
     S = (int)(s < 1 ? 1 : s);
-    if (S > stride) S = stride;
+    if (S > units) S = units;
     // The largest split sets the time; use no more splits than that size
     // needs (fewer partials to write and merge, fewer blocks repeating
     // per-sequence work).
-    const int pps = (stride + S - 1) / S;
-    S = (stride + pps - 1) / pps;
+    const int per = (units + S - 1) / S;
+    S = (units + per - 1) / per;
   }
-  if (S > stride) S = stride;
-  const int min_splits = (stride + vx::kMaxPagesPerSplit - 1) / vx::kMaxPagesPerSplit;
+  if (S > units) S = units;
+  const int min_splits = (units + unit_cap - 1) / unit_cap;
   if (S < min_splits) S = min_splits;
-  const int pps = (stride + S - 1) / S;  // largest split
+  const int per = (units + S - 1) / S;  // largest split, in units
   out->num_splits = S;
-  out->pages_per_split = pps;
+  out->pages_per_split = per;
   out->score_pages_per_block = 4 * kScorePagesPerWave;
   out->score_blocks = (p->total_pages + out->score_pages_per_block - 1) / out->score_pages_per_block;
   out->topk_threads = p->max_pages > vx::kBlockSelectMin ? 512 : 64;
@@ -272,7 +274,7 @@ void split_buffers(const vx_pages* p, const vx_geom* g, int S, void* ws, float**
 // code never uses the array's name as an address: the device address comes
 // from hipGetSymbolAddress, looked up once per device with that device
 // current, and kept per device.
-constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 void* g_scratch[64];  // per-device address of `scratch`, null until looked up
 
@@ -553,7 +555,9 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
   }
   if (geom->mla && pages->total_pages > 0 &&
       vx::decode_step_mla_fusable(pages->max_pages, sel_stride)) {
-    // scores, then selection + attention in one kernel, then the merge
+    // scores, then selection + attention in one kernel, then the merge (a
+    // merge by the last split block to finish was measured slower: that block
+    // reads every split's partials alone)
     const vx::Meta m = meta_of(pages);
     const int S = plan.num_splits;
     float* part_o = nullptr;

@@ -128,6 +128,56 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 
+// Log-sum-exp merge of S split partials of one (sequence, head), 4 value
+// columns: po = partial outputs (split stride dv), ml = (m, l) pairs per
+// split; out[0..3] = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m),
+// *lse (nullable) = (max m + log2 sum_s w_s l_s) ln 2. Up to kMergeBatch splits
+// have every load in flight at once; the arithmetic and its order are the
+// same for any S (so every merge writes the same bits).
+constexpr int kMergeBatch = 16;
+VX_DEV void merge_row(int S, int dv, const float* __restrict__ po, const float* __restrict__ ml,
+                      float* __restrict__ out, float* __restrict__ lse) {
+  float mmax = kNegBig;
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (S <= kMergeBatch) {
+    float2 mlv[kMergeBatch];
+    float4 x[kMergeBatch];
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s < S) {
+        mlv[s] = *(const float2*)(ml + 2 * s);
+        x[s] = *(const float4*)(po + (size_t)s * dv);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s)
+      if (s < S) mmax = fmaxf(mmax, mlv[s].x);
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s < S) {
+        const float wt = __builtin_amdgcn_exp2f(mlv[s].x - mmax);
+        wsum = fmaf(mlv[s].y, wt, wsum);
+        acc.x = fmaf(x[s].x, wt, acc.x); acc.y = fmaf(x[s].y, wt, acc.y);
+        acc.z = fmaf(x[s].z, wt, acc.z); acc.w = fmaf(x[s].w, wt, acc.w);
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+      const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
+      wsum = fmaf(ml[2 * s + 1], wt, wsum);
+      const float4 xs = *(const float4*)(po + (size_t)s * dv);
+      acc.x = fmaf(xs.x, wt, acc.x); acc.y = fmaf(xs.y, wt, acc.y);
+      acc.z = fmaf(xs.z, wt, acc.z); acc.w = fmaf(xs.w, wt, acc.w);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *(float4*)out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (lse) *lse = wsum > 0.f ? (mmax + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Four consecutive elements: raw load, then widening to fp32 (kept apart so

@@ -56,7 +56,7 @@ def test_static_scratch_limit():
     """Partials above the scratch size: VX_ERR_WORKSPACE, nothing launched
     (the pointers are never dereferenced)."""
     bad = 0x1000
-    pages = V.make_pages(8, 16, 2000, 1600, 200, bad, bad, bad)
+    pages = V.make_pages(16, 16, 4000, 3200, 200, bad, bad, bad)
     geom = V.make_geom(32, 8, 128, 128, 0, V.VX_BF16, V.VX_BF16)
     with pytest.raises(V.VxError) as e:
         V.vx_decode_step_static(pages, geom, bad, bad, bad, bad, None, True, 0.1, 0.1, 128, 1, 2,
