@@ -179,6 +179,8 @@ __device__ __forceinline__ uint32_t reg_compact(const uint32_t (&code)[R], const
   off = __builtin_amdgcn_readfirstlane(off);
   members = __builtin_amdgcn_readfirstlane(members);
   uint32_t written = __builtin_amdgcn_readfirstlane(o0), tie_seen = 0;
+  // r == 0 or r == members: every tie is dropped or every tie taken, no ranks needed
+  const bool ranked = r != 0 && r < members;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     if (u >= ru) break;
@@ -186,15 +188,15 @@ __device__ __forceinline__ uint32_t reg_compact(const uint32_t (&code)[R], const
     const bool forced = i >= 0 && i < n && (i < n_sink || i >= n - n_local);
     const bool above = code[u] > tau;
     const bool tie = code[u] != 0u && code[u] == tau;
-    const unsigned long long tmask = __ballot(tie);
-    const uint32_t trank = tie_seen + rank_below(tmask);
-    tie_seen += (uint32_t)__popcll(tmask);
-    bool take = forced || above;
-    if (tie && members) {
+    bool take = forced || above || (tie && r != 0);
+    if (ranked) {
+      const unsigned long long tmask = __ballot(tie);
+      const uint32_t trank = tie_seen + rank_below(tmask);
+      tie_seen += (uint32_t)__popcll(tmask);
       // cyclic position from off: trank, off < members, so one wrap at most
       uint32_t pos = trank + members - off;
       pos = pos >= members ? pos - members : pos;
-      take = take || pos < r;
+      take = forced || above || (tie && pos < r);
     }
     const unsigned long long smask = __ballot(take);
     if (take) {
