@@ -37,9 +37,13 @@ struct MfmaShared {
   __attribute__((aligned(16))) uint16_t ptile[NW][16 * kPRow];
 };
 
-VX_DEV uint32_t elem16(const u32x4& v, int e) {
-  const uint32_t wv = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (wv >> 16) : (wv & 0xffffu);
+// Element e of a and of b (16-bit elements) as the low and high half of one
+// word: one byte permute.
+VX_DEV uint32_t pair16(const u32x4& a, const u32x4& b, int e) {
+  const int k = e >> 1;
+  const uint32_t wa = k == 0 ? a.x : k == 1 ? a.y : k == 2 ? a.z : a.w;
+  const uint32_t wb = k == 0 ? b.x : k == 1 ? b.y : k == 2 ? b.z : b.w;
+  return __builtin_amdgcn_perm(wb, wa, (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // A operand of q.k^T: head row l%16 of the group (zero past G), dims
@@ -111,37 +115,48 @@ VX_DEV void mfma_chunk(MfmaShared<G, NW>& sm, MfmaState& st, int phys, int first
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[ks]),
                                                    __builtin_bit_cast(bf16x8_t, kr[ks]), sacc,
                                                    0, 0, 0);
+  // Rows 4 q4 + i of the tile; with G < 4 only i < G of the lanes with
+  // q4 == 0 are heads, so the softmax runs for those rows only. The other
+  // rows' P entries are never written, which only touches output rows past
+  // G (an MFMA output row depends on its own A row alone), never read.
+  constexpr int NI = G < 4 ? G : 4;
   const bool tok_ok = col < nvc;
   float alpha[4];
   bool grow = false;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const float z = tok_ok ? sacc[i] * qscale : -INFINITY;
     const float mnew = fmaxf(st.mrow[i], group_max<16>(z));
     alpha[i] = __builtin_amdgcn_exp2f(st.mrow[i] - mnew);
     grow = grow || (mnew > st.mrow[i]);
-    const float pv = __builtin_amdgcn_exp2f(z - mnew);
+    const float pv = __builtin_amdgcn_exp2f(z - mnew);  // in [0, 1], never NaN
     st.lrow[i] = fmaf(st.lrow[i], alpha[i], group_sum<16>(pv));
     st.mrow[i] = mnew;
-    pw[(4 * q4 + i) * kPRow + col] = f32_to_bf16(pv);
+    // round to nearest even (v_cvt_pk_bf16_f32)
+    pw[(4 * q4 + i) * kPRow + col] = __builtin_bit_cast(uint16_t, (__bf16)pv);
   }
   if (__ballot(grow)) {  // rescale only when some row's maximum moved
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.o[e][i] *= alpha[i];
+      for (int i = 0; i < NI; ++i) st.o[e][i] *= alpha[i];
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint2 pa = *(const uint2*)(pw + col * kPRow + 4 * q4);
   u32x4 v[4];
+  if (nvc >= 16) {  // a whole chunk (uniform): no value row to clear
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = (4 * q4 + r < nvc) ? vr[r] : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < 4; ++r) v[r] = vr[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (4 * q4 + r < nvc) ? vr[r] : u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t b01 = elem16(v[0], e) | (elem16(v[1], e) << 16);
-    const uint32_t b23 = elem16(v[2], e) | (elem16(v[3], e) << 16);
+    const uint32_t b01 = pair16(v[0], v[1], e);
+    const uint32_t b23 = pair16(v[2], v[3], e);
     st.o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
         __builtin_bit_cast(bf16x4_t, pa), __builtin_bit_cast(bf16x4_t, uint2{b01, b23}), st.o[e],
         0, 0, 0);

@@ -54,6 +54,16 @@ __global__ __launch_bounds__(1024) void rank_sequences_kernel(Meta m, int32_t* _
   }
 }
 
+// The whole-step kernels' selection (kept in LDS, count <= stride entries)
+// to a.sel / a.sel_count, -1 past the count, by wave 0. The LDS copy stays
+// unchanged from the select to here.
+VX_DEV void write_selection(const SegArgs& a, int seg, const int32_t* sel_l, int count) {
+  if (threadIdx.x >= 64) return;
+  int32_t* so = a.sel + (size_t)seg * a.stride;
+  for (int i = threadIdx.x; i < a.stride; i += 64) so[i] = i < count ? sel_l[i] : -1;
+  if (threadIdx.x == 0) a.sel_count[seg] = count;
+}
+
 template <int G, int P, int NW, bool BOUNDS>
 __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                                                              const uint16_t* __restrict__ vp,
@@ -77,19 +87,24 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   st.init();
   // With a forced sink and newest page, the first and last page of the
   // selection are pages 0 and n-1 whatever the scores: while wave 0 selects,
-  // the waves that the chunk deal gives their chunks attend them.
+  // the waves that the chunk deal gives their chunks attend them. Wave 0
+  // loads its query rows before it selects, so that load is not waited for
+  // at the barrier after the selection.
   bool q_loaded = false, ends_done = false;
-  auto idle = [&](int n, int L) {
+  auto idle = [&](int n, int L, bool selects) {
     mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
     q_loaded = true;
-    if (a.n_sink >= 1 && a.n_local >= 1 && n >= 1) {
+    if (!selects && a.n_sink >= 1 && a.n_local >= 1 && n >= 1) {
       const ChunkDeal<P / 16> d(n >= 2 ? 2 : 1);
       mfma_end_chunks<G, P, NW>(sm, st, d, pid_l[0], min(P, L), pid_l[n - 1],
                                 min(P, L - (n - 1) * P), g, a.hkv, qa, kp, vp, qscale);
       ends_done = true;
     }
   };
-  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, idle);
+  // The selection goes to a.sel after the attention (write_selection), so
+  // its stores are not waited for at the barriers in between.
+  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, idle,
+                                                        false);
 
   const Meta& m = a.m;
   if (!q_loaded) mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
@@ -108,6 +123,7 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                               pg_nv[count - 1], g, a.hkv, qa, kp, vp, qscale);
   mfma_mid_chunks<G, P, NW>(sm, st, d, pg_phys, pg_nv, g, a.hkv, qa, kp, vp, qscale);
   mfma_finish<G, NW>(sm, st, b, g, a.hkv, 1, 0, out, lse, nullptr, nullptr);
+  write_selection(a, seg, sel_l, count);
 }
 
 template <typename KV, int G, int DK, int P, bool BOUNDS>
@@ -127,7 +143,8 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs 
 
   const int seg = block_segment(a);
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
-  index_segment<KV, KV, DK, G, kVecWaves, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l);
+  index_segment<KV, KV, DK, G, kVecWaves, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, NoIdle{},
+                                                  false);
 
   const Meta& m = a.m;
   const int b = seg / a.hkv, g = seg % a.hkv;
@@ -144,6 +161,7 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs 
   __syncthreads();  // page list ready
   vec_attend<KV, KV, G, DK, P>(sm, pg_phys, pg_nv, count, b, g, a.hkv, vq, (const KV*)a.kp, vp,
                                qscale, 1, 0, out, lse, nullptr, nullptr);
+  write_selection(a, seg, sel_l, count);
 }
 
 template <typename KV, int DK, int P, bool BOUNDS>

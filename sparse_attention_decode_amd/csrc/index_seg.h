@@ -56,7 +56,7 @@ struct SegArgs {
 
 // What the waves other than wave 0 do while wave 0 selects: nothing.
 struct NoIdle {
-  VX_DEV void operator()(int, int) const {}
+  VX_DEV void operator()(int, int, bool) const {}
 };
 
 // The index of segment seg = b * Hkv + g by a block of NW waves (NW <= 16).
@@ -64,14 +64,17 @@ struct NoIdle {
 // receives the physical page of every entry in use; sel_lds / count_lds
 // (nullable) a copy of the selection. Ends after the selection is written;
 // its LDS copies are visible to the block after a barrier. When one wave
-// selects (segments of up to kBlockSelectMin pages), the other waves call
-// idle(n, L) meanwhile (n pages in use, L tokens; the keys and pid_lds are
-// then visible); a longer segment is selected by every wave and idle is not
-// called.
+// selects (segments of up to kBlockSelectMin pages), that wave calls
+// idle(n, L, true) just before its selection and the other waves call
+// idle(n, L, false) meanwhile (n pages in use, L tokens; the keys and pid_lds
+// are then visible); a longer segment is selected by every wave and idle is
+// not called. sel_global == false leaves a.sel / a.sel_count unwritten (the
+// caller writes them later from sel_lds / count_lds).
 template <typename QT, typename KV, int DK, int GG, int NW, bool BOUNDS = false,
           typename Idle = NoIdle>
 VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_lds,
-                          int32_t* sel_lds, int32_t* count_lds, Idle idle = Idle{}) {
+                          int32_t* sel_lds, int32_t* count_lds, Idle idle = Idle{},
+                          bool sel_global = true) {
   constexpr int W = DK / 4;    // lanes per row slice
   constexpr int PPI = 64 / W;  // pages per load instruction
   constexpr int kChunk = kSegChunk * PPI;
@@ -214,16 +217,18 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   }
   __syncthreads();  // every key of the segment is in LDS
   const uint32_t rnd = a.mode == VX_TOPK_APPROX ? a.rnd[seg] : 0u;
-  if (n > kBlockSelectMin)
+  int32_t* const so = sel_global ? a.sel + (size_t)seg * a.stride : nullptr;
+  int32_t* const sc = sel_global ? a.sel_count + seg : nullptr;
+  if (n > kBlockSelectMin) {
     block_select_keys<NW>(keys, keys + a.cap_keys, keys + a.cap_keys + kSelectHistWords, n, a.k, a.n_sink,
-                          a.n_local, a.mode, rnd, a.sel + (size_t)seg * a.stride, a.stride,
-                          a.sel_count + seg, sel_lds, count_lds);
-  else if (w == 0)
-    wave_select_keys(keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd,
-                     a.sel + (size_t)seg * a.stride, a.stride, a.sel_count + seg, lane, sel_lds,
-                     count_lds);
-  else
-    idle(n, L);
+                          a.n_local, a.mode, rnd, so, a.stride, sc, sel_lds, count_lds);
+  } else if (w == 0) {
+    idle(n, L, true);
+    wave_select_keys(keys, n, a.k, a.n_sink, a.n_local, a.mode, rnd, so, a.stride, sc, lane,
+                     sel_lds, count_lds);
+  } else {
+    idle(n, L, false);
+  }
 }
 
 }  // namespace vx
