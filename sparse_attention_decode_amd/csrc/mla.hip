@@ -303,14 +303,22 @@ __device__ __forceinline__ void mla_attend(uint8_t* slot0, uint8_t* slot1, uint1
     }
   };
   // Chunk c: consumed from `slot`; chunk c + 1 streams into `other`.
-  auto chunk = [&](int c, const uint8_t* slot, uint8_t* other) {
-    // Wait for this wave's loads of chunk c (vmcnt 0: nothing else is in
-    // flight here, except chunk 1 at c = 0, issued together with chunk 0);
-    // the barrier then makes every wave's share visible and ends every read
-    // of chunk c - 1, whose slot chunk c + 1 takes.
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    __syncthreads();  // (A)
-    if (c >= 1 && c + 1 < np) issue(c + 1, other);
+  // `first` (a literal at each call) is chunk 0.
+  auto chunk = [&](int c, const uint8_t* slot, uint8_t* other, bool first) {
+    // Wait for this wave's loads of chunk c; the barrier then makes every
+    // wave's share visible and ends every read of chunk c - 1, whose slot
+    // chunk c + 1 takes. For chunk 0 the LPW loads into slot1 (issued after
+    // chunk 0's, and vmcnt retires loads in issue order) stay in flight, so
+    // chunk 0 is computed while they land, and the barrier waits for LDS
+    // only. Later, nothing but chunk c is in flight here (vmcnt 0).
+    if (first) {
+      __builtin_amdgcn_s_waitcnt((LPW & 15) | ((LPW >> 4) << 14) | (7 << 4) | (15 << 8));
+      barrier_lds();  // (A)
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      __syncthreads();  // (A)
+      if (c + 1 < np) issue(c + 1, other);
+    }
     const int nv = pg_nv[c];
 
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -389,11 +397,22 @@ __device__ __forceinline__ void mla_attend(uint8_t* slot0, uint8_t* slot1, uint1
     }
   };
 
-  if (np > 0) issue(0, slot0);
-  if (np > 1) issue(1, slot1);
-  for (int c = 0; c < np; c += 2) {
-    chunk(c, slot0, slot1);
-    if (c + 1 < np) chunk(c + 1, slot1, slot0);
+  // Chunk 0 is computed before the loop (a loop entry waits for every load
+  // in flight, the query rows loaded above being used inside it; then that
+  // is chunk 1 only, needed next anyway), and slot1 is loaded on every path
+  // into it (chunk 1, or with np == 1 a copy of chunk 0 that is never read),
+  // so that the compiler's own wait before the reads of slot0 stays at
+  // chunk 1's LPW loads.
+  if (np > 0) {
+    issue(0, slot0);
+    // chunk 0's loads are issued before slot1's (the wait at c = 0 counts on it)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue(np > 1 ? 1 : 0, slot1);
+    chunk(0, slot0, slot1, true);
+  }
+  for (int c = 1; c < np; c += 2) {
+    chunk(c, slot1, slot0, false);
+    if (c + 1 < np) chunk(c + 1, slot0, slot1, false);
   }
 
   // Row sums: over the 16 tokens of the lane group, then the four token tiles.
@@ -507,8 +526,16 @@ __global__ __launch_bounds__(256 * MT) void decode_mla_kernel(MlaStepArgs a) {
   const int n = min(min((L + CHT - 1) / CHT, cap), a.cap_keys);
   uint32_t* keys = (uint32_t*)slot0;  // cap_keys + kSelectExtraWords words
   int32_t* sel_l = (int32_t*)slot1;   // the selection, ascending
-  for (int i = t; i < n; i += 64 * NW)
+  // The physical page of every entry, loaded together with the scores when
+  // it fits in slot1 after the selection's stride: the page list then needs
+  // no global load after the select.
+  const int pid_off = (a.stride + 63) / 64 * 64;
+  const bool pid_in_lds = (size_t)(pid_off + n) * 4 <= (size_t)kSlotBytes;
+  int32_t* pid_l = sel_l + pid_off;
+  for (int i = t; i < n; i += 64 * NW) {
     keys[i] = (i < a.n_sink || i >= n - a.n_local) ? 0u : topk_detail::score_key(a.scores[row0 + i]);
+    if (pid_in_lds) pid_l[i] = phys_page(m, row0 + i);
+  }
   __syncthreads();
   const uint32_t rnd = a.mode == VX_TOPK_APPROX ? a.rnd[b] : 0u;
   int32_t* gsel = s == 0 ? a.sel + (size_t)b * a.stride : nullptr;
@@ -526,7 +553,7 @@ __global__ __launch_bounds__(256 * MT) void decode_mla_kernel(MlaStepArgs a) {
   const int np = max(0, min(p1, count) - p0);
   if (t < np) {
     const int lp = sel_l[p0 + t];
-    pg_phys[t] = phys_page(m, row0 + lp);
+    pg_phys[t] = pid_in_lds ? pid_l[lp] : phys_page(m, row0 + lp);
     pg_nv[t] = max(0, min(CHT, L - lp * CHT));
   }
   __syncthreads();  // page list ready; keys and selection no longer read
