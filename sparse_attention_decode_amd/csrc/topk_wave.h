@@ -380,50 +380,22 @@ __device__ __forceinline__ void wave_select_keys(const uint32_t* __restrict__ ke
                                   count_out, lane, out_lds, count_lds);
 }
 
-// Exact block select by local top-kk lists (see the top of the file): wave
-// w selects the kk best keys of its range of ceil(n / NW) <= 64 R1 keys, then
-// wave 0 selects kk of the NW kk <= 64 R2 candidates. hist: LDS for the
-// candidate ids. Called by every thread with 0 < kk < the candidate count.
-template <int NW, int R1, int R2>
-__device__ __forceinline__ void block_union_select(const uint32_t* __restrict__ keys,
-                                                   uint32_t* __restrict__ hist, int n, int kk,
-                                                   int n_sink, int n_local,
-                                                   int32_t* __restrict__ out, int stride,
-                                                   int32_t* __restrict__ count_out,
-                                                   int32_t* __restrict__ out_lds,
-                                                   int32_t* __restrict__ count_lds) {
+// The last step of the block selects, by one wave: kk of the nsl <= 64 R2
+// candidate ids cand[0 .. nsl) (LDS, ascending page index, -1 = no
+// candidate; their keys are nonzero and at least kk of them) are selected by
+// the register select; the forced prefix [0, ns) and suffix [ss, n) frame
+// them in the output.
+template <int R2>
+__device__ __forceinline__ void final_select(const uint32_t* __restrict__ keys,
+                                             const int32_t* __restrict__ cand, int nsl, int n,
+                                             int kk, int n_sink, int n_local,
+                                             int32_t* __restrict__ out, int stride,
+                                             int32_t* __restrict__ count_out,
+                                             int32_t* __restrict__ out_lds,
+                                             int32_t* __restrict__ count_lds, int lane) {
   using namespace topk_detail;
-  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nf = min(n, n_sink + n_local);
-  const int per = (n + NW - 1) / NW;
-  // Local top kk of wave w's range [lo, hi): candidate ids to cand[w kk ..
-  // (w + 1) kk), in index order, -1 after the last.
-  int32_t* cand = (int32_t*)hist;
-  const int lo = min(n, w * per), hi = min(n, lo + per);
-  const int ru1 = R1 <= 2 ? R1 : (hi - lo + 63) / 64;  // keys past hi are 0, never counted
-  uint32_t kv[R1];
-  int32_t ix[R1];
-#pragma unroll
-  for (int u = 0; u < R1; ++u) {
-    const int i = lo + 64 * u + lane;
-    ix[u] = i;
-    kv[u] = (u < ru1 && i < hi) ? keys[i] : 0u;
-  }
-  uint32_t tau = 0, rr = 0, mem = 0;  // fewer than kk candidates: take them all
-  if (count_ge<R1>(kv, ru1, 1u) > (uint32_t)kk) {
-    tau = select_threshold<R1>(kv, ru1, (uint32_t)kk, 31);
-    const uint32_t above = count_ge<R1>(kv, ru1, tau + 1u);
-    mem = count_ge<R1>(kv, ru1, tau) - above;
-    rr = (uint32_t)kk - above;
-  }
-  const uint32_t c = reg_compact<R1>(kv, ix, ru1, n, 0, 0, tau, rr, 0u, mem, nullptr,
-                                     cand + w * kk, 0u);
-  for (int j = (int)c + lane; j < kk; j += 64) cand[w * kk + j] = -1;
-  __syncthreads();
-  if (w != 0) return;
-  // One wave selects kk of the candidates; slot order is index order. The
-  // forced prefix [0, ns) and suffix [ss, n) frame them in the output.
-  const int nsl = NW * kk, ru2 = R2 <= 4 ? R2 : (nsl + 63) / 64;
+  const int ru2 = R2 <= 4 ? R2 : (nsl + 63) / 64;
   uint32_t cv[R2];
   int32_t cx[R2];
 #pragma unroll
@@ -457,6 +429,144 @@ __device__ __forceinline__ void block_union_select(const uint32_t* __restrict__ 
   }
 }
 
+// Exact block select by local top-kk lists (see the top of the file): wave
+// w selects the kk best keys of its range of ceil(n / NW) <= 64 R1 keys, then
+// wave 0 selects kk of the NW kk <= 64 R2 candidates. hist: LDS for the
+// candidate ids. Called by every thread with 0 < kk < the candidate count.
+template <int NW, int R1, int R2>
+__device__ __forceinline__ void block_union_select(const uint32_t* __restrict__ keys,
+                                                   uint32_t* __restrict__ hist, int n, int kk,
+                                                   int n_sink, int n_local,
+                                                   int32_t* __restrict__ out, int stride,
+                                                   int32_t* __restrict__ count_out,
+                                                   int32_t* __restrict__ out_lds,
+                                                   int32_t* __restrict__ count_lds) {
+  using namespace topk_detail;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int per = (n + NW - 1) / NW;
+  // Local top kk of wave w's range [lo, hi): candidate ids to cand[w kk ..
+  // (w + 1) kk), in index order, -1 after the last.
+  int32_t* cand = (int32_t*)hist;
+  const int lo = min(n, w * per), hi = min(n, lo + per);
+  const int ru1 = R1 <= 2 ? R1 : (hi - lo + 63) / 64;  // keys past hi are 0, never counted
+  uint32_t kv[R1];
+  int32_t ix[R1];
+#pragma unroll
+  for (int u = 0; u < R1; ++u) {
+    const int i = lo + 64 * u + lane;
+    ix[u] = i;
+    kv[u] = (u < ru1 && i < hi) ? keys[i] : 0u;
+  }
+  uint32_t tau = 0, rr = 0, mem = 0;  // fewer than kk candidates: take them all
+  if (count_ge<R1>(kv, ru1, 1u) > (uint32_t)kk) {
+    tau = select_threshold<R1>(kv, ru1, (uint32_t)kk, 31);
+    const uint32_t above = count_ge<R1>(kv, ru1, tau + 1u);
+    mem = count_ge<R1>(kv, ru1, tau) - above;
+    rr = (uint32_t)kk - above;
+  }
+  const uint32_t c = reg_compact<R1>(kv, ix, ru1, n, 0, 0, tau, rr, 0u, mem, nullptr,
+                                     cand + w * kk, 0u);
+  for (int j = (int)c + lane; j < kk; j += 64) cand[w * kk + j] = -1;
+  __syncthreads();
+  if (w != 0) return;
+  final_select<R2>(keys, cand, NW * kk, n, kk, n_sink, n_local, out, stride, count_out, out_lds,
+                   count_lds, lane);
+}
+
+// Exact block select by a lower bound (see the top of the file): wave w
+// takes the q = ceil(kk / NW) largest keys of its range of ceil(n / NW) <=
+// 64 R1 keys by q rounds of wave max (each round takes every key equal to
+// the maximum, so ties count fully) and reports the smallest taken, T_w, and
+// how many it took, c_w. Every key >= min_w T_w is a survivor: at least
+// sum_w c_w keys reach that bound, so when that sum is >= kk the kk-th
+// largest key does too, and the survivors hold the whole selection,
+// boundary ties included. The survivors' ids go to hist in index order and
+// one wave selects kk of them. Returns false, after a barrier and with
+// nothing written, when the bound does not hold (some ranges hold fewer than
+// q candidates) or more than 256 keys survive; the caller then selects
+// another way. red: 2 NW words; hist: kSelectHistWords words. Called by
+// every thread with 0 < kk < the candidate count and q <= kMaxBoundRounds.
+constexpr int kMaxBoundRounds = 8;
+template <int NW, int R1>
+__device__ __forceinline__ bool block_bounded_select(const uint32_t* __restrict__ keys,
+                                                     uint32_t* __restrict__ hist,
+                                                     uint32_t* __restrict__ red, int n, int kk,
+                                                     int n_sink, int n_local,
+                                                     int32_t* __restrict__ out, int stride,
+                                                     int32_t* __restrict__ count_out,
+                                                     int32_t* __restrict__ out_lds,
+                                                     int32_t* __restrict__ count_lds) {
+  using namespace topk_detail;
+  static_assert(NW <= 16, "survivor counts at the end of hist");
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int per = (n + NW - 1) / NW;
+  const int lo = min(n, w * per), hi = min(n, lo + per);
+  const int ru1 = R1 <= 2 ? R1 : (hi - lo + 63) / 64;  // keys past hi are 0
+  uint32_t kv[R1], work[R1];
+  int32_t ix[R1];
+#pragma unroll
+  for (int u = 0; u < R1; ++u) {
+    const int i = lo + 64 * u + lane;
+    ix[u] = i;
+    kv[u] = (u < ru1 && i < hi) ? keys[i] : 0u;
+    work[u] = kv[u];
+  }
+  const int q = (kk + NW - 1) / NW;
+  uint32_t taken = 0, tw = 0;
+  for (int round = 0; round < q; ++round) {
+    uint32_t lm = 0u;
+#pragma unroll
+    for (int u = 0; u < R1; ++u)
+      if (u < ru1) lm = max(lm, work[u]);
+    const uint32_t v = wave_max(lm);
+    if (v == 0u) break;  // no key left in the range
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < R1; ++u) {
+      if (u < ru1) {
+        const bool e = work[u] == v;
+        c += (uint32_t)__popcll(__ballot(e));
+        work[u] = e ? 0u : work[u];
+      }
+    }
+    taken += __builtin_amdgcn_readfirstlane(c);
+    tw = v;
+    if (taken >= (uint32_t)q) break;
+  }
+  if (lane == 0) {
+    red[w] = tw;
+    red[NW + w] = taken;
+  }
+  __syncthreads();
+  const uint32_t cw = lane < NW ? red[NW + lane] : 0u;
+  const uint32_t tl = lane < NW ? red[lane] : 0u;
+  const uint32_t bound = ~wave_max(cw ? ~tl : 0u);  // min of T_w over ranges that took keys
+  const uint32_t reach = __builtin_amdgcn_readlane(prefix_sum(cw), 63);
+  const uint32_t mine = count_ge<R1>(kv, ru1, bound);
+  uint32_t* scount = hist + kSelectHistWords - 16;
+  if (lane == 0) scount[w] = mine;
+  __syncthreads();
+  const uint32_t sv = lane < NW ? scount[lane] : 0u;
+  const uint32_t pre = prefix_sum(sv);
+  const uint32_t S = __builtin_amdgcn_readlane(pre, 63);
+  const uint32_t off = __builtin_amdgcn_readlane(pre - sv, w);
+  if (reach < (uint32_t)kk || S > 256u) {  // the same decision in every wave
+    __syncthreads();  // every wave is done with red and hist
+    return false;
+  }
+  int32_t* cand = (int32_t*)hist;
+  reg_compact<R1>(kv, ix, ru1, n, 0, 0, bound - 1u, 0u, 0u, 0u, nullptr, cand, off);
+  __syncthreads();
+  if (w != 0) return true;
+  if (S <= 64u)
+    final_select<1>(keys, cand, (int)S, n, kk, n_sink, n_local, out, stride, count_out, out_lds,
+                    count_lds, lane);
+  else
+    final_select<4>(keys, cand, (int)S, n, kk, n_sink, n_local, out, stride, count_out, out_lds,
+                    count_lds, lane);
+  return true;
+}
+
 // Select for one segment with all NW waves of a block (every thread calls
 // it; n is the same for all). keys as for wave_select_keys; `hist` is
 // kSelectHistWords words of LDS, `red` 2 * NW more. The min / max sweep and each digit pass's histogram
@@ -483,6 +593,15 @@ __device__ __forceinline__ void block_select_keys(uint32_t* __restrict__ keys,
   const int nc = n - nf;
   const int kk = min(k, nc);
   const int per = (n + NW - 1) / NW;
+  if (mode == VX_TOPK_EXACT && kk > 0 && kk < nc && per <= 512 &&
+      (kk + NW - 1) / NW <= kMaxBoundRounds) {
+    const bool done =
+        per <= 128 ? block_bounded_select<NW, 2>(keys, hist, red, n, kk, n_sink, n_local, out,
+                                                 stride, count_out, out_lds, count_lds)
+                   : block_bounded_select<NW, 8>(keys, hist, red, n, kk, n_sink, n_local, out,
+                                                 stride, count_out, out_lds, count_lds);
+    if (done) return;
+  }
   if (mode == VX_TOPK_EXACT && kk > 0 && kk < nc && per <= 512 && NW * kk <= kSelectHistWords) {
     if (per <= 128 && NW * kk <= 256)
       block_union_select<NW, 2, 4>(keys, hist, n, kk, n_sink, n_local, out, stride, count_out,

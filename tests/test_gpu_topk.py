@@ -130,3 +130,37 @@ def test_topk_maximum_segment(mode):
             want = O.topk_approx(scores[b], 200, 1, 2, int(rnd[b, 0]))
         np.testing.assert_array_equal(sel[b, 0][:len(want)], want)  # padded with -1
         assert cnt[b, 0] == int((want >= 0).sum())
+
+
+@pytest.mark.parametrize("case", ["few_survivors", "many_survivors", "tied_fallback",
+                                  "short_ranges_fallback"])
+def test_topk_block_bound_cases(case):
+    """Segments of more than 256 pages go to the block select, whose exact
+    path first bounds the k-th largest key from below by each wave's
+    ceil(k / waves) largest keys and selects among the keys at or above the
+    bound. Cases: distinct scores with a small k (few survivors) and a larger
+    k (up to 256 survivors); scores from 5 values (more than 256 keys tie at
+    the bound: the select falls back to its other paths); a sink long enough
+    to leave the first wave's range without candidates, so the ranges' keys
+    do not reach k (fallback as well). Each against the oracle, bit-exact."""
+    rng = np.random.default_rng(77)
+    hkv = 1
+    if case == "few_survivors":
+        ns, k, n_sink, n_local = np.array([1024, 700]), 32, 1, 1
+        scores = [rng.standard_normal(n).astype(np.float32) for n in ns]
+    elif case == "many_survivors":
+        ns, k, n_sink, n_local = np.array([1024, 2048]), 64, 1, 1
+        scores = [rng.standard_normal(n).astype(np.float32) for n in ns]
+    elif case == "tied_fallback":
+        ns, k, n_sink, n_local = np.array([1024, 600]), 32, 1, 1
+        scores = [rng.integers(0, 5, size=n).astype(np.float32) for n in ns]
+    else:
+        ns, k, n_sink, n_local = np.array([270, 300]), 64, 40, 1
+        scores = [rng.standard_normal(n).astype(np.float32) for n in ns]
+    rnd = np.zeros((len(ns), hkv), dtype=np.uint32)
+    sel, cnt = run_topk(ns, scores, hkv, k, n_sink, n_local, V.VX_TOPK_EXACT, rnd)
+    for b in range(len(ns)):
+        want = O.topk_exact(scores[b].astype(np.float64), k, n_sink, n_local)
+        np.testing.assert_array_equal(sel[b, 0][:len(want)], want, err_msg=f"{case} b={b}")
+        assert (sel[b, 0][len(want):] == -1).all()
+        assert cnt[b, 0] == len(want)
