@@ -242,7 +242,7 @@ VX_DEV void mfma_finish(MfmaShared<G, NW>& sm, const MfmaState& st, int b, int g
         lse[(size_t)b * hq + head] = lsum > 0.f ? (mmax + log2f(lsum)) * kLn2 : -INFINITY;
     } else {
       const size_t ps = ((size_t)b * hq + head) * S + s;
-      part_o[ps * DK + d] = acc;
+      __builtin_nontemporal_store(acc, part_o + ps * DK + d);  // read once, by the merge
       if (d == 0) {
         part_ml[2 * ps] = mmax;
         part_ml[2 * ps + 1] = lsum;

@@ -264,7 +264,9 @@ VX_DEV void vec_attend(VecShared<G, DK>& sm, const int* pg_phys, const int* pg_n
         lse[(size_t)b * hq + head] = lsum > 0.f ? (mmax + log2f(lsum)) * kLn2 : -INFINITY;
     } else {
       const size_t ps = ((size_t)b * hq + head) * S + s;
-      *(float4*)(part_o + ps * DK + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(f4v{acc[0], acc[1], acc[2], acc[3]},
+                                  (f4v*)(part_o + ps * DK + d));  // read once, by the merge
       if (d == 0) {
         part_ml[2 * ps] = mmax;
         part_ml[2 * ps + 1] = lsum;

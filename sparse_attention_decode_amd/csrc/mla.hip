@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
 // of its own token; the sums are reduced once, at the end.
 constexpr int CHT = 64;                   // tokens per chunk (one page)
 constexpr int kChunkLoads = CHT * DK / 8 / 64;   // 72 wave-wide 16-byte loads
+constexpr int kCpolNT = 2;  // cache-policy operand of the direct loads: non-temporal
 constexpr int kSlotBytes = kChunkLoads * 1024;
 constexpr int PROW = CHT + 8;             // padded P row (bf16), 144 B
 constexpr float kLazy = 8.f;
@@ -298,8 +299,9 @@ __device__ __forceinline__ void mla_attend(uint8_t* slot0, uint8_t* slot1, uint1
       const int i = w + NW * k;
       const int off = k < 64 / NW ? 4 * (i & 15) * DK + 128 * (i >> 4) + src_lat
                                   : 8 * (i - 64) * DK + src_rope;
+      // cache policy nt: each page is read once per step
       __builtin_amdgcn_global_load_lds((const void*)(page + off), (lds_void*)(slot + 1024 * NW * k),
-                                       16, 0, 0);
+                                       16, 0, kCpolNT);
     }
   };
   // Chunk c: consumed from `slot`; chunk c + 1 streams into `other`.
@@ -441,8 +443,10 @@ __device__ __forceinline__ void mla_attend(uint8_t* slot0, uint8_t* slot1, uint1
     } else {
       const size_t ps = ((size_t)b * HQ + head) * S + s;
       float* dst = part_o + ps * DV + d0;
-      *(float4*)dst = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
-      *(float4*)(dst + 4) = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
+      // Non-temporal: the partials are read once, by the merge, and a
+      // kernel's end then has no dirty L2 lines of them to write back.
+      __builtin_nontemporal_store(f32x4{o[0][i], o[1][i], o[2][i], o[3][i]}, (f32x4*)dst);
+      __builtin_nontemporal_store(f32x4{o[4][i], o[5][i], o[6][i], o[7][i]}, (f32x4*)(dst + 4));
       if (u == 0 && col == 0) {
         part_ml[2 * ps] = mrow[i];
         part_ml[2 * ps + 1] = l;

@@ -135,6 +135,11 @@ constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxi
 // have every load in flight at once; the arithmetic and its order are the
 // same for any S (so every merge writes the same bits).
 constexpr int kMergeBatch = 16;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+VX_DEV float4 load_nt4(const float* p) {  // a partial row: read once
+  const f32x4v r = __builtin_nontemporal_load((const f32x4v*)p);
+  return make_float4(r.x, r.y, r.z, r.w);
+}
 VX_DEV void merge_row(int S, int dv, const float* __restrict__ po, const float* __restrict__ ml,
                       float* __restrict__ out, float* __restrict__ lse) {
   float mmax = kNegBig;
@@ -147,7 +152,7 @@ VX_DEV void merge_row(int S, int dv, const float* __restrict__ po, const float* 
     for (int s = 0; s < kMergeBatch; ++s) {
       if (s < S) {
         mlv[s] = *(const float2*)(ml + 2 * s);
-        x[s] = *(const float4*)(po + (size_t)s * dv);
+        x[s] = load_nt4(po + (size_t)s * dv);
       }
     }
 #pragma unroll
@@ -168,7 +173,7 @@ VX_DEV void merge_row(int S, int dv, const float* __restrict__ po, const float* 
     for (int s = 0; s < S; ++s) {
       const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
       wsum = fmaf(ml[2 * s + 1], wt, wsum);
-      const float4 xs = *(const float4*)(po + (size_t)s * dv);
+      const float4 xs = load_nt4(po + (size_t)s * dv);
       acc.x = fmaf(xs.x, wt, acc.x); acc.y = fmaf(xs.y, wt, acc.y);
       acc.z = fmaf(xs.z, wt, acc.z); acc.w = fmaf(xs.w, wt, acc.w);
     }
