@@ -329,6 +329,36 @@ vx_status vx_decode_step_static(const vx_pages* pages, const vx_geom* geom,
                                 int32_t* sel_count, float* out, float* lse,
                                 int32_t num_splits, hipStream_t stream);
 
+/* One generated token per sequence, then the whole step (Vortex paper note,
+ * "System design > 1. vFlow": the cache stage's statistic follows the newest
+ * token; "System design > 3. Execution backend": sequence-local fusion).
+ * seq_lens already count the new token; k_new [batch][Hkv][Dk] (and v_new
+ * [batch][Hkv][Dv], NULL for MLA, whose values are the latent rows) hold its
+ * rows in the KV dtype. Writes the same bits as vx_centroid_update(pages,
+ * geom, k_pool, v_pool, first_token = -1 for every sequence, k_new, v_new,
+ * centroids, cent_bf16) followed by vx_decode_step(..., refresh_newest = 0,
+ * ...) with the remaining arguments. When vx_decode_step is one kernel
+ * (GQA), that kernel writes the rows into the token's slot and computes the
+ * page's centroid with the new key taken from k_new; otherwise the append
+ * kernel runs first. The same precondition as refresh_newest = 1: no
+ * sequence's newest physical page appears in another sequence's table.
+ * k_pool and v_pool are written. workspace == NULL: writes the bytes needed
+ * to *workspace_bytes (as for vx_decode_step) and returns VX_OK. Argument
+ * errors (VX_ERR_INVALID_ARG, as for vx_decode_step, plus a NULL k_new, or a
+ * NULL v_new without MLA, or a v_new with MLA, when batch > 0) are reported
+ * before any launch. */
+vx_status vx_append_decode_step(const vx_pages* pages, const vx_geom* geom,
+                                const void* q, void* k_pool, void* v_pool,
+                                const void* k_new, const void* v_new,
+                                float* centroids, void* cent_bf16,
+                                float score_scale, float sm_scale, int32_t k,
+                                int32_t n_sink, int32_t n_local, int32_t mode,
+                                const uint32_t* rand_u32, float* scores,
+                                int32_t* sel, int32_t sel_stride,
+                                int32_t* sel_count, float* out, float* lse,
+                                int32_t num_splits, void* workspace,
+                                size_t* workspace_bytes, hipStream_t stream);
+
 /* The whole step with the Quest-style indexer (GQA only; the mechanism is
  * Quest's, the other baseline of the Vortex paper note, "Paper context" and
  * "Key results > User-side latency"). Writes the same bits as

@@ -18,7 +18,7 @@ __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
     "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
     "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
-    "vx_bound_scores", "vx_bound_decode_step", "vx_decode_step_static", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
+    "vx_bound_scores", "vx_bound_decode_step", "vx_decode_step_static", "vx_append_decode_step", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
 
@@ -27,8 +27,9 @@ VX_F32, VX_BF16 = 0, 1
 VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
 ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
                 "vx_bounds_update", "vx_bound_scores", "vx_bound_decode_step",
-                "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static", "vx_plan_decode",
-                "vx_status_string", "vx_last_error", "vx_abi_version")
+                "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static",
+                "vx_append_decode_step", "vx_plan_decode", "vx_status_string", "vx_last_error",
+                "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
 
@@ -96,6 +97,11 @@ def load() -> ctypes.CDLL:
                                           c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                           c_int32, c_void_p, c_void_p, c_void_p, c_int32,
                                           c_void_p]
+    lib.vx_append_decode_step.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_float, c_float, c_int32, c_int32,
+                                          c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                          c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                          POINTER(c_size_t), c_void_p]
     lib.vx_plan_decode.argtypes = [P, G, c_int32, c_int32, c_int32, POINTER(VxPlan)]
     lib.vx_bounds_update.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.vx_bound_scores.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_int32, c_float,
@@ -106,8 +112,9 @@ def load() -> ctypes.CDLL:
                                          c_void_p, c_void_p, c_int32, c_void_p,
                                          POINTER(c_size_t), c_void_p]
     for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-                 "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static", "vx_plan_decode",
-                 "vx_bounds_update", "vx_bound_scores", "vx_bound_decode_step"):
+                 "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static",
+                 "vx_append_decode_step", "vx_plan_decode", "vx_bounds_update", "vx_bound_scores",
+                 "vx_bound_decode_step"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -238,6 +245,25 @@ def vx_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, centroids, c
                                  n_sink, n_local, mode, _ptr(rand_u32), _ptr(scores), _ptr(sel),
                                  sel_stride, _ptr(sel_count), _ptr(out), _ptr(lse), num_splits,
                                  _ptr(workspace), ctypes.byref(nbytes), _stream(stream)))
+    return nbytes.value
+
+
+def vx_append_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, k_new, v_new,
+                          centroids, cent_bf16, score_scale: float, sm_scale: float, k: int,
+                          n_sink: int, n_local: int, mode: int, rand_u32, scores, sel,
+                          sel_stride: int, sel_count, out, lse, num_splits: int = 0,
+                          workspace=None, workspace_bytes: Optional[int] = None,
+                          stream=None) -> int:
+    """Append of the newest token's K/V rows + the whole step; with workspace=None only
+    returns the bytes needed."""
+    nbytes = _nbytes(workspace, workspace_bytes)
+    _check(load().vx_append_decode_step(ctypes.byref(pages), ctypes.byref(geom), _ptr(q),
+                                        _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                        _ptr(centroids), _ptr(cent_bf16), float(score_scale),
+                                        float(sm_scale), k, n_sink, n_local, mode,
+                                        _ptr(rand_u32), _ptr(scores), _ptr(sel), sel_stride,
+                                        _ptr(sel_count), _ptr(out), _ptr(lse), num_splits,
+                                        _ptr(workspace), ctypes.byref(nbytes), _stream(stream)))
     return nbytes.value
 
 

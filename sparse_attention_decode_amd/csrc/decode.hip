@@ -250,10 +250,15 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
-                                  const int32_t* order, hipStream_t s) {
+                                  const int32_t* order, const void* k_new, const void* v_new,
+                                  hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   SegArgs a{};
   a.order = order;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.vp = const_cast<void*>(v_pool);
+  a.dv = g.head_dim_v;
   a.m = m;
   a.hq = g.num_q_heads;
   a.hkv = g.num_kv_heads;

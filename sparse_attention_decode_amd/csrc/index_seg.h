@@ -52,6 +52,14 @@ struct SegArgs {
   int32_t* sel_count;
   int cap_keys;
   const int32_t* order;  // nullable: order[i] = the sequence block row i serves (whole step)
+  // Append (nullable, centroid indexer with refresh only): the newest token's
+  // key and value rows, [B][Hkv][Dk] and [B][Hkv][dv] of the KV type. The
+  // refresh then writes both into the token's slot (vp: the value pool) and
+  // sums the key from k_new for that slot.
+  const void* k_new;
+  const void* v_new;
+  void* vp;
+  int dv;
 };
 
 // What the waves other than wave 0 do while wave 0 selects: nothing.
@@ -184,18 +192,42 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
     } else {
       const KV* col = (const KV*)a.kp + ((size_t)pid * a.hkv + g) * P * DK + 4 * dl;
       constexpr int kTok = sizeof(KV) == 2 ? 32 : 16;
+      // Append: the new token (slot nv - 1) is written here; its key enters
+      // the sum from registers. Its rows are read back by the attention only
+      // after the block barrier below, which waits for these stores.
+      const bool app = a.k_new != nullptr;
+      const int slot = app ? nv - 1 : -1;
+      typename Quad<KV>::raw knew{};
+      if (app) {
+        using Raw = typename Quad<KV>::raw;
+        const size_t row = (size_t)b * a.hkv + g;
+        if (own) {
+          knew = Quad<KV>::load((const KV*)a.k_new + row * DK + 4 * dl);
+          *(Raw*)(const_cast<KV*>(col) + (size_t)slot * DK) = knew;
+        }
+        KV* vrow = (KV*)a.vp + (((size_t)pid * a.hkv + g) * P + slot) * a.dv;
+        for (int d = 4 * lane; d < a.dv; d += 256)
+          *(Raw*)(vrow + d) = Quad<KV>::load((const KV*)a.v_new + row * a.dv + d);
+      }
+      // Token-order sum; the new token is the page's last, added after the
+      // stored ones (the same order as summing it in place).
+      const int nsum = app ? nv - 1 : nv;
       float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int t0 = 0; t0 < nv; t0 += kTok) {
+      for (int t0 = 0; t0 < nsum; t0 += kTok) {
         typename Quad<KV>::raw x[kTok];
 #pragma unroll
         for (int t = 0; t < kTok; ++t)
-          if (own && t0 + t < nv) x[t] = Quad<KV>::load(col + (size_t)(t0 + t) * DK);
+          if (own && t0 + t < nsum) x[t] = Quad<KV>::load(col + (size_t)(t0 + t) * DK);
 #pragma unroll
         for (int t = 0; t < kTok; ++t)
-          if (own && t0 + t < nv) {
+          if (own && t0 + t < nsum) {
             const float4 v = Quad<KV>::widen(x[t]);
             s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
           }
+      }
+      if (app && own) {
+        const float4 v = Quad<KV>::widen(knew);
+        s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
       }
       const float fn = (float)nv;
       const float4 c4 = make_float4(s4.x / fn, s4.y / fn, s4.z / fn, s4.w / fn);

@@ -298,7 +298,7 @@ vx_status static_scratch(void** out) {
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 5; }
+int32_t vx_abi_version(void) { return 6; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {
@@ -505,25 +505,37 @@ vx_status vx_sparse_decode(const vx_pages* pages, const vx_geom* geom, const voi
   return VX_OK;
 }
 
-vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void* q,
-                         const void* k_pool, const void* v_pool, float* centroids,
-                         void* cent_bf16, int32_t refresh_newest, float score_scale,
-                         float sm_scale, int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
-                         const uint32_t* rand_u32, float* scores, int32_t* sel,
-                         int32_t sel_stride, int32_t* sel_count, float* out, float* lse,
-                         int32_t num_splits, void* workspace, size_t* workspace_bytes,
-                         hipStream_t stream) {
+namespace {
+
+// vx_decode_step, and with k_new (append) vx_append_decode_step: the new
+// token's rows are written and the newest page's centroid recomputed, by the
+// whole-step kernel's refresh when the step is one kernel, else by the
+// append kernel before the step's kernels (which then skip the refresh).
+vx_status decode_step_impl(const vx_pages* pages, const vx_geom* geom, const void* q,
+                           const void* k_pool, const void* v_pool, const void* k_new,
+                           const void* v_new, float* centroids, void* cent_bf16,
+                           int32_t refresh_newest, float score_scale, float sm_scale, int32_t k,
+                           int32_t n_sink, int32_t n_local, int32_t mode,
+                           const uint32_t* rand_u32, float* scores, int32_t* sel,
+                           int32_t sel_stride, int32_t* sel_count, float* out, float* lse,
+                           int32_t num_splits, void* workspace, size_t* workspace_bytes,
+                           hipStream_t stream) {
   vx_status st;
   if ((st = check_pages(pages)) != VX_OK) return st;
   if ((st = check_geom(geom)) != VX_OK) return st;
   VX_CHECK(workspace_bytes, VX_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  if (k_new || v_new) {
+    VX_CHECK(pages->batch == 0 || k_new, VX_ERR_INVALID_ARG, "k_new is NULL");
+    VX_CHECK(geom->mla ? !v_new : (pages->batch == 0 || v_new), VX_ERR_INVALID_ARG,
+             geom->mla ? "MLA takes no v_new (values are the latent rows)" : "v_new is NULL");
+  }
   if ((st = check_decode_args(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
                               out, workspace != nullptr)) != VX_OK)
     return st;
   if (workspace &&
-      (st = check_index_args(pages, geom, q, k_pool, centroids, cent_bf16, refresh_newest,
-                             score_scale, scores, k, n_sink, n_local, mode, rand_u32, sel,
-                             sel_stride, sel_count)) != VX_OK)
+      (st = check_index_args(pages, geom, q, k_pool, centroids, cent_bf16,
+                             k_new ? 1 : refresh_newest, score_scale, scores, k, n_sink, n_local,
+                             mode, rand_u32, sel, sel_stride, sel_count)) != VX_OK)
     return st;
   int cus = 0;
   if ((st = device_cus(&cus)) != VX_OK) return st;
@@ -548,10 +560,17 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
     }
     e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, nullptr,
-        refresh_newest,
-        score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
-        sel_count, out, lse, pages->max_pages, order, stream);
+        k_new ? 1 : refresh_newest, score_scale, sm_scale, scores, k, n_sink, n_local, mode,
+        rand_u32, sel, sel_stride, sel_count, out, lse, pages->max_pages, order, k_new, v_new,
+        stream);
     return hip_status(e, "decode step kernel launch");
+  }
+  if (k_new && pages->total_pages > 0) {
+    hipError_t e = vx::launch_centroid_append(meta_of(pages), *geom, const_cast<void*>(k_pool),
+                                              const_cast<void*>(v_new ? v_pool : nullptr), nullptr,
+                                              k_new, v_new, centroids, (uint16_t*)cent_bf16,
+                                              stream);
+    if (e != hipSuccess) return hip_status(e, "centroid kernel launch");
   }
   if (geom->mla && pages->total_pages > 0 &&
       vx::decode_step_mla_fusable(pages->max_pages, sel_stride)) {
@@ -584,6 +603,39 @@ vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void*
     return st;
   return vx_sparse_decode(pages, geom, q, k_pool, v_pool, sel, sel_stride, sel_count, sm_scale,
                           out, lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+}  // namespace
+
+vx_status vx_decode_step(const vx_pages* pages, const vx_geom* geom, const void* q,
+                         const void* k_pool, const void* v_pool, float* centroids,
+                         void* cent_bf16, int32_t refresh_newest, float score_scale,
+                         float sm_scale, int32_t k, int32_t n_sink, int32_t n_local, int32_t mode,
+                         const uint32_t* rand_u32, float* scores, int32_t* sel,
+                         int32_t sel_stride, int32_t* sel_count, float* out, float* lse,
+                         int32_t num_splits, void* workspace, size_t* workspace_bytes,
+                         hipStream_t stream) {
+  return decode_step_impl(pages, geom, q, k_pool, v_pool, nullptr, nullptr, centroids, cent_bf16,
+                          refresh_newest, score_scale, sm_scale, k, n_sink, n_local, mode,
+                          rand_u32, scores, sel, sel_stride, sel_count, out, lse, num_splits,
+                          workspace, workspace_bytes, stream);
+}
+
+vx_status vx_append_decode_step(const vx_pages* pages, const vx_geom* geom, const void* q,
+                                void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                                float* centroids, void* cent_bf16, float score_scale,
+                                float sm_scale, int32_t k, int32_t n_sink, int32_t n_local,
+                                int32_t mode, const uint32_t* rand_u32, float* scores,
+                                int32_t* sel, int32_t sel_stride, int32_t* sel_count, float* out,
+                                float* lse, int32_t num_splits, void* workspace,
+                                size_t* workspace_bytes, hipStream_t stream) {
+  // batch > 0 needs k_new (and v_new unless MLA); checked in decode_step_impl,
+  // which this call reaches with k_new set whenever there are sequences.
+  VX_CHECK(k_new || !pages || pages->batch == 0, VX_ERR_INVALID_ARG, "k_new is NULL");
+  return decode_step_impl(pages, geom, q, k_pool, v_pool, k_new, v_new, centroids, cent_bf16, 0,
+                          score_scale, sm_scale, k, n_sink, n_local, mode, rand_u32, scores, sel,
+                          sel_stride, sel_count, out, lse, num_splits, workspace, workspace_bytes,
+                          stream);
 }
 
 vx_status vx_decode_step_static(const vx_pages* pages, const vx_geom* geom, const void* q,
@@ -676,7 +728,7 @@ vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom, const
     e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, nullptr, nullptr, bounds, refresh_newest,
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
-        sel_count, out, lse, pages->max_pages, order, stream);
+        sel_count, out, lse, pages->max_pages, order, nullptr, nullptr, stream);
     return hip_status(e, "decode step kernel launch");
   }
   if ((st = vx_bound_scores(pages, geom, q, k_pool, bounds, refresh_newest, score_scale, scores,

@@ -235,7 +235,8 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
-                                  const int32_t* order, hipStream_t s);
+                                  const int32_t* order, const void* k_new, const void* v_new,
+                                  hipStream_t s);
 // order[r] = the sequence with the r-th most pages in use (ties: lower index
 // first), for the whole-step kernel's block order. batch <= kMaxOrderedBatch.
 hipError_t launch_rank_sequences(const Meta& m, int32_t* order, hipStream_t s);

@@ -151,11 +151,8 @@ class DecodeStep:
                                self.k_out, self.sel_count, self.out, self.lse, self.num_splits,
                                self.workspace, self.workspace_bytes, stream)
 
-    def append_kv(self, stream=None) -> None:
-        """Cache stage of an appending decode step: write each sequence's new
-        token's K/V (self.k_new / self.v_new) into the slot of its newest
-        token and recompute that page's centroid (vx_centroid_update with
-        first_token = -1, k_new and v_new)."""
+    def _draw_new(self) -> None:
+        """The appended token's K/V rows (seeded, drawn once)."""
         w = self.w
         if self.k_new is None:
             s = w.spec
@@ -167,17 +164,43 @@ class DecodeStep:
             if not s.mla:
                 self.v_new = torch.randn(shape + (s.head_dim_v,), generator=g,
                                          device=w.device).to(w.k_pool.dtype)
+
+    def append_kv(self, stream=None) -> None:
+        """Cache stage of an appending decode step: write each sequence's new
+        token's K/V (self.k_new / self.v_new) into the slot of its newest
+        token and recompute that page's centroid (vx_centroid_update with
+        first_token = -1, k_new and v_new)."""
+        w = self.w
+        self._draw_new()
         V.vx_centroid_update(self.pages, self.geom, w.k_pool,
                              None if w.spec.mla else w.v_pool, self.newest, self.k_new,
                              self.v_new, self.centroids, self.cent_bf16, stream)
 
-    def run_append(self, stream=None) -> None:
-        """An appending decode step: the new token's K/V slot write and its
-        page's centroid (append_kv), then the indexer and attention without a
-        second refresh."""
-        self.append_kv(stream)
+    def append_step(self, stream=None) -> None:
+        """vx_append_decode_step: the new token's K/V rows and its page's
+        centroid, then the indexer and the attention, in one call (one kernel
+        when the step is)."""
+        w = self.w
+        self._draw_new()
+        V.vx_append_decode_step(self.pages, self.geom, w.q, w.k_pool,
+                                None if w.spec.mla else w.v_pool, self.k_new, self.v_new,
+                                self.centroids, self.cent_bf16, self.score_scale, self.sm_scale,
+                                self.k, self.n_sink, self.n_local, self.mode, w.d_rand_u32,
+                                self.scores, self.sel, self.k_out, self.sel_count, self.out,
+                                self.lse, self.num_splits, self.workspace, self.workspace_bytes,
+                                stream)
+
+    def run_append(self, stream=None, one_call: bool = True) -> None:
+        """An appending decode step: vx_append_decode_step, or (one_call =
+        False) its two calls: the new token's K/V slot write and its page's
+        centroid (append_kv), then the indexer and attention without a second
+        refresh."""
         if self.indexer == "bounds":
             raise ValueError("the appending step is built for the centroid indexer")
+        if one_call:
+            self.append_step(stream)
+            return
+        self.append_kv(stream)
         self.step(refresh=False, stream=stream)
 
     def plan(self) -> dict:

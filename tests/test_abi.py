@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 5
+    assert lib.vx_abi_version() == 6
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -360,3 +360,31 @@ def test_bound_decode_step_argument_checks():
     assert call(bounds=None) == V.VX_ERR_INVALID_ARG
     assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
     assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
+
+
+def test_append_decode_step_argument_checks():
+    """vx_append_decode_step: vx_decode_step's checks plus the new token's
+    rows (k_new always, v_new without MLA, none with MLA), all before any HIP
+    call."""
+    p, g = pages(), geom()
+    ok = dict(q=BAD, k_pool=BAD, v_pool=BAD, k_new=BAD, v_new=BAD, centroids=BAD, cent_bf16=None,
+              sscale=1.0, smscale=1.0, k=4, n_sink=1, n_local=1, mode=0, rand_u32=None,
+              scores=BAD, sel=BAD, stride=6, count=BAD, out=BAD, lse=None, splits=0, pages=p,
+              geom=g)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return status_of(V.vx_append_decode_step, a["pages"], a["geom"], a["q"], a["k_pool"],
+                         a["v_pool"], a["k_new"], a["v_new"], a["centroids"], a["cent_bf16"],
+                         a["sscale"], a["smscale"], a["k"], a["n_sink"], a["n_local"], a["mode"],
+                         a["rand_u32"], a["scores"], a["sel"], a["stride"], a["count"], a["out"],
+                         a["lse"], a["splits"], workspace=BAD, workspace_bytes=1 << 30, stream=0)
+
+    assert call(k_new=None) == V.VX_ERR_INVALID_ARG
+    assert call(v_new=None) == V.VX_ERR_INVALID_ARG
+    mla = geom(hq=32, hkv=1, dk=576, dv=512, mla=1)
+    assert call(geom=mla, v_pool=None) == V.VX_ERR_INVALID_ARG  # v_new given with MLA
+    assert call(sscale=float("nan")) == V.VX_ERR_INVALID_ARG
+    assert call(stride=5) == V.VX_ERR_INVALID_ARG
+    assert call(out=None) == V.VX_ERR_INVALID_ARG
+    assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
