@@ -32,6 +32,72 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 }
 
 // ------------------------------------------------------------------ scoring
+// The centroid of sequence b's newest page (page n - 1, its valid tokens
+// among L): thread t < DK / 4 sums columns 4t .. 4t+3 over the tokens in
+// order, all of its loads in flight at once, divides once (IEEE), and writes
+// the fp32 centroid, its bf16 copy and that copy to `row` (LDS).
+__device__ __forceinline__ void mla_newest_centroid(const Meta& m, const uint16_t* __restrict__ kp,
+                                                    float* __restrict__ cent32,
+                                                    uint16_t* __restrict__ cent, int b, int n,
+                                                    int L, uint16_t* __restrict__ row) {
+  constexpr int kQuads = DK / 4;  // 4-column groups of a key row
+  const int t = threadIdx.x;
+  const int P = m.page_size;
+  const int nv = min(P, L - (n - 1) * P);
+  const int pid = phys_page(m, m.indptr[b] + n - 1);
+  if (t < kQuads) {
+    const uint16_t* kb = kp + (size_t)pid * P * DK + 4 * t;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int t0 = 0; t0 < nv; t0 += 64) {
+      uint2 x[64];
+      // Loads past the last token repeat it (never added), so no load has a
+      // condition: one mask per load would not fit the scalar registers.
+#pragma unroll
+      for (int u = 0; u < 64; ++u) x[u] = *(const uint2*)(kb + (size_t)min(t0 + u, nv - 1) * DK);
+      // every load issued before the first add (the scheduler would
+      // otherwise interleave them and wait for each load in turn)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 64; ++u)
+        if (t0 + u < nv) {
+          s0 += bf16_lo(x[u].x); s1 += bf16_hi(x[u].x);
+          s2 += bf16_lo(x[u].y); s3 += bf16_hi(x[u].y);
+        }
+    }
+    const float fn = (float)nv;
+    const float c0 = s0 / fn, c1 = s1 / fn, c2 = s2 / fn, c3 = s3 / fn;
+    const size_t o = (size_t)pid * DK + 4 * t;
+    *(float4*)(cent32 + o) = make_float4(c0, c1, c2, c3);
+    const uint2 h = make_uint2((uint32_t)f32_to_bf16(c0) | ((uint32_t)f32_to_bf16(c1) << 16),
+                               (uint32_t)f32_to_bf16(c2) | ((uint32_t)f32_to_bf16(c3) << 16));
+    *(uint2*)(cent + o) = h;
+    *(uint2*)(row + 4 * t) = h;
+  }
+}
+
+// Score partial of this lane's page column: the 16 MT query rows staged in
+// LDS (qs) times the lane's centroid slice bf, summed over the rows and the
+// lane group; lanes of one column hold the same sum.
+template <int MT, int KS>
+__device__ __forceinline__ float mla_column_score(const uint16_t* __restrict__ qs,
+                                                  const u32x4 (&bf)[KS], int lane) {
+  const int col = lane & 15, q4 = lane >> 4;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* arow = qs + (16 * mt + col) * ROW + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma(*(const u32x4*)(arow + 32 * ks), bf[ks], acc[mt]);
+  }
+  float sc = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) sc += (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
+  sc += __shfl_xor(sc, 16);
+  sc += __shfl_xor(sc, 32);
+  return sc;
+}
+
 // grid (ceil(max_pages / 64) [+ 1 with refresh], B), 4 waves. Scoring block
 // x: wave w scores the 16 pages [64 x + 16 w, +16) of sequence blockIdx.y;
 // each lane loads its page id and centroid slice before the query rows are
@@ -84,35 +150,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
     for (int ks = 0; ks < KS; ++ks)
       bf[ks] = valid ? *(const u32x4*)(crow + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
   } else {
-    // Newest page: thread t < 144 sums columns 4t .. 4t+3 over the valid
-    // tokens in order, all of its loads in flight at once.
-    const int P = m.page_size;
-    const int nv = min(P, L - (n - 1) * P);
-    const int pid = phys_page(m, row0 + n - 1);
-    if (t < kQuads) {
-      const uint16_t* kb = kp + (size_t)pid * P * DK + 4 * t;
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-      for (int t0 = 0; t0 < nv; t0 += 64) {
-        uint2 x[64];
-#pragma unroll
-        for (int u = 0; u < 64; ++u)
-          if (t0 + u < nv) x[u] = *(const uint2*)(kb + (size_t)(t0 + u) * DK);
-#pragma unroll
-        for (int u = 0; u < 64; ++u)
-          if (t0 + u < nv) {
-            s0 += bf16_lo(x[u].x); s1 += bf16_hi(x[u].x);
-            s2 += bf16_lo(x[u].y); s3 += bf16_hi(x[u].y);
-          }
-      }
-      const float fn = (float)nv;
-      const float c0 = s0 / fn, c1 = s1 / fn, c2 = s2 / fn, c3 = s3 / fn;
-      const size_t o = (size_t)pid * DK + 4 * t;
-      *(float4*)(cent32 + o) = make_float4(c0, c1, c2, c3);
-      const uint2 h = make_uint2((uint32_t)f32_to_bf16(c0) | ((uint32_t)f32_to_bf16(c1) << 16),
-                                 (uint32_t)f32_to_bf16(c2) | ((uint32_t)f32_to_bf16(c3) << 16));
-      *(uint2*)(cent + o) = h;
-      *(uint2*)(newrow + 4 * t) = h;
-    }
+    mla_newest_centroid(m, kp, cent32, cent, b, n, L, newrow);
   }
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
@@ -129,19 +167,7 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
     return;
   }
 
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* arow = qs + (16 * mt + col) * ROW + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma(*(const u32x4*)(arow + 32 * ks), bf[ks], acc[mt]);
-  }
-  float sc = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) sc += (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
-  sc += __shfl_xor(sc, 16);
-  sc += __shfl_xor(sc, 32);
+  const float sc = mla_column_score<MT, KS>(qs, bf, lane);
   if (lane < 16 && valid) scores[row0 + p] = sc * scale;
 }
 
@@ -513,14 +539,57 @@ struct MlaStepArgs {
   float* part_o;
   float* part_ml;
   int cap_keys;
+  // Newest-page refresh in blocks B * S .. B * S + B - 1 (refresh_blocks):
+  // only when the newest page is forced, so its score is not needed by the
+  // selections read meanwhile.
+  int refresh_blocks;
+  float* cent32;
+  uint16_t* cent;
+  float score_scale;
+  float* scores_w;  // = scores
 };
 
-template <int MT>
+// The refresh the scorer's last block does (mla_newest_centroid, then that
+// page's score from the new bf16 row), for sequence b by a whole block of
+// the step kernel: qs and row are LDS (the attention's slots, unused here).
+template <int MT, int KS>
+__device__ __forceinline__ void mla_step_refresh(const MlaStepArgs& a, int b, uint16_t* qs,
+                                                 uint16_t* row) {
+  const Meta& m = a.m;
+  const int t = threadIdx.x, lane = t & 63;
+  const int row0 = m.indptr[b];
+  const int cap = m.indptr[b + 1] - row0;
+  const int L = seq_len_clamped(m, b);
+  const int n = min((L + m.page_size - 1) / m.page_size, cap);
+  if (n == 0) return;  // whole block: no barrier reached
+  const uint16_t* qb = a.q + (size_t)b * (16 * MT) * DK;
+  for (int c = t; c < 16 * MT * (DK / 8); c += blockDim.x)
+    *(u32x4*)(qs + (c / (DK / 8)) * ROW + 8 * (c % (DK / 8))) =
+        *(const u32x4*)(qb + (c / (DK / 8)) * DK + 8 * (c % (DK / 8)));
+  mla_newest_centroid(m, a.kp, a.cent32, a.cent, b, n, L, row);
+  __syncthreads();
+  if (t >= 64) return;
+  const int col = lane & 15, q4 = lane >> 4;
+  u32x4 bf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bf[ks] = col == 0 ? *(const u32x4*)(row + 8 * q4 + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+  const float sc = mla_column_score<MT, KS>(qs, bf, lane);
+  if (lane == 0) a.scores_w[row0 + n - 1] = sc * a.score_scale;
+}
+
+template <int MT, int KS>
 __global__ __launch_bounds__(256 * MT) void decode_mla_kernel(MlaStepArgs a) {
   VX_MLA_ATTN_LDS(MT)
   __shared__ int32_t cnt_l;
   constexpr int NW = 4 * MT;
   static_assert(kMaxPagesPerSplit <= 256 * MT, "one page-list entry per thread");
+  static_assert(DK / 4 <= 256 * MT, "the refresh takes one 4-column group per thread");
+  static_assert(16 * MT * ROW * 2 <= kSlotBytes, "the refresh stages the query rows in a slot");
+  if ((int)blockIdx.x >= a.m.batch * a.S) {  // whole block
+    mla_step_refresh<MT, KS>(a, blockIdx.x - a.m.batch * a.S, (uint16_t*)slot0, (uint16_t*)slot1);
+    return;
+  }
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int s = blockIdx.x % a.S, b = blockIdx.x / a.S;
   const Meta& m = a.m;
@@ -599,9 +668,15 @@ hipError_t launch_decode_step_mla(const Meta& m, const vx_geom& g, const void* q
                                   int n_local, int mode, const uint32_t* rnd, int32_t* sel,
                                   int sel_stride, int32_t* sel_count, float sm_scale,
                                   int num_splits, float* out, float* lse, float* part_o,
-                                  float* part_ml, int max_pages, hipStream_t s) {
+                                  float* part_ml, int max_pages, int refresh, float* cent32,
+                                  uint16_t* cent_bf16, float score_scale, hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   MlaStepArgs a{};
+  a.refresh_blocks = refresh;
+  a.cent32 = cent32;
+  a.cent = cent_bf16;
+  a.score_scale = score_scale;
+  a.scores_w = const_cast<float*>(scores);
   a.m = m;
   a.q = (const uint16_t*)q;
   a.kp = (const uint16_t*)k_pool;
@@ -621,13 +696,21 @@ hipError_t launch_decode_step_mla(const Meta& m, const vx_geom& g, const void* q
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.cap_keys = (max_pages + 63) / 64 * 64;
-  dim3 grid(m.batch * num_splits);
-  if (g.num_q_heads == 32)
-    hipLaunchKernelGGL(decode_mla_kernel<2>, grid, dim3(512), 0, s, a);
-  else if (g.num_q_heads == 16)
-    hipLaunchKernelGGL(decode_mla_kernel<1>, grid, dim3(256), 0, s, a);
-  else
+  dim3 grid(m.batch * num_splits + (refresh ? m.batch : 0));
+  const bool latent_only = g.score_dim == DV;
+  if (g.num_q_heads == 32) {
+    if (latent_only)
+      hipLaunchKernelGGL((decode_mla_kernel<2, DV / 32>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mla_kernel<2, KSTEPS>), grid, dim3(512), 0, s, a);
+  } else if (g.num_q_heads == 16) {
+    if (latent_only)
+      hipLaunchKernelGGL((decode_mla_kernel<1, DV / 32>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mla_kernel<1, KSTEPS>), grid, dim3(256), 0, s, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

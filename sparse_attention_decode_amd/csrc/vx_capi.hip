@@ -582,13 +582,19 @@ vx_status decode_step_impl(const vx_pages* pages, const vx_geom* geom, const voi
     float* part_o = nullptr;
     float* part_ml = nullptr;
     split_buffers(pages, geom, S, workspace, &part_o, &part_ml);
+    // With the newest page forced (n_local >= 1) its score takes no part in
+    // the selections, so its refresh runs in extra blocks of the step kernel,
+    // beside the attention, instead of at the end of the scorer; the scorer
+    // scores it from the old centroid and the refresh then writes its score.
+    const int late = refresh_newest && n_local >= 1;
     hipError_t e = vx::launch_scores_mla_sized(m, *geom, q, k_pool, centroids,
-                                               (uint16_t*)cent_bf16, refresh_newest, score_scale,
-                                               scores, pages->max_pages, stream);
+                                               (uint16_t*)cent_bf16, late ? 0 : refresh_newest,
+                                               score_scale, scores, pages->max_pages, stream);
     if (e != hipSuccess) return hip_status(e, "score kernel launch");
     e = vx::launch_decode_step_mla(m, *geom, q, k_pool, scores, k, n_sink, n_local, mode,
                                    rand_u32, sel, sel_stride, sel_count, sm_scale, S, out, lse,
-                                   part_o, part_ml, pages->max_pages, stream);
+                                   part_o, part_ml, pages->max_pages, late, centroids,
+                                   (uint16_t*)cent_bf16, score_scale, stream);
     if (e != hipSuccess) return hip_status(e, "decode step kernel launch");
     if (S > 1) {
       e = vx::launch_merge(pages->batch, geom->num_q_heads, geom->head_dim_v, S, part_o, part_ml,

@@ -270,7 +270,8 @@ hipError_t launch_decode_step_mla(const Meta& m, const vx_geom& g, const void* q
                                   int n_local, int mode, const uint32_t* rnd, int32_t* sel,
                                   int sel_stride, int32_t* sel_count, float sm_scale,
                                   int num_splits, float* out, float* lse, float* part_o,
-                                  float* part_ml, int max_pages, hipStream_t s);
+                                  float* part_ml, int max_pages, int refresh, float* cent32,
+                                  uint16_t* cent_bf16, float score_scale, hipStream_t s);
 // Quest-style page bounds (GQA): rebuild every entry (first_token NULL) or
 // refresh each sequence's pages from first_token[b]; bounds in the KV dtype.
 hipError_t launch_bounds_update(const Meta& m, const vx_geom& g, const void* k_pool,
