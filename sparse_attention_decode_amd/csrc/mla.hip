@@ -459,16 +459,31 @@ __device__ __forceinline__ void mla_attend(uint8_t* slot0, uint8_t* slot1, uint1
       if (lse && u == 0 && col == 0)
         lse[(size_t)b * HQ + head] = l > 0.f ? (mrow[i] + log2f(l)) * kLn2 : -INFINITY;
     } else {
-      const size_t ps = ((size_t)b * HQ + head) * S + s;
-      float* dst = part_o + ps * DV + d0;
-      // Non-temporal: the partials are read once, by the merge, and a
-      // kernel's end then has no dirty L2 lines of them to write back.
-      __builtin_nontemporal_store(f32x4{o[0][i], o[1][i], o[2][i], o[3][i]}, (f32x4*)dst);
-      __builtin_nontemporal_store(f32x4{o[4][i], o[5][i], o[6][i], o[7][i]}, (f32x4*)(dst + 4));
+      // The split's partial rows go through slot0 (no chunk is in flight or
+      // read any more), stored below as whole rows.
+      float* tile = (float*)slot0;
+      *(f32x4*)(tile + head * DV + d0) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+      *(f32x4*)(tile + head * DV + d0 + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
       if (u == 0 && col == 0) {
+        const size_t ps = ((size_t)b * HQ + head) * S + s;
         part_ml[2 * ps] = mrow[i];
         part_ml[2 * ps + 1] = l;
       }
+    }
+  }
+  if (S > 1) {
+    // Non-temporal stores (the partials are read once, by the merge, and a
+    // kernel's end then has no dirty L2 lines of them to write back), each
+    // covering 1 KB of a row: from the registers' layout (8 columns per
+    // lane, lanes 32 B apart) every store would fill half lines, which the
+    // memory then writes twice (21.6 against 14.7 MB per step).
+    static_assert(16 * MT * DV * 4 <= kSlotBytes, "the partial rows fit in a slot");
+    __syncthreads();
+    const float* tile = (const float*)slot0;
+    for (int c = t; c < HQ * DV / 4; c += 64 * NW) {
+      const int head = c / (DV / 4), d = 4 * (c % (DV / 4));
+      __builtin_nontemporal_store(*(const f32x4*)(tile + head * DV + d),
+                                  (f32x4*)(part_o + (((size_t)b * HQ + head) * S + s) * DV + d));
     }
   }
 }
