@@ -132,6 +132,13 @@ typedef struct vx_plan {
                                 first on the device (segments span more than
                                 two rounds of blocks); its workspace then
                                 holds 4 more bytes per sequence */
+  int32_t pair_segments;     /* R > 0: every whole-step block is resident
+                                from the start, two per compute unit, and
+                                block rows i and i + R (Hkv blocks a row)
+                                share compute units: the step kernel ranks
+                                the sequences by pages in use itself and
+                                gives rows i < R the longest, row R + k the
+                                k-th shortest; 0: not paired */
 } vx_plan;
 
 /* Cache stage: refresh the key centroids of pages.

@@ -56,7 +56,8 @@ class VxPlan(ctypes.Structure):
     _fields_ = [("num_splits", c_int32), ("pages_per_split", c_int32),
                 ("score_pages_per_block", c_int32), ("score_blocks", c_int32),
                 ("topk_threads", c_int32), ("num_cus", c_int32), ("fused_step", c_int32),
-                ("workspace_bytes", c_size_t), ("order_segments", c_int32)]
+                ("workspace_bytes", c_size_t), ("order_segments", c_int32),
+                ("pair_segments", c_int32)]
 
 
 _LIB: Optional[ctypes.CDLL] = None

@@ -22,8 +22,40 @@ namespace {
 // The segment (sequence b, KV head g) = b * Hkv + g this block serves: block
 // row i = blockIdx.x / Hkv takes sequence order[i] when the planner ordered
 // the sequences (longest first), else sequence i.
-__device__ __forceinline__ int block_segment(const SegArgs& a) {
+// With pair_rows = R: the sequences ranked by pages in use (most first,
+// ties: lower index first; the same count the index uses), rows i < R take
+// ranks 0 .. R - 1 and row R + k, which shares compute units with row k,
+// rank B - 1 - k: each compute unit then holds one long and one short
+// segment. Any order gives the same results (each segment is one block's
+// whole work); this one balances the compute units. Every thread calls it
+// (one barrier); counts: LDS, batch + 1 ints, free until the index phase.
+VX_DEV int paired_row(const SegArgs& a, int* counts, int* row) {
+  const Meta& m = a.m;
+  const int B = m.batch, P = m.page_size;
+  const int i = blockIdx.x / a.hkv;
+  const int want = i < a.pair_rows ? i : B - 1 - (i - a.pair_rows);
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int cap = m.indptr[b + 1] - m.indptr[b];
+    const int L = min(max(m.seq_lens[b], 0), cap * P);
+    counts[b] = min((L + P - 1) / P, cap);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int nb = counts[b];
+    int r = 0;
+    for (int j = 0; j < B; ++j) {
+      const int nj = counts[j];
+      r += (nj > nb || (nj == nb && j < b)) ? 1 : 0;
+    }
+    if (r == want) *row = b;
+  }
+  __syncthreads();
+  return *row;
+}
+
+__device__ __forceinline__ int block_segment(const SegArgs& a, int* counts, int* row) {
   const int i = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+  if (a.pair_rows > 0) return paired_row(a, counts, row) * a.hkv + g;
   if (!a.order) return blockIdx.x;
   const int b = a.order[i];
   return (b < 0 ? 0 : (b >= a.m.batch ? a.m.batch - 1 : b)) * a.hkv + g;
@@ -77,8 +109,9 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   __shared__ int pg_nv[kMaxPagesPerSplit];
   __shared__ MfmaShared<G, NW> sm;
   static_assert(kMaxPagesPerSplit <= 64 * NW, "one page-list entry per thread");
+  __shared__ int row_l;
 
-  const int seg = block_segment(a);
+  const int seg = block_segment(a, (int*)dyn, &row_l);
   const int b = seg / a.hkv, g = seg % a.hkv;
   const uint16_t* kp = (const uint16_t*)a.kp;
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
@@ -140,8 +173,9 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs 
   __shared__ int pg_nv[kMaxPagesPerSplit];
   __shared__ VecShared<G, DK> sm;
   static_assert(kMaxPagesPerSplit <= 64 * kVecWaves, "one page-list entry per thread");
+  __shared__ int row_l;
 
-  const int seg = block_segment(a);
+  const int seg = block_segment(a, (int*)dyn, &row_l);
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
   index_segment<KV, KV, DK, G, kVecWaves, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, NoIdle{},
                                                   false);
@@ -250,11 +284,12 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
-                                  const int32_t* order, const void* k_new, const void* v_new,
-                                  hipStream_t s) {
+                                  const int32_t* order, int pair_rows, const void* k_new,
+                                  const void* v_new, hipStream_t s) {
   if (m.batch == 0) return hipSuccess;
   SegArgs a{};
   a.order = order;
+  a.pair_rows = pair_rows;
   a.k_new = k_new;
   a.v_new = v_new;
   a.vp = const_cast<void*>(v_pool);

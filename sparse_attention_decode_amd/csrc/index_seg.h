@@ -52,6 +52,7 @@ struct SegArgs {
   int32_t* sel_count;
   int cap_keys;
   const int32_t* order;  // nullable: order[i] = the sequence block row i serves (whole step)
+  int pair_rows;         // > 0: block rows ranked in the kernel and paired (whole step)
   // Append (nullable, centroid indexer with refresh only): the newest token's
   // key and value rows, [B][Hkv][Dk] and [B][Hkv][dv] of the KV type. The
   // refresh then writes both into the token's slot (vp: the value pool) and

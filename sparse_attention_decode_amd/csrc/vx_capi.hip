@@ -1,6 +1,7 @@
 // C ABI of the block top-k sparse-attention decode step: argument checks,
 // the workload planner, and kernel dispatch. Every check here runs on the
 // host before any HIP call, so a rejected call touches no GPU state.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -245,6 +246,20 @@ vx_status make_plan(const vx_pages* p, const vx_geom* g, int sel_stride, int num
   // first, so the long segments start early and short ones fill the tail.
   out->order_segments = out->fused_step && items0 > 2L * num_cus &&
                         p->batch <= vx::kMaxOrderedBatch;
+  // Up to two rounds of 8-wave blocks are all resident from the start, two
+  // per compute unit, and the GPU places block j + num_cus beside block j:
+  // a row of long segments and a row of short ones then share each compute
+  // unit (ranked inside the step kernel, which is cheaper than a ranking
+  // launch for a batch this size).
+  const bool bf16_128 = g->kv_dtype == VX_BF16 && g->head_dim_k == 128;
+  const int waves = bf16_128 ? vx::gqa_attn_waves(g->num_q_heads / std::max(1, g->num_kv_heads),
+                                                  p->max_pages)
+                             : 8;
+  out->pair_segments = (out->fused_step && waves == 8 && items0 > num_cus &&
+                        items0 <= 2L * num_cus && num_cus % g->num_kv_heads == 0 &&
+                        p->batch <= vx::kMaxPairedBatch)
+                           ? num_cus / g->num_kv_heads
+                           : 0;
   return VX_OK;
 }
 
@@ -561,8 +576,8 @@ vx_status decode_step_impl(const vx_pages* pages, const vx_geom* geom, const voi
     e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, centroids, (uint16_t*)cent_bf16, nullptr,
         k_new ? 1 : refresh_newest, score_scale, sm_scale, scores, k, n_sink, n_local, mode,
-        rand_u32, sel, sel_stride, sel_count, out, lse, pages->max_pages, order, k_new, v_new,
-        stream);
+        rand_u32, sel, sel_stride, sel_count, out, lse, pages->max_pages, order,
+        plan.pair_segments, k_new, v_new, stream);
     return hip_status(e, "decode step kernel launch");
   }
   if (k_new && pages->total_pages > 0) {
@@ -734,7 +749,8 @@ vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom, const
     e = vx::launch_decode_step_gqa(
         meta_of(pages), *geom, q, k_pool, v_pool, nullptr, nullptr, bounds, refresh_newest,
         score_scale, sm_scale, scores, k, n_sink, n_local, mode, rand_u32, sel, sel_stride,
-        sel_count, out, lse, pages->max_pages, order, nullptr, nullptr, stream);
+        sel_count, out, lse, pages->max_pages, order, plan.pair_segments, nullptr, nullptr,
+        stream);
     return hip_status(e, "decode step kernel launch");
   }
   if ((st = vx_bound_scores(pages, geom, q, k_pool, bounds, refresh_newest, score_scale, scores,

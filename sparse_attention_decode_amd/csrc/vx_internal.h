@@ -235,8 +235,8 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
                                   float sm_scale, float* scores, int k, int n_sink, int n_local,
                                   int mode, const uint32_t* rnd, int32_t* sel, int stride,
                                   int32_t* sel_count, float* out, float* lse, int max_pages,
-                                  const int32_t* order, const void* k_new, const void* v_new,
-                                  hipStream_t s);
+                                  const int32_t* order, int pair_rows, const void* k_new,
+                                  const void* v_new, hipStream_t s);
 // order[r] = the sequence with the r-th most pages in use (ties: lower index
 // first), for the whole-step kernel's block order. batch <= kMaxOrderedBatch.
 hipError_t launch_rank_sequences(const Meta& m, int32_t* order, hipStream_t s);
@@ -297,6 +297,9 @@ inline int gqa_attn_waves(int G, int max_pages) {
 // Largest page capacity for which the whole-step kernel keeps every entry's
 // key and physical page in LDS.
 constexpr int kMaxFusedStepPages = 4096;
+// Largest batch the whole-step kernel ranks itself (each block compares every
+// sequence's page count against every other's).
+constexpr int kMaxPairedBatch = 256;
 // LDS words a segment's selection needs besides its keys: three 256-word
 // digit histograms and the block select's 2 * 16 reduction words.
 constexpr int kSelectHistWords = 3 * 256;  // three rotating digit histograms

@@ -179,10 +179,19 @@ def test_planner_orders_long_batches():
     plan = V.vx_plan_decode(big, g, 64, 0, 256)
     assert plan["fused_step"] == 1 and plan["order_segments"] == 1
     assert plan["workspace_bytes"] == 0  # vx_decode_step adds 256 x 4 bytes for the order
-    # one round (the long-generation shape, 512 segments): no ordering, no workspace
+    assert plan["pair_segments"] == 0
+    # every block resident from the start, two 8-wave blocks per compute unit
+    # (the long-generation shape, 512 segments on 256): no ranking launch, no
+    # workspace; the step kernel pairs 32 rows of long sequences with the rest
     plan = V.vx_plan_decode(pages(batch=64, nnz=81920, pool=102400, maxp=2052), geom(hq=32), 131,
                             0, 256)
     assert plan["fused_step"] == 1 and plan["order_segments"] == 0
+    assert plan["pair_segments"] == 32 and plan["workspace_bytes"] == 0
+    # one block per compute unit (256 segments), or 16-wave blocks: not paired
+    plan = V.vx_plan_decode(pages(batch=32, nnz=6144, pool=7680, maxp=256), geom(), 18, 0, 256)
+    assert plan["fused_step"] == 1 and plan["pair_segments"] == 0
+    plan = V.vx_plan_decode(pages(batch=48, nnz=9216, pool=11520, maxp=256), geom(), 18, 0, 256)
+    assert plan["fused_step"] == 1 and plan["pair_segments"] == 0
     # split plans are not whole-step kernels: never ordered
     plan = V.vx_plan_decode(big, g, 64, 3, 256)
     assert plan["order_segments"] == 0

@@ -218,6 +218,26 @@ def test_full_size_decode_step_equals_calls(name, fused):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,batch,lengths", [("largebatch_bf16", 40, ("uniform", 2000, 9000)),
+                                                ("longgen_bf16", 48, ("uniform", 8200, 12000))])
+def test_paired_rows_decode_step(name, batch, lengths):
+    """Between one and two rounds of 8-wave whole-step blocks (320 and 384
+    segments on 256 compute units) the step kernel ranks the sequences
+    itself and pairs rows of long sequences with rows of short ones: the same
+    bits as the separate calls, and the oracle's results on a sample."""
+    sp = W.spec(name, batch=batch, lengths=lengths, headroom_tokens=40)
+    w = W.make(sp, "cuda", seed=21)
+    one = step_vs_calls(w, appends=2)
+    plan = one.plan()
+    assert plan["fused_step"] == 1
+    segs = batch * sp.num_kv_heads
+    if plan["num_cus"] < segs <= 2 * plan["num_cus"] and plan["num_cus"] % sp.num_kv_heads == 0:
+        assert plan["pair_segments"] == plan["num_cus"] // sp.num_kv_heads
+    assert check_step_against_oracle(w, one, [0, batch // 2, batch - 1]) <= 1
+    del w, one
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["gqa_small", "large_small", "longgen_small"])
 def test_fused_decode_step_matches_oracle(name):
     """One split per segment (the whole-step kernel where the shape allows),
