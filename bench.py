@@ -574,7 +574,10 @@ def dense_compare(a):
 # workload's step appends a token (K/V slot write + that page's centroid),
 # and the two large ones also report the indexer in exact and approximate
 # top-k mode.
-EXTRA_WORKLOADS = ("mla_bf16", "longgen_bf16", "largebatch_bf16", "tiny_fp32")
+# The largest workload first: its 27 GB of pools, allocated after the other
+# workloads' pools have been freed, ran 3-5 % slower (the same kernels, a
+# different physical placement of the pools).
+EXTRA_WORKLOADS = ("largebatch_bf16", "mla_bf16", "longgen_bf16", "tiny_fp32")
 APPEND_WORKLOADS = ("longgen_bf16",)
 INDEX_MODE_WORKLOADS = ("longgen_bf16", "largebatch_bf16")
 
