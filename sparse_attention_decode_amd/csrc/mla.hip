@@ -98,8 +98,9 @@ __device__ __forceinline__ float mla_column_score(const uint16_t* __restrict__ q
   return sc;
 }
 
-// grid (ceil(max_pages / 64) [+ 1 with refresh], B), 4 waves. Scoring block
-// x: wave w scores the 16 pages [64 x + 16 w, +16) of sequence blockIdx.y;
+// grid (ceil(max_pages / 64) [+ 1 with refresh], B), 4 waves; the blocks
+// are renumbered XCD-major into (x, sequence b) below. Scoring block x: wave
+// w scores the 16 pages [64 x + 16 w, +16) of sequence b;
 // each lane loads its page id and centroid slice before the query rows are
 // staged, so the block waits on two dependent loads, not three. With
 // `refresh`, the last block of each row instead recomputes the sequence's
@@ -118,7 +119,11 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
   static_assert(kQuads <= 256, "the refresh takes one 4-column group per thread");
   __shared__ __attribute__((aligned(16))) uint16_t qs[16 * MT * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t newrow[DK];
-  const int b = blockIdx.y;
+  // A sequence's blocks on one XCD (its 37 KB of query rows fetched once
+  // there, not by all eight), its refresh block (the longest) dispatched
+  // first among them.
+  const int vb = xcd_major(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int b = vb / gridDim.x, bx = gridDim.x - 1 - vb % gridDim.x;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int col = lane & 15, q4 = lane >> 4;
@@ -127,9 +132,9 @@ __global__ __launch_bounds__(256) void scores_mla_kernel(Meta m, const uint16_t*
   const int L = seq_len_clamped(m, b);
   int n = (L + m.page_size - 1) / m.page_size;
   n = n > cap ? cap : n;
-  const bool refresh_block = refresh && blockIdx.x == gridDim.x - 1;
+  const bool refresh_block = refresh && bx == gridDim.x - 1;
   const int n_scored = refresh ? n - 1 : n;  // pages the scoring blocks take
-  const int blk0 = blockIdx.x * 64;
+  const int blk0 = bx * 64;
   if (refresh_block ? n == 0 : blk0 >= n_scored) return;  // whole block: no barrier reached
 
   // This sequence's query rows (16 * MT heads x 576), loaded now, stored in LDS below.

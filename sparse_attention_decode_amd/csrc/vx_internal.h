@@ -84,6 +84,17 @@ VX_DEV int seq_len_clamped(const Meta& m, int b) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// The dispatcher deals a launch's blocks to the chip's 8 XCDs (each with its
+// own L2) round-robin by linear block id. xcd_major(i, n) renumbers the
+// blocks [0, n) so that each XCD takes one contiguous run of the new ids:
+// blocks that read the same rows (one sequence's query rows) then share an
+// L2 instead of fetching them once per XCD. A bijection of [0, n).
+constexpr int kXcds = 8;
+VX_DEV int xcd_major(int i, int n) {
+  const int per = n / kXcds, extra = n % kXcds, x = i % kXcds, j = i / kXcds;
+  return x * per + (x < extra ? x : extra) + j;
+}
+
 VX_DEV int phys_page(const Meta& m, int j) {
   int p = m.page_ids[j];
   return p < 0 ? 0 : (p >= m.pool ? m.pool - 1 : p);
