@@ -116,6 +116,17 @@ typedef struct vx_geom {
    * note, "Key results > MLA": routing on the rope part matters; this option
    * measures how much). Attention always uses every column. */
   int32_t score_dim;
+  /* GQA with bf16 KV: 1 scores the pages on cent_bf16, the round-to-nearest-
+   * even bf16 copy of the fp32 centroids, instead of the fp32 rows (the
+   * indexer then reads half the bytes); every call that scores then needs
+   * cent_bf16 (vx_page_scores takes the copy as its `centroids`), and so
+   * does vx_centroid_update, which keeps the copy. The
+   * pages leave the centroids' storage precision open; the scores are the
+   * fp32 dot of the group-summed query with the bf16 values. 0: the fp32
+   * rows. Any other value: VX_ERR_INVALID_ARG; 1 with fp32 KV:
+   * VX_ERR_UNSUPPORTED. MLA always scores the bf16 copy and ignores it, and
+   * so do the Quest-style entry points (vx_bound_*), which score bounds. */
+  int32_t score_bf16;
 } vx_geom;
 
 /* Launch plan chosen by the workload planner (host only). */
@@ -171,7 +182,8 @@ vx_status vx_centroid_update(const vx_pages* pages, const vx_geom* geom,
  * product of the query with the centroids).
  * GQA: scores[g][j] = score_scale * sum_{h in group g} q[b][h] . centroids[pid][g]
  *   with fp32 centroids, evaluated as the dot of the fp32 group-summed query
- *   with the centroid row.
+ *   with the centroid row; with geom->score_bf16, centroids is the bf16 copy
+ *   [pool][Hkv][Dk] and the same dot runs on its values.
  * MLA: centroids is the bf16 copy [pool][576]; the [Hq x 576] x [576 x pages]
  *   product runs on bf16 MFMA with fp32 accumulation and is summed over the
  *   query heads: scores[0][j] = score_scale * sum_h q[b][h] . cent_bf16[pid].
@@ -244,7 +256,8 @@ vx_status vx_bound_scores(const vx_pages* pages, const vx_geom* geom,
  *      sequence's newest token (exactly vx_centroid_update with
  *      first_token[b] = -1 and no k_new: centroids, and cent_bf16 when given,
  *      are rewritten for that page);
- *   2. the scores of vx_page_scores (GQA reads `centroids`, MLA `cent_bf16`);
+ *   2. the scores of vx_page_scores (GQA reads `centroids`, or `cent_bf16`
+ *      with geom->score_bf16; MLA `cent_bf16`);
  *   3. the selection of vx_topk_pages over those scores;
  * and writes the same bits as those three calls in that order. For GQA it
  * is one kernel with a block per (sequence, KV head): the block streams that

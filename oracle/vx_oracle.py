@@ -32,7 +32,11 @@ the design notes of the repository):
   (score descending, logical index ascending) and the first min(k, #) kept;
   the selection is reported in ascending logical order;
 * the MLA scorer consumes bf16 operands: its centroids are rounded to bf16
-  (round to nearest, ties to even) before scoring.
+  (round to nearest, ties to even) before scoring;
+* a GQA scorer that keeps its centroids in bf16 (``score_bf16``) scores the
+  bf16 rounding (nearest, ties to even) of the cache stage's fp32 centroid
+  (``centroids_fp32``), the value such a store holds; the query is not
+  rounded.
 
 Parity status: the pages print no worked example, so every function here is
 pinned by closed forms, invariants, brute force or an independent library
@@ -329,12 +333,13 @@ def decode_sequence(seq: dict, *, page_size: int, num_kv_heads: int, k: int,
                     n_sink: int, n_local: int, score_scale: float,
                     sm_scale: float, mla: bool = False, head_dim_v: int = None,
                     approx: bool = False, score_dim: int = None,
-                    indexer: str = "centroid") -> dict:
+                    indexer: str = "centroid", score_bf16: bool = False) -> dict:
     """The whole step for one sequence: cache stage, scoring, selection,
     attention. ``seq`` holds q, k, v (v None for MLA), seq_len and rand_u32
     ([Hkv] uint32 draws for the approximate selection); ``score_dim`` as in
     page_scores; ``indexer`` "centroid" (the method) or "bounds" (Quest's
-    page bounds, GQA only)."""
+    page bounds, GQA only); ``score_bf16`` (GQA) scores the bf16 rounding of
+    the fp32 centroids (centroids_fp32) instead of the exact means."""
     q, kk, vv, L = seq["q"], seq["k"], seq["v"], seq["seq_len"]
     if mla:
         vv = kk[..., :head_dim_v]
@@ -343,7 +348,12 @@ def decode_sequence(seq: dict, *, page_size: int, num_kv_heads: int, k: int,
         lo, hi = page_bounds(kk, L, page_size)
         scores = bound_scores(q, lo, hi, num_kv_heads, score_scale)
     else:
-        score_cent = round_to_bf16(cent) if mla else cent
+        if mla:
+            score_cent = round_to_bf16(cent)
+        elif score_bf16:
+            score_cent = round_to_bf16(centroids_fp32(kk, L, page_size))
+        else:
+            score_cent = cent
         scores = page_scores(q, score_cent, num_kv_heads, score_scale, score_dim)
     k_out = k + n_sink + n_local
     sel = np.full((num_kv_heads, k_out), -1, dtype=np.int64)

@@ -49,7 +49,7 @@ class VxPages(ctypes.Structure):
 class VxGeom(ctypes.Structure):
     _fields_ = [("num_q_heads", c_int32), ("num_kv_heads", c_int32), ("head_dim_k", c_int32),
                 ("head_dim_v", c_int32), ("mla", c_int32), ("q_dtype", c_int32),
-                ("kv_dtype", c_int32), ("score_dim", c_int32)]
+                ("kv_dtype", c_int32), ("score_dim", c_int32), ("score_bf16", c_int32)]
 
 
 class VxPlan(ctypes.Structure):
@@ -162,11 +162,11 @@ def make_pages(batch, page_size, num_pool_pages, total_pages, max_pages, indptr,
 
 
 def make_geom(num_q_heads, num_kv_heads, head_dim_k, head_dim_v, mla, q_dtype, kv_dtype,
-              score_dim: int = 0) -> VxGeom:
+              score_dim: int = 0, score_bf16: bool = False) -> VxGeom:
     q = q_dtype if isinstance(q_dtype, int) else dtype_code(q_dtype)
     kv = kv_dtype if isinstance(kv_dtype, int) else dtype_code(kv_dtype)
     return VxGeom(num_q_heads, num_kv_heads, head_dim_k, head_dim_v, int(mla), q, kv,
-                  int(score_dim))
+                  int(score_dim), int(score_bf16))
 
 
 def vx_centroid_update(pages: VxPages, geom: VxGeom, k_pool, v_pool, first_token, k_new, v_new,

@@ -9,7 +9,8 @@
 // can attend at once: the chosen ids and the physical page of every entry
 // are already in its LDS (no kernel boundary, no reload of the selection or
 // of the page table). BOUNDS: the Quest-style indexer (page key bounds) in
-// place of the centroids. bf16 keys with Dk = 128 attend on the matrix cores
+// place of the centroids; CB16: the centroids' bf16 copy scored in place of
+// the fp32 rows (index_seg.h). bf16 keys with Dk = 128 attend on the matrix cores
 // (mfma_attend); fp32 keys or Dk = 64 on the vector ALUs (vec_attend), the
 // bodies of the stand-alone attention kernels, so the bits are the same.
 #include "attn_mfma.h"
@@ -96,7 +97,7 @@ VX_DEV void write_selection(const SegArgs& a, int seg, const int32_t* sel_l, int
   if (threadIdx.x == 0) a.sel_count[seg] = count;
 }
 
-template <int G, int P, int NW, bool BOUNDS>
+template <int G, int P, int NW, bool BOUNDS, bool CB16>
 __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
                                                              const uint16_t* __restrict__ vp,
                                                              float qscale, float* __restrict__ out,
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   };
   // The selection goes to a.sel after the attention (write_selection), so
   // its stores are not waited for at the barriers in between.
-  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, idle,
-                                                        false);
+  index_segment<uint16_t, uint16_t, 128, G, NW, BOUNDS, CB16>(a, seg, dyn, pid_l, sel_l, &cnt_l,
+                                                              idle, false);
 
   const Meta& m = a.m;
   if (!q_loaded) mfma_load_q<G>((const uint16_t*)a.q, b, g, a.hkv, qa);
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(64 * NW) void decode_seg_kernel(SegArgs a,
   write_selection(a, seg, sel_l, count);
 }
 
-template <typename KV, int G, int DK, int P, bool BOUNDS>
+template <typename KV, int G, int DK, int P, bool BOUNDS, bool CB16>
 __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs a,
                                                                     const KV* __restrict__ vp,
                                                                     float qscale,
@@ -177,8 +178,8 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs 
 
   const int seg = block_segment(a, (int*)dyn, &row_l);
   int* pid_l = (int*)(dyn + a.cap_keys + kSelectExtraWords);
-  index_segment<KV, KV, DK, G, kVecWaves, BOUNDS>(a, seg, dyn, pid_l, sel_l, &cnt_l, NoIdle{},
-                                                  false);
+  index_segment<KV, KV, DK, G, kVecWaves, BOUNDS, CB16>(a, seg, dyn, pid_l, sel_l, &cnt_l,
+                                                        NoIdle{}, false);
 
   const Meta& m = a.m;
   const int b = seg / a.hkv, g = seg % a.hkv;
@@ -198,14 +199,14 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_seg_vec_kernel(SegArgs 
   write_selection(a, seg, sel_l, count);
 }
 
-template <typename KV, int DK, int P, bool BOUNDS>
+template <typename KV, int DK, int P, bool BOUNDS, bool CB16>
 hipError_t launch_vec(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
                       hipStream_t s) {
   dim3 grid(a.m.batch * a.hkv), block(64 * kVecWaves);
   const size_t lds = (size_t)(2 * a.cap_keys + kSelectExtraWords) * sizeof(uint32_t);
 #define VX_VEC(GG)                                                                              \
   case GG:                                                                                      \
-    hipLaunchKernelGGL((decode_seg_vec_kernel<KV, GG, DK, P, BOUNDS>), grid, block, lds, s, a, \
+    hipLaunchKernelGGL((decode_seg_vec_kernel<KV, GG, DK, P, BOUNDS, CB16>), grid, block, lds, s, a, \
                        (const KV*)v_pool, qscale, out, lse);                                    \
     break;
   switch (a.hq / a.hkv) {
@@ -223,39 +224,43 @@ hipError_t launch_vec(const SegArgs& a, const void* v_pool, float qscale, float*
 template <int P>
 hipError_t launch_vec_p(const SegArgs& a, const vx_geom& g, bool bounds, const void* v_pool,
                         float qscale, float* out, float* lse, hipStream_t s) {
-  if (g.kv_dtype == VX_F32) {  // the bounds indexer is bf16 only (see decode_step_fusable)
-    if (g.head_dim_k == 128) return launch_vec<float, 128, P, false>(a, v_pool, qscale, out, lse, s);
-    return launch_vec<float, 64, P, false>(a, v_pool, qscale, out, lse, s);
+  // the bounds indexer and the bf16 centroid copy are bf16 only (host checks)
+  if (g.kv_dtype == VX_F32) {
+    if (g.head_dim_k == 128)
+      return launch_vec<float, 128, P, false, false>(a, v_pool, qscale, out, lse, s);
+    return launch_vec<float, 64, P, false, false>(a, v_pool, qscale, out, lse, s);
   }
-  if (bounds) return launch_vec<uint16_t, 64, P, true>(a, v_pool, qscale, out, lse, s);
-  return launch_vec<uint16_t, 64, P, false>(a, v_pool, qscale, out, lse, s);
+  if (bounds) return launch_vec<uint16_t, 64, P, true, false>(a, v_pool, qscale, out, lse, s);
+  if (g.score_bf16)
+    return launch_vec<uint16_t, 64, P, false, true>(a, v_pool, qscale, out, lse, s);
+  return launch_vec<uint16_t, 64, P, false, false>(a, v_pool, qscale, out, lse, s);
 }
 
-template <int G, int P, bool BOUNDS>
+template <int G, int P, bool BOUNDS, bool CB16>
 hipError_t launch_g(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
                     int max_pages, hipStream_t s) {
   dim3 grid(a.m.batch * a.hkv);
   const size_t lds = (size_t)(2 * a.cap_keys + kSelectExtraWords) * sizeof(uint32_t);
   if constexpr (G <= 4) {
     if (gqa_attn_waves(G, max_pages) == 16) {
-      hipLaunchKernelGGL((decode_seg_kernel<G, P, 16, BOUNDS>), grid, dim3(1024), lds, s, a,
+      hipLaunchKernelGGL((decode_seg_kernel<G, P, 16, BOUNDS, CB16>), grid, dim3(1024), lds, s, a,
                          (const uint16_t*)v_pool, qscale, out, lse);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_seg_kernel<G, P, 8, BOUNDS>), grid, dim3(512), lds, s, a,
+  hipLaunchKernelGGL((decode_seg_kernel<G, P, 8, BOUNDS, CB16>), grid, dim3(512), lds, s, a,
                      (const uint16_t*)v_pool, qscale, out, lse);
   return hipGetLastError();
 }
 
-template <int P, bool BOUNDS>
+template <int P, bool BOUNDS, bool CB16>
 hipError_t launch_p(const SegArgs& a, const void* v_pool, float qscale, float* out, float* lse,
                     int max_pages, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_g<1, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
-    case 2: return launch_g<2, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
-    case 4: return launch_g<4, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
-    case 8: return launch_g<8, P, BOUNDS>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 1: return launch_g<1, P, BOUNDS, CB16>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 2: return launch_g<2, P, BOUNDS, CB16>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 4: return launch_g<4, P, BOUNDS, CB16>(a, v_pool, qscale, out, lse, max_pages, s);
+    case 8: return launch_g<8, P, BOUNDS, CB16>(a, v_pool, qscale, out, lse, max_pages, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -321,11 +326,18 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
     return launch_vec_p<64>(a, g, bounds != nullptr, v_pool, qscale, out, lse, s);
   }
   if (bounds) {
-    if (m.page_size == 16) return launch_p<16, true>(a, v_pool, qscale, out, lse, max_pages, s);
-    return launch_p<64, true>(a, v_pool, qscale, out, lse, max_pages, s);
+    if (m.page_size == 16)
+      return launch_p<16, true, false>(a, v_pool, qscale, out, lse, max_pages, s);
+    return launch_p<64, true, false>(a, v_pool, qscale, out, lse, max_pages, s);
   }
-  if (m.page_size == 16) return launch_p<16, false>(a, v_pool, qscale, out, lse, max_pages, s);
-  return launch_p<64, false>(a, v_pool, qscale, out, lse, max_pages, s);
+  if (g.score_bf16) {
+    if (m.page_size == 16)
+      return launch_p<16, false, true>(a, v_pool, qscale, out, lse, max_pages, s);
+    return launch_p<64, false, true>(a, v_pool, qscale, out, lse, max_pages, s);
+  }
+  if (m.page_size == 16)
+    return launch_p<16, false, false>(a, v_pool, qscale, out, lse, max_pages, s);
+  return launch_p<64, false, false>(a, v_pool, qscale, out, lse, max_pages, s);
 }
 
 }  // namespace vx

@@ -20,12 +20,18 @@
 //     from its keys (fp32, token order, one IEEE divide: the cache stage's
 //     arithmetic) with up to 32 tokens in flight per lane, writes it back and
 //     scores it.
+//   - CB16: the rows are read from the bf16 copy of the centroids, 8 bytes
+//     per lane for the same 4 dims and the same arithmetic on the bf16
+//     values (half the bytes); the refresh scores its page from the bf16
+//     rounding of the fresh centroid, the value the copy then holds.
 //   - BOUNDS: the Quest-style indexer instead (bounds.h): a head's slice of a
 //     page's key bounds is as many bytes as its fp32 centroid slice (bf16
 //     minima and maxima, 16 bytes per lane), scored with the stand-alone
 //     bound scorer's arithmetic; the refresh recomputes the newest page's
 //     bounds.
 #pragma once
+
+#include <type_traits>
 
 #include "bounds.h"
 #include "topk_wave.h"
@@ -80,7 +86,7 @@ struct NoIdle {
 // not called. sel_global == false leaves a.sel / a.sel_count unwritten (the
 // caller writes them later from sel_lds / count_lds).
 template <typename QT, typename KV, int DK, int GG, int NW, bool BOUNDS = false,
-          typename Idle = NoIdle>
+          bool CB16 = false, typename Idle = NoIdle>
 VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_lds,
                           int32_t* sel_lds, int32_t* count_lds, Idle idle = Idle{},
                           bool sel_global = true) {
@@ -90,6 +96,7 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   static_assert(kChunk <= 64, "one page id per lane");
   static_assert(NW <= 16, "block select reduction words");
   static_assert(!BOUNDS || sizeof(KV) == 2, "bounds slices are 16 bytes per lane for bf16 keys");
+  static_assert(!(BOUNDS && CB16), "one page statistic per indexer");
 
   const Meta& m = a.m;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -129,11 +136,17 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
   float* scores = a.scores + (size_t)g * m.nnz + row0;
 
   // this lane's share of a page's score, from its 16 bytes of the row slice
-  auto lane_part = [&](const u32x4& raw) {
+  auto lane_part = [&](const auto& raw) {
     if constexpr (BOUNDS) {
       float lo[4], hi[4];
       Unit<uint16_t>::widen(raw, lo, hi);
       return unit_bound(qs, lo, hi);
+    } else if constexpr (CB16) {
+      float sc = qs.x * bf16_lo(raw.x);
+      sc = fmaf(qs.y, bf16_hi(raw.x), sc);
+      sc = fmaf(qs.z, bf16_lo(raw.y), sc);
+      sc = fmaf(qs.w, bf16_hi(raw.y), sc);
+      return sc;
     } else {
       float sc = qs.x * __uint_as_float(raw.x);
       sc = fmaf(qs.y, __uint_as_float(raw.y), sc);
@@ -156,17 +169,19 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
       const bool mine = cb + lane < pw1 && lane < kChunk;
       const int my_pid = mine ? phys_page(m, row0 + cb + lane) : 0;
       if (pid_lds && mine) pid_lds[cb + lane] = my_pid;
-      u32x4 r[kSegChunk];
+      using Slice = std::conditional_t<CB16, u32x2, u32x4>;  // this lane's part of a row
+      Slice r[kSegChunk];
 #pragma unroll
       for (int t = 0; t < kSegChunk; ++t) {
         const int p = cb + t * PPI + sub;
         const int pid = __shfl(my_pid, t * PPI + sub);
         // rows are streamed once per step: non-temporal loads
-        const u32x4* src =
-            BOUNDS ? (const u32x4*)((const uint16_t*)a.bounds +
-                                    (((size_t)pid * a.hkv + g) * W + dl) * 8)
-                   : (const u32x4*)(a.cent + ((size_t)pid * a.hkv + g) * DK + 4 * dl);
-        r[t] = p < pw1 ? __builtin_nontemporal_load(src) : u32x4{0u, 0u, 0u, 0u};
+        const size_t row = (size_t)pid * a.hkv + g;
+        const Slice* src =
+            BOUNDS ? (const Slice*)((const uint16_t*)a.bounds + (row * W + dl) * 8)
+                   : CB16 ? (const Slice*)(a.cent_bf16 + row * DK + 4 * dl)
+                          : (const Slice*)(a.cent + row * DK + 4 * dl);
+        r[t] = p < pw1 ? __builtin_nontemporal_load(src) : Slice{};
       }
 #pragma unroll
       for (int t = 0; t < kSegChunk; ++t) {
@@ -241,10 +256,15 @@ VX_DEV void index_segment(const SegArgs& a, int seg, uint32_t* keys, int* pid_ld
           *(uint2*)(a.cent_bf16 + o) = make_uint2(lo, hi);
         }
       }
-      float part = qs.x * c4.x;
-      part = fmaf(qs.y, c4.y, part);
-      part = fmaf(qs.z, c4.z, part);
-      part = fmaf(qs.w, c4.w, part);
+      // CB16: the page is scored from the copy's value, the bf16 rounding
+      const float4 cs =
+          CB16 ? make_float4(bf16_to_f32(f32_to_bf16(c4.x)), bf16_to_f32(f32_to_bf16(c4.y)),
+                             bf16_to_f32(f32_to_bf16(c4.z)), bf16_to_f32(f32_to_bf16(c4.w)))
+               : c4;
+      float part = qs.x * cs.x;
+      part = fmaf(qs.y, cs.y, part);
+      part = fmaf(qs.z, cs.z, part);
+      part = fmaf(qs.w, cs.w, part);
       emit(p, part, own);
     }
   }

@@ -23,7 +23,9 @@
 // over a window of indptr, loading all its centroid rows before using any. A
 // row [Hkv][Dk] fp32 is read as 16-byte chunks, chunk c = i*64 + lane, so
 // every load instruction covers 1 KB contiguous; chunk c belongs to head
-// c / (Dk/4), whose Dk/4 lanes reduce with DPP row ops.
+// c / (Dk/4), whose Dk/4 lanes reduce with DPP row ops. CB16: the rows are
+// the centroids' bf16 copy, chunk c being its 8 bytes of the same 4 dims,
+// scored with the same arithmetic on the bf16 values.
 #include "vx_internal.h"
 
 namespace vx {
@@ -98,7 +100,7 @@ __device__ __forceinline__ void score_chunk(float4 qs, float4 r, bool ok, int c,
 // (wave w % R takes chunk group w % R, so a row's chunks load in parallel
 // and every lane has up to 32 tokens in flight) and scored from the fresh
 // values with the same arithmetic as (b).
-template <typename QT, typename KV, int DK, int R, int GG, bool FULL>
+template <typename QT, typename KV, int DK, int R, int GG, bool FULL, bool CB16>
 __global__ __launch_bounds__(64 * kWaves) void index_gqa_kernel(IndexArgs a) {
   constexpr int W = DK / 4;
   __shared__ float4 qsum[R * 64];  // the block's first sequence's scaled query sum
@@ -126,15 +128,22 @@ __global__ __launch_bounds__(64 * kWaves) void index_gqa_kernel(IndexArgs a) {
   if (active) {
 #pragma unroll
     for (int u = 0; u < kPPW; ++u) {
-      const float4* r = (const float4*)(a.cent + (size_t)__builtin_amdgcn_readlane(my_pid, u) * a.hkv * DK);
+      const size_t row = (size_t)__builtin_amdgcn_readlane(my_pid, u) * a.hkv * DK;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int ch = i * 64 + lane;
+        const bool in = FULL || ch < nchunk;
         // centroid rows are streamed once per step: non-temporal loads
-        const u32x4 raw = (FULL || ch < nchunk) ? __builtin_nontemporal_load((const u32x4*)(r + ch))
-                                                : u32x4{0u, 0u, 0u, 0u};
-        rows[u][i] = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y),
-                                 __uint_as_float(raw.z), __uint_as_float(raw.w));
+        if constexpr (CB16) {
+          const u32x2 raw = in ? __builtin_nontemporal_load((const u32x2*)(a.cent_bf16 + row) + ch)
+                               : u32x2{0u, 0u};
+          rows[u][i] = make_float4(bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y));
+        } else {
+          const u32x4 raw = in ? __builtin_nontemporal_load((const u32x4*)(a.cent + row) + ch)
+                               : u32x4{0u, 0u, 0u, 0u};
+          rows[u][i] = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y),
+                                   __uint_as_float(raw.z), __uint_as_float(raw.w));
+        }
       }
     }
   }
@@ -254,15 +263,21 @@ __global__ __launch_bounds__(64 * kWaves) void index_gqa_kernel(IndexArgs a) {
     float4 qs;
     if (b == b_blk) qs = qsum[c];
     else qs = own ? group_query<QT, DK, GG>(q, a.hq, G, b, c, a.scale) : make_float4(0.f, 0.f, 0.f, 0.f);
-    score_chunk<W>(qs, c4, own, c, m.nnz, j, a.scores);
+    // CB16: the page is scored from the copy's value, the bf16 rounding
+    const float4 cs =
+        CB16 ? make_float4(bf16_to_f32(f32_to_bf16(c4.x)), bf16_to_f32(f32_to_bf16(c4.y)),
+                           bf16_to_f32(f32_to_bf16(c4.z)), bf16_to_f32(f32_to_bf16(c4.w)))
+             : c4;
+    score_chunk<W>(qs, cs, own, c, m.nnz, j, a.scores);
   }
 }
 
-template <typename QT, typename KV, int DK, int R, bool FULL>
+template <typename QT, typename KV, int DK, int R, bool FULL, bool CB16>
 hipError_t launch_r(const IndexArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   dim3 grid((a.m.nnz + kSpan - 1) / kSpan), block(64 * kWaves);
-#define VX_IX(GG) hipLaunchKernelGGL((index_gqa_kernel<QT, KV, DK, R, GG, FULL>), grid, block, 0, s, a)
+#define VX_IX(GG) \
+  hipLaunchKernelGGL((index_gqa_kernel<QT, KV, DK, R, GG, FULL, CB16>), grid, block, 0, s, a)
   switch (G) {
     case 1: VX_IX(1); break;
     case 2: VX_IX(2); break;
@@ -274,16 +289,20 @@ hipError_t launch_r(const IndexArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename QT, typename KV, int DK>
+template <typename QT, typename KV, int DK, bool CB16 = false>
 hipError_t launch_dk(const IndexArgs& a, hipStream_t s) {
   const int nchunk = a.hkv * DK / 4;
   if (nchunk <= 64)
-    return nchunk == 64 ? launch_r<QT, KV, DK, 1, true>(a, s) : launch_r<QT, KV, DK, 1, false>(a, s);
+    return nchunk == 64 ? launch_r<QT, KV, DK, 1, true, CB16>(a, s)
+                        : launch_r<QT, KV, DK, 1, false, CB16>(a, s);
   if (nchunk <= 128)
-    return nchunk == 128 ? launch_r<QT, KV, DK, 2, true>(a, s) : launch_r<QT, KV, DK, 2, false>(a, s);
+    return nchunk == 128 ? launch_r<QT, KV, DK, 2, true, CB16>(a, s)
+                         : launch_r<QT, KV, DK, 2, false, CB16>(a, s);
   if (nchunk <= 256)
-    return nchunk == 256 ? launch_r<QT, KV, DK, 4, true>(a, s) : launch_r<QT, KV, DK, 4, false>(a, s);
-  return nchunk == 512 ? launch_r<QT, KV, DK, 8, true>(a, s) : launch_r<QT, KV, DK, 8, false>(a, s);
+    return nchunk == 256 ? launch_r<QT, KV, DK, 4, true, CB16>(a, s)
+                         : launch_r<QT, KV, DK, 4, false, CB16>(a, s);
+  return nchunk == 512 ? launch_r<QT, KV, DK, 8, true, CB16>(a, s)
+                       : launch_r<QT, KV, DK, 8, false, CB16>(a, s);
 }
 
 }  // namespace
@@ -303,10 +322,14 @@ hipError_t launch_scores_gqa(const Meta& m, const vx_geom& g, const void* q, con
   a.refresh = refresh;
   a.scale = scale;
   a.scores = scores;
-  const bool f32 = g.kv_dtype == VX_F32;
+  const bool f32 = g.kv_dtype == VX_F32;  // the bf16 copy is scored with bf16 keys only
   if (g.head_dim_k == 64)
-    return f32 ? launch_dk<float, float, 64>(a, s) : launch_dk<uint16_t, uint16_t, 64>(a, s);
-  return f32 ? launch_dk<float, float, 128>(a, s) : launch_dk<uint16_t, uint16_t, 128>(a, s);
+    return f32 ? launch_dk<float, float, 64>(a, s)
+               : g.score_bf16 ? launch_dk<uint16_t, uint16_t, 64, true>(a, s)
+                              : launch_dk<uint16_t, uint16_t, 64>(a, s);
+  return f32 ? launch_dk<float, float, 128>(a, s)
+             : g.score_bf16 ? launch_dk<uint16_t, uint16_t, 128, true>(a, s)
+                            : launch_dk<uint16_t, uint16_t, 128>(a, s);
 }
 
 }  // namespace vx

@@ -58,6 +58,8 @@ vx_status check_geom(const vx_geom* g) {
            "num_q_heads %d not a multiple of num_kv_heads %d", g->num_q_heads, g->num_kv_heads);
   VX_CHECK(g->q_dtype == VX_F32 || g->q_dtype == VX_BF16, VX_ERR_INVALID_ARG, "q_dtype");
   VX_CHECK(g->kv_dtype == VX_F32 || g->kv_dtype == VX_BF16, VX_ERR_INVALID_ARG, "kv_dtype");
+  VX_CHECK(g->score_bf16 == 0 || g->score_bf16 == 1, VX_ERR_INVALID_ARG,
+           "score_bf16 %d (0 or 1)", g->score_bf16);
   if (g->mla) {
     VX_CHECK(g->num_kv_heads == 1, VX_ERR_INVALID_ARG, "MLA has one latent stream (num_kv_heads 1)");
     VX_CHECK(g->num_q_heads == 16 || g->num_q_heads == 32, VX_ERR_UNSUPPORTED,
@@ -78,6 +80,8 @@ vx_status check_geom(const vx_geom* g) {
              "num_kv_heads * head_dim > 2048");
     VX_CHECK(g->score_dim == 0 || g->score_dim == g->head_dim_k, VX_ERR_UNSUPPORTED,
              "GQA scores every column (score_dim 0 or head_dim_k)");
+    VX_CHECK(!g->score_bf16 || g->kv_dtype == VX_BF16, VX_ERR_UNSUPPORTED,
+             "score_bf16 needs bf16 KV");
   }
   return VX_OK;
 }
@@ -123,8 +127,9 @@ vx_status check_index_args(const vx_pages* pages, const vx_geom* geom, const voi
   VX_CHECK(pages->batch == 0 || q, VX_ERR_INVALID_ARG, "q is NULL");
   VX_CHECK(pages->total_pages == 0 || scores, VX_ERR_INVALID_ARG, "scores is NULL");
   VX_CHECK(pages->total_pages == 0 || centroids, VX_ERR_INVALID_ARG, "centroids is NULL");
-  VX_CHECK(!geom->mla || pages->total_pages == 0 || cent_bf16, VX_ERR_INVALID_ARG,
-           "MLA scores the bf16 centroids: cent_bf16 is NULL");
+  VX_CHECK(!(geom->mla || geom->score_bf16) || pages->total_pages == 0 || cent_bf16,
+           VX_ERR_INVALID_ARG, "%s scores the bf16 centroids: cent_bf16 is NULL",
+           geom->mla ? "MLA" : "score_bf16");
   VX_CHECK(!refresh_newest || pages->total_pages == 0 || k_pool, VX_ERR_INVALID_ARG,
            "refresh_newest needs k_pool");
   return VX_OK;
@@ -313,7 +318,7 @@ vx_status static_scratch(void** out) {
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 6; }
+int32_t vx_abi_version(void) { return 7; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {
@@ -352,6 +357,8 @@ vx_status vx_centroid_update(const vx_pages* pages, const vx_geom* geom, void* k
   VX_CHECK(!v_new || (first_token && v_pool && !geom->mla), VX_ERR_INVALID_ARG,
            "v_new needs first_token and v_pool (and no MLA)");
   VX_CHECK(!(geom->mla && v_pool), VX_ERR_INVALID_ARG, "MLA has no separate v_pool");
+  VX_CHECK(geom->mla || !geom->score_bf16 || pages->total_pages == 0 || cent_bf16,
+           VX_ERR_INVALID_ARG, "score_bf16 scores the bf16 copy: cent_bf16 is NULL");
   if (pages->batch == 0) return VX_OK;
   const vx::Meta m = meta_of(pages);
   hipError_t e;
@@ -380,6 +387,10 @@ vx_status vx_page_scores(const vx_pages* pages, const vx_geom* geom, const void*
     e = vx::launch_scores_mla_sized(m, *geom, q, nullptr, nullptr,
                                     const_cast<uint16_t*>((const uint16_t*)centroids), 0,
                                     score_scale, scores, pages->max_pages, stream);
+  else if (geom->score_bf16)  // centroids is the bf16 copy
+    e = vx::launch_scores_gqa(m, *geom, q, nullptr, nullptr,
+                              const_cast<uint16_t*>((const uint16_t*)centroids), 0, score_scale,
+                              scores, stream);
   else
     e = vx::launch_scores_gqa(m, *geom, q, nullptr, const_cast<float*>((const float*)centroids),
                               nullptr, 0, score_scale, scores, stream);

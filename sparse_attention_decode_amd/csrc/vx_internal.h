@@ -195,6 +195,7 @@ VX_DEV void merge_row(int S, int dv, const float* __restrict__ po, const float* 
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Four consecutive elements: raw load, then widening to fp32 (kept apart so
 // that many loads can be in flight in raw form).

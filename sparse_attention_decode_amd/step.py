@@ -7,7 +7,8 @@ attention. Python only marshals arguments; every stage is a gfx950 kernel.
 
 indexer="bounds" swaps the centroid cache stage and scorer for the
 Quest-style page bounds (vx_bounds_update / vx_bound_scores, GQA only);
-selection and attention are unchanged.
+selection and attention are unchanged. score_bf16=True (GQA, bf16 KV)
+scores the pages on the centroids' bf16 copy (MLA always does).
 """
 
 from __future__ import annotations
@@ -26,7 +27,7 @@ class DecodeStep:
     def __init__(self, w: Workload, mode: int = V.VX_TOPK_EXACT, num_splits: int = 0,
                  k: Optional[int] = None, n_sink: Optional[int] = None,
                  n_local: Optional[int] = None, with_lse: bool = True, fused: bool = True,
-                 score_dim: int = 0, indexer: str = "centroid"):
+                 score_dim: int = 0, indexer: str = "centroid", score_bf16: bool = False):
         if indexer not in ("centroid", "bounds"):
             raise ValueError(f"indexer {indexer!r}")
         s = w.spec
@@ -44,13 +45,14 @@ class DecodeStep:
         self.pages = V.make_pages(s.batch, s.page_size, w.pool_pages, w.nnz, w.max_pages,
                                   w.d_indptr, w.d_page_ids, w.d_seq_lens)
         self.score_dim = score_dim
+        self.score_bf16 = bool(score_bf16) and not s.mla
         self.geom = V.make_geom(s.num_q_heads, s.num_kv_heads, s.head_dim_k, s.head_dim_v,
-                                s.mla, w.q.dtype, w.k_pool.dtype, score_dim)
+                                s.mla, w.q.dtype, w.k_pool.dtype, score_dim, self.score_bf16)
         H = s.num_kv_heads
         self.centroids = torch.zeros((w.pool_pages, H, s.head_dim_k), dtype=torch.float32,
                                      device=dev)
         self.cent_bf16 = (torch.zeros((w.pool_pages, H, s.head_dim_k), dtype=torch.bfloat16,
-                                      device=dev) if s.mla else None)
+                                      device=dev) if s.mla or self.score_bf16 else None)
         # [pool][Hkv][Dk/4][2][4]: per 4 dims, their 4 key minima then 4 maxima
         self.bounds = (torch.zeros((w.pool_pages, H, s.head_dim_k // 4, 2, 4),
                                    dtype=w.k_pool.dtype, device=dev)
@@ -107,7 +109,7 @@ class DecodeStep:
             self.rebuild_centroids(stream)
 
     def score(self, stream=None) -> None:
-        cent = self.cent_bf16 if self.w.spec.mla else self.centroids
+        cent = self.cent_bf16 if self.w.spec.mla or self.score_bf16 else self.centroids
         V.vx_page_scores(self.pages, self.geom, self.w.q, cent, self.score_scale, self.scores,
                          stream)
 

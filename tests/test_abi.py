@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 6
+    assert lib.vx_abi_version() == 7
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -34,8 +34,9 @@ def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
     return V.make_pages(batch, page_size, pool, nnz, maxp, p, p, p)
 
 
-def geom(hq=16, hkv=8, dk=128, dv=128, mla=0, qd=V.VX_BF16, kvd=V.VX_BF16, score_dim=0):
-    return V.make_geom(hq, hkv, dk, dv, mla, qd, kvd, score_dim)
+def geom(hq=16, hkv=8, dk=128, dv=128, mla=0, qd=V.VX_BF16, kvd=V.VX_BF16, score_dim=0,
+         score_bf16=0):
+    return V.make_geom(hq, hkv, dk, dv, mla, qd, kvd, score_dim, score_bf16)
 
 
 def status_of(fn, *a, **kw):
@@ -75,6 +76,8 @@ def test_bad_pages_rejected(kw, status):
     (dict(hkv=32, hq=32, dk=128, dv=128), V.VX_ERR_UNSUPPORTED),  # 32*128 > 2048
     (dict(score_dim=64), V.VX_ERR_UNSUPPORTED),  # GQA scores every column
     (dict(hkv=1, mla=1, dk=576, dv=512, hq=32, score_dim=500), V.VX_ERR_UNSUPPORTED),
+    (dict(score_bf16=2), V.VX_ERR_INVALID_ARG),
+    (dict(score_bf16=1, qd=V.VX_F32, kvd=V.VX_F32), V.VX_ERR_UNSUPPORTED),  # bf16 KV only
 ])
 def test_bad_geometry_rejected(kw, status):
     assert status_of(V.vx_page_scores, pages(), geom(**kw), BAD, BAD, 1.0, BAD, stream=0) == status
@@ -109,6 +112,9 @@ def test_centroid_argument_checks():
                      stream=0) == V.VX_ERR_INVALID_ARG
     assert status_of(V.vx_centroid_update, p, g, BAD, None, None, None, None, None, None,
                      stream=0) == V.VX_ERR_INVALID_ARG
+    # score_bf16: the cache stage keeps the bf16 copy
+    assert status_of(V.vx_centroid_update, p, geom(score_bf16=1), BAD, None, None, None, None,
+                     BAD, None, stream=0) == V.VX_ERR_INVALID_ARG
 
 
 def test_decode_argument_checks():
@@ -226,6 +232,7 @@ def test_index_pages_argument_checks():
     mla = V.make_geom(32, 1, 576, 512, 1, V.VX_BF16, V.VX_BF16)
     mp = pages(page_size=64)
     assert call(geom=mla, pages=mp) == V.VX_ERR_INVALID_ARG  # MLA scores cent_bf16
+    assert call(geom=geom(score_bf16=1)) == V.VX_ERR_INVALID_ARG  # so does score_bf16
     assert call(geom=geom(dk=96, dv=96)) == V.VX_ERR_UNSUPPORTED
     assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
     big = V.make_pages(1, 16, 20000, 17000, 17000, BAD, BAD, BAD)
@@ -260,6 +267,7 @@ def test_decode_step_argument_checks():
     assert call(out=None) == V.VX_ERR_INVALID_ARG
     assert call(scores=None) == V.VX_ERR_INVALID_ARG
     assert call(centroids=None) == V.VX_ERR_INVALID_ARG
+    assert call(geom=geom(score_bf16=1)) == V.VX_ERR_INVALID_ARG  # scores need cent_bf16
     assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
     assert call(pages=pages(page_size=32)) == V.VX_ERR_UNSUPPORTED
 

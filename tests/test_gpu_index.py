@@ -188,6 +188,8 @@ def step_vs_calls(w, num_splits=0, mode=V.VX_TOPK_EXACT, appends=2, **kw):
         one.run()
         T.sync()
         assert torch.equal(sep.centroids[used], one.centroids[used])
+        if sep.cent_bf16 is not None:
+            assert torch.equal(sep.cent_bf16[used], one.cent_bf16[used])
         assert torch.equal(sep.scores[:, valid], one.scores[:, valid])
         assert torch.equal(sep.sel_count, one.sel_count)
         assert torch.equal(sep.sel, one.sel)
@@ -214,6 +216,32 @@ def test_full_size_decode_step_equals_calls(name, fused):
     w = W.make(sp, "cuda", seed=2)
     one = step_vs_calls(w)
     assert one.plan()["fused_step"] == fused
+    del w, one
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+@pytest.mark.parametrize("name", ["gqa_small", "large_small", "longgen_small"])
+def test_small_bf16_centroid_step_equals_calls(name, num_splits):
+    """Scores on the centroids' bf16 copy: the whole-step kernel (one
+    split), the fused indexer (three splits: vx_index_pages then the
+    attention) and the separate calls (vx_page_scores on the copy) give the
+    same bits, and match the oracle's bf16-centroid reading."""
+    w = on_gpu(W.make(SMALL[name].replace(headroom_tokens=40), "cpu", seed=25))
+    one = step_vs_calls(w, num_splits=num_splits, score_bf16=True)
+    assert one.plan()["fused_step"] == int(one.plan()["num_splits"] == 1)
+    assert check_step_against_oracle(w, one, range(w.batch)) <= max(1, w.batch * w.spec.num_kv_heads // 20)
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "largebatch_bf16", "longgen_bf16"])
+def test_full_size_bf16_centroid_step_equals_calls(name):
+    """The benchmarked shapes with bf16-copy scoring: whole step equals the
+    separate calls bit for bit; sampled sequences match the oracle."""
+    sp = W.spec(name, headroom_tokens=max(64, W.spec(name).headroom_tokens))
+    w = W.make(sp, "cuda", seed=2)
+    one = step_vs_calls(w, score_bf16=True)
+    assert one.plan()["fused_step"] == 1
+    assert check_step_against_oracle(w, one, [0, w.batch // 2, w.batch - 1]) <= 1
     del w, one
     torch.cuda.empty_cache()
 

@@ -120,3 +120,28 @@ def test_full_size_approximate_selection_on_gpu_scores():
             assert cnt[b, g] == int((want >= 0).sum())
     del w, step
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,sample", [("gqa_small", None), ("large_small", None),
+                                         ("gqa_bf16", [0, 9, 20, 31]),
+                                         ("longgen_bf16", [0, 40, 63])])
+def test_bf16_centroid_scoring(name, sample):
+    """GQA scores on the centroids' bf16 copy (vx_page_scores on the copy,
+    the separate calls): scores within the condition-aware bound of the
+    oracle's reading (bf16 rounding of the fp32 token-order centroid), the
+    selection, and the attention, as in the default pipeline."""
+    if sample is None:
+        w = W.make(SMALL[name], "cpu", seed=3)
+        w = W.Workload(spec=w.spec, device=torch.device("cuda"), seq_lens=w.seq_lens,
+                       indptr=w.indptr, page_ids=w.page_ids, pool_pages=w.pool_pages,
+                       q=w.q.cuda(), k_pool=w.k_pool.cuda(), v_pool=w.v_pool.cuda(),
+                       rand_u32=w.rand_u32)
+        sample = range(w.batch)
+    else:
+        w = W.make(W.spec(name), "cuda", seed=3)
+    step = DecodeStep(w, score_bf16=True)
+    assert step.cent_bf16 is not None
+    _, _, differing = pipeline_check(w, sample, step=step)
+    assert differing <= max(1, len(sample) * w.spec.num_kv_heads // 20)
+    del w, step
+    torch.cuda.empty_cache()

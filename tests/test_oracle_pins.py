@@ -464,3 +464,32 @@ def test_centroids_fp32_matches_fp64_when_exact():
     c64 = O.centroids(k, L, P)
     np.testing.assert_array_equal(c32, c64.astype(np.float32))
     assert c32.shape == (3, 2, 8)
+
+
+def test_decode_sequence_bf16_centroid_scores():
+    """score_bf16: each score is the fp32-summed query (not rounded) times
+    the bf16 rounding of the fp32 token-order centroid. P=3, L=6, two query
+    heads of 1 + 2**-12 on dim 0 (sum 2 + 2**-11). Page 0's keys
+    1 + 2**-8 (twice) and 1 + 2**-8 + 2**-23 sum in fp32 to 3 + 3 * 2**-8
+    (the last addition ties and rounds to even), so the fp32 centroid is
+    1 + 2**-8, halfway between the bf16 values 1 and 1 + 2**-7, and rounds
+    to even: 1.0; the exact mean lies above that midpoint and would round up.
+    Page 1's mean 1 + 3 * 2**-9 is exact and rounds to the nearest bf16,
+    1 + 2**-7."""
+    k = np.zeros((2, 1, 3, 2))
+    k[0, 0, :, 0] = [1 + 2.0 ** -8, 1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -23]
+    k[1, 0, :, 0] = [1.0, 1.0, 1 + 9 * 2.0 ** -9]
+    q = np.zeros((2, 2))
+    q[:, 0] = 1 + 2.0 ** -12
+    seq = {"q": q, "k": k, "v": np.ones((2, 1, 3, 2)), "seq_len": 6,
+           "rand_u32": np.zeros(1, np.uint32)}
+    kw = dict(page_size=3, num_kv_heads=1, k=1, n_sink=0, n_local=0, score_scale=1.0,
+              sm_scale=1.0)
+    r = O.decode_sequence(seq, score_bf16=True, **kw)
+    qs = 2 + 2.0 ** -11
+    assert r["scores"][0, 0] == qs * 1.0
+    assert r["scores"][0, 1] == qs * (1 + 2.0 ** -7)
+    assert list(r["sel"][0]) == [1]
+    mean64 = O.centroids(k, 6, 3)[0, 0, 0]
+    assert mean64 > 1 + 2.0 ** -8 and O.round_to_bf16(np.array([mean64]))[0] == 1 + 2.0 ** -7
+    assert O.centroids_fp32(k, 6, 3)[0, 0, 0] == np.float32(1 + 2.0 ** -8)

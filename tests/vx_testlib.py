@@ -35,7 +35,8 @@ def oracle_seq(w: W.Workload, step: DecodeStep, b: int, approx: bool = False) ->
                           score_scale=step.score_scale, sm_scale=step.sm_scale, mla=s.mla,
                           head_dim_v=s.head_dim_v, approx=approx,
                           score_dim=step.score_dim or None,
-                          indexer=getattr(step, "indexer", "centroid"))
+                          indexer=getattr(step, "indexer", "centroid"),
+                          score_bf16=getattr(step, "score_bf16", False))
     r["seq"] = seq
     return r
 
@@ -99,7 +100,8 @@ def check_scores(w, step, b, ref):
     got = step.scores[:, lo:lo + n].double().cpu().numpy()
     d = step.score_dim or s.head_dim_k  # columns scored
     q = ref["seq"]["q"][:, :d]
-    cent = (O.round_to_bf16(ref["centroids"]) if s.mla else ref["centroids"])[..., :d]
+    bf16 = s.mla or getattr(step, "score_bf16", False)
+    cent = (O.round_to_bf16(ref["centroids"]) if bf16 else ref["centroids"])[..., :d]
     G = s.num_q_heads // s.num_kv_heads
     bound = np.zeros((s.num_kv_heads, n))
     for g in range(s.num_kv_heads):
