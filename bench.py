@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--mode", default="exact", choices=["exact", "approx"])
     ap.add_argument("--indexer", default="centroid", choices=["centroid", "bounds"],
                     help="bounds: the Quest-style page-bounds indexer (GQA workloads)")
+    ap.add_argument("--score-bf16", action="store_true",
+                    help="GQA: score the pages on the centroids' bf16 copy (vx_geom.score_bf16)")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 1 GB touched")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
@@ -82,7 +84,10 @@ def step_bytes(w, step):
     cnt = step.sel_count.cpu().numpy()
     P = s.page_size
     kv_elt = 4 if s.kv_dtype == "f32" else 2
-    cent_elt = 2 * kv_elt if step.indexer == "bounds" else (2 if s.mla else 4)
+    if step.indexer == "bounds":
+        cent_elt = 2 * kv_elt
+    else:  # MLA, and GQA with score_bf16, score the centroids' bf16 copy
+        cent_elt = 2 if s.mla or getattr(step, "score_bf16", False) else 4
     n_pages = np.array([w.n_pages(b) for b in range(s.batch)])
     cent_bytes = int(n_pages.sum()) * s.num_kv_heads * s.head_dim_k * cent_elt
     row = (s.head_dim_k if s.mla else s.head_dim_k + s.head_dim_v) * kv_elt
@@ -174,7 +179,8 @@ def cpu_baseline(w, step, seconds):
         kw = dict(page_size=s.page_size, num_kv_heads=s.num_kv_heads, k=step.k,
                   n_sink=step.n_sink, n_local=step.n_local, score_scale=step.score_scale,
                   sm_scale=step.sm_scale, mla=s.mla, head_dim_v=s.head_dim_v,
-                  approx=step.mode == 1, indexer=step.indexer)
+                  approx=step.mode == 1, indexer=step.indexer,
+                  score_bf16=getattr(step, "score_bf16", False))
         cores = max(1, min(len(os.sched_getaffinity(0)), 16))
         ctx = mp.get_context("spawn")  # no fork of a process that holds the GPU
         res = {}
@@ -238,7 +244,7 @@ def measured_traffic(workload, stage):
 
 
 # Kernels whose HBM bytes make up each stage bench.py can report as dominant,
-# per profiled run (workload, or workload + "_bounds" for --indexer bounds).
+# per profiled run (workload, or workload + a suffix of RUN_VARIANTS).
 PROFILE_STAGES = {
     "gqa_bf16": {"decode_step": ["decode_seg_kernel"], "indexer": ["index_seg_kernel"],
                  "attention_merge": ["attn_gqa_mfma_kernel"]},
@@ -253,16 +259,31 @@ PROFILE_STAGES = {
     "gqa_bf16_bounds": {"decode_step": ["decode_seg_kernel"]},
     "largebatch_bf16_bounds": {"decode_step": ["decode_seg_kernel"]},
     "longgen_bf16_bounds": {"decode_step": ["decode_seg_kernel"]},
+    "gqa_bf16_cb16": {"decode_step": ["decode_seg_kernel"]},
+    "largebatch_bf16_cb16": {"decode_step": ["decode_seg_kernel"]},
+    "longgen_bf16_cb16": {"decode_step": ["decode_seg_kernel"]},
 }
+# Run-name suffixes: the indexer variant and its bench.py flag.
+RUN_VARIANTS = {"_bounds": "--indexer bounds", "_cb16": "--score-bf16"}
+# The whole-step kernel's last two template arguments (bounds indexer, bf16
+# centroid copy) for each variant.
+STEP_KERNEL_TAIL = {"": "false, false>", "_bounds": "true, false>", "_cb16": "false, true>"}
+
+
+def run_parts(run):
+    """(workload, variant suffix, bench.py flags) of a profiled run name."""
+    for suf, flag in RUN_VARIANTS.items():
+        if run.endswith(suf):
+            wl = run[:-len(suf)]
+            return wl, suf, f"--workload {wl} {flag}"
+    return run, "", f"--workload {run}"
 
 
 def profile_commands(run):
     """The rocprofv3 runs a profiled run `run` (a PROFILE_STAGES key) needs,
     with their outputs under $OUT: a kernel trace, then one pass per HBM
     counter; the copy calibration passes run once for all."""
-    bounds = run.endswith("_bounds")
-    wl = run[:-len("_bounds")] if bounds else run
-    flags = f"--workload {wl}{' --indexer bounds' if bounds else ''}"
+    _, _, flags = run_parts(run)
     cmds = [f"rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{run}_trace -o run -- "
             f"python3 $R/bench.py {flags} --steps 50 --warmup 5 --stage-reps 5 --no-cpu-baseline --no-extras"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -314,8 +335,8 @@ def summarize_profiles(out, commit):
     for run, stages in PROFILE_STAGES.items():
         if not os.path.isdir(os.path.join(out, run + "_trace")):
             continue
-        bounds = run.endswith("_bounds")
-        wl = run[:-len("_bounds")] if bounds else run
+        wl, suf, _ = run_parts(run)
+        bounds = suf == "_bounds"
         dur = durations(os.path.join(out, run + "_trace"))
         fe, nf = counters(os.path.join(out, run + "_FETCH_SIZE"), "FETCH_SIZE")
         wr, _ = counters(os.path.join(out, run + "_WRITE_SIZE"), "WRITE_SIZE")
@@ -325,10 +346,12 @@ def summarize_profiles(out, commit):
             r"step touches ([\d.]+) MB \(centroids ([\d.]+), selected KV ([\d.]+)\)", text).groups())
         step_us = re.search(r"\d+ steps: ([\d.]+) us/step", text).group(1)
         stage_line = re.search(r"stage us: (.*)", text).group(1)
-        title = f"{wl} with the Quest-style bounds indexer" if bounds else wl
+        title = {"": wl, "_bounds": f"{wl} with the Quest-style bounds indexer",
+                 "_cb16": f"{wl} scoring the centroids' bf16 copy"}[suf]
         lines = [f"# {title}: one decode step, kernel durations and HBM traffic", "",
                  f"Profiled at commit `{commit}` on one MI355X. Algorithmic bytes per step: {tot:.1f} MB "
-                 f"({'page bounds' if bounds else 'centroids'} {cent:.1f} MB + selected valid KV "
+                 f"({'page bounds' if bounds else 'bf16 centroids' if suf else 'centroids'} "
+                 f"{cent:.1f} MB + selected valid KV "
                  f"{kv:.1f} MB).", "",
                  "Commands (`cd /tmp && export TMPDIR=/tmp` first; `$R` = the repository, `$OUT` = the "
                  "output directory), then `python3 $R/bench.py --summarize-profiles $OUT`:", "", "```",
@@ -351,7 +374,7 @@ def summarize_profiles(out, commit):
             parts, total = [], 0.0
             for pat in pats:
                 match = [k for k in fe if pat in k and (not pat.startswith("decode_seg")
-                                                        or k.endswith("true>") == bounds)]
+                                                        or k.endswith(STEP_KERNEL_TAIL[suf]))]
                 if not match:
                     raise SystemExit(f"{run}: no counters for {pat}")
                 k = max(match, key=lambda x: nf[x])  # the stage's instantiation: most dispatches
@@ -585,16 +608,17 @@ INDEX_MODE_WORKLOADS = ("longgen_bf16", "largebatch_bf16")
 class Bench:
     """The replicas of one workload, their step graphs and timings."""
 
-    def __init__(self, name, mode, indexer, replicas, append):
+    def __init__(self, name, mode, indexer, replicas, append, score_bf16=False):
         import torch
         from sparse_attention_decode_amd import workloads as W
         from sparse_attention_decode_amd.step import DecodeStep
         self.name, self.mode, self.indexer, self.append = name, mode, indexer, append
+        self.score_bf16 = score_bf16
         sp = W.spec(name)
         self.spec = sp
         log(f"workload {name}: generating on cuda:0")
         w0 = W.make(sp, "cuda", seed=0)
-        base = DecodeStep(w0, mode=mode, indexer=indexer)
+        base = DecodeStep(w0, mode=mode, indexer=indexer, score_bf16=score_bf16)
         base.rebuild()
         self.run_fn = (lambda st: st.run_append()) if append else (lambda st: st.run())
         self.run_fn(base)
@@ -609,7 +633,7 @@ class Bench:
         self.ws, self.steps = [w0], [base]
         for _ in range(self.R - 1):
             w = w0.replicate()
-            st = DecodeStep(w, mode=mode, indexer=indexer)
+            st = DecodeStep(w, mode=mode, indexer=indexer, score_bf16=score_bf16)
             st.rebuild()
             self.ws.append(w)
             self.steps.append(st)
@@ -726,7 +750,8 @@ class Bench:
         else:
             dom = max(("indexer", "attention_merge"), key=lambda k: stage_us[k])
         achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
-        run = self.name + ("_bounds" if self.indexer == "bounds" else "")
+        run = self.name + ("_bounds" if self.indexer == "bounds" else
+                           "_cb16" if self.score_bf16 else "")
         rec = {"workload": f"{self.name}: {DESCR[self.name]}",
                "ms_per_step": us / 1e3, "seqs_per_s": s.batch / t_step,
                "kv_tokens_per_s": self.tokens / s.num_kv_heads / t_step,
@@ -747,6 +772,45 @@ class Bench:
         del self.steps, self.ws, self.base, self.w0
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+
+
+def bf16_copy_scoring(b, a):
+    """The same workload and replicas with the pages scored on the
+    centroids' bf16 copy (GQA, vx_geom.score_bf16): the step's time, bytes
+    and rate, and the recall@k of its selection against the fp32-centroid
+    selection of the same step on the same inputs."""
+    import torch
+    from sparse_attention_decode_amd.step import DecodeStep
+    fp32, alt = b.steps, []
+    for w in b.ws:
+        st = DecodeStep(w, mode=b.mode, score_bf16=True)
+        st.rebuild()
+        alt.append(st)
+    b.steps = alt
+    try:
+        us = b.time_step(a.steps, a.warmup)
+        dec = b.time_stage(lambda x: x.step(refresh=not b.append), a.stage_reps)
+    finally:
+        b.steps = fp32
+    b.base.step(refresh=True)
+    alt[0].step(refresh=True)
+    torch.cuda.synchronize()
+    rec = overlap(b.w0, b.base, alt[0].sel, alt[0].sel_count, b.base.sel, b.base.sel_count)
+    cent_b, kv_b, _ = step_bytes(b.w0, alt[0])
+    del alt
+    torch.cuda.empty_cache()
+    s = b.spec
+    out = {"ms_per_step": us / 1e3, "seqs_per_s": s.batch / (us * 1e-6),
+           "step_bytes": cent_b + kv_b, "centroid_bytes": cent_b,
+           "step_hbm_GBps": (cent_b + kv_b) / (us * 1e-6) / 1e9,
+           "decode_step_us": dec, "recall_at_k_vs_fp32_centroids": rec}
+    log(f"{b.name} scoring the bf16 centroid copy: {us:.2f} us/step, decode_step {dec:.2f} us, "
+        f"recall@k vs fp32 centroids mean {rec['mean']:.4f} min {rec['min']:.4f}")
+    return out
+
+
+# GQA bf16 workloads that also report bf16-copy scoring in the default run.
+BF16_COPY_WORKLOADS = ("gqa_bf16", "longgen_bf16", "largebatch_bf16")
 
 
 def index_modes(name, a):
@@ -802,7 +866,11 @@ def main():
         print("the bounds indexer is implemented for GQA workloads only", file=sys.stderr)
         sys.exit(2)
     append = a.workload in APPEND_WORKLOADS and not bounds
-    main_b = Bench(a.workload, mode, a.indexer, a.replicas, append)
+    if a.score_bf16 and (sp.mla or bounds or sp.kv_dtype != "bf16"):
+        print("--score-bf16 applies to the centroid indexer of bf16 GQA workloads",
+              file=sys.stderr)
+        sys.exit(2)
+    main_b = Bench(a.workload, mode, a.indexer, a.replicas, append, a.score_bf16)
     w0, base = main_b.w0, main_b.base
     recall = approx_recall(w0, base) if mode == V.VX_TOPK_APPROX else None
     if recall:
@@ -846,7 +914,8 @@ def main():
         "dtype": "f32" if s.kv_dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": rec["workload"], "topk_mode": a.mode,
-                   "indexer": a.indexer, "replicas": rec["replicas"], "hip_graph": True,
+                   "indexer": a.indexer + (" (bf16 copy)" if a.score_bf16 else ""),
+                   "replicas": rec["replicas"], "hip_graph": True,
                    "num_splits": rec["num_splits"], "fused_step": rec["fused_step"],
                    "appends_token": rec["appends_token"]},
         "kv_tokens_per_s": rec["kv_tokens_per_s"],
@@ -865,6 +934,8 @@ def main():
     if quality:
         result["selection_quality"] = quality
     if not a.no_extras and not bounds and mode == V.VX_TOPK_EXACT:
+        if a.workload in BF16_COPY_WORKLOADS and not a.score_bf16:
+            result["bf16_centroid_scoring"] = bf16_copy_scoring(main_b, a)
         # The other workloads, each measured in this same run.
         main_b.free()
         result["workloads"] = {}
@@ -873,6 +944,8 @@ def main():
                 continue
             b = Bench(name, mode, "centroid", a.replicas, name in APPEND_WORKLOADS)
             r = b.record(a, full=False)
+            if name in BF16_COPY_WORKLOADS:
+                r["bf16_centroid_scoring"] = bf16_copy_scoring(b, a)
             b.free()
             if name in INDEX_MODE_WORKLOADS:
                 r["topk_modes"] = index_modes(name, a)
@@ -882,7 +955,7 @@ def main():
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         if main_b is None:
-            main_b = Bench(a.workload, mode, a.indexer, 1, append)
+            main_b = Bench(a.workload, mode, a.indexer, 1, append, a.score_bf16)
         result["cpu_baseline"] = cpu_baseline(main_b.w0, main_b.base, a.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -96,7 +96,7 @@ def test_summarize_profiles_calibrates_counters(tmp_path, monkeypatch):
     B = load_bench()
     out = tmp_path / "prof"
     copy = "void at::native::copy_kernel(float)"
-    kern = "void vx::(anonymous namespace)::decode_seg_kernel<2, 16, 16, false>(vx::SegArgs)"
+    kern = "void vx::(anonymous namespace)::decode_seg_kernel<2, 16, 16, false, false>(vx::SegArgs)"
     cc = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     _csv(str(out / "copy_FETCH_SIZE" / "run_counter_collection.csv"), cc,
          [[f'"{copy}"', "FETCH_SIZE", 524288.0]])
@@ -124,5 +124,16 @@ def test_summarize_profiles_calibrates_counters(tmp_path, monkeypatch):
     st = t["workloads"]["gqa_bf16"]["stages"]["decode_step"]
     assert st["hbm_bytes_per_launch"] == (1000.0 * 2 + 10.0) * 1024
     md = (tmp_path / "profiles" / "gqa_bf16_step.md").read_text()
-    assert "| `decode_seg_kernel<2, 16, 16, false>` | 2 | 18.00 |" in md
+    assert "| `decode_seg_kernel<2, 16, 16, false, false>` | 2 | 18.00 |" in md
     assert "abc1234" in md
+
+
+def test_run_names_map_to_bench_flags():
+    """A profiled run's name gives its workload, variant and bench.py flags."""
+    import bench as B
+    assert B.run_parts("gqa_bf16") == ("gqa_bf16", "", "--workload gqa_bf16")
+    assert B.run_parts("longgen_bf16_bounds") == ("longgen_bf16", "_bounds",
+                                                  "--workload longgen_bf16 --indexer bounds")
+    assert B.run_parts("largebatch_bf16_cb16") == ("largebatch_bf16", "_cb16",
+                                                   "--workload largebatch_bf16 --score-bf16")
+    assert set(B.STEP_KERNEL_TAIL) == {""} | set(B.RUN_VARIANTS)
