@@ -38,8 +38,10 @@
  *     an idle slot: no page scored, an empty selection, out = 0 and
  *     lse = -inf. Kernels clamp both so that no access leaves its buffer;
  *     results for a sequence that breaks them are unspecified.
- *   - Entry points are reentrant; the only library state is a per-device
- *     cache of the compute-unit count.
+ *   - Entry points are reentrant; the only library state is per device: a
+ *     cache of the compute-unit count, and the address of the scratch array
+ *     of vx_decode_step_static (a device array in the library's code object,
+ *     loaded with it; no entry point allocates).
  *
  * Memory layouts (row-major, innermost last)
  *   q          [B][Hq][Dk]                     q_dtype
