@@ -8,6 +8,7 @@
  *   indexer        query x centroid scores                    -> vx_page_scores
  *                  top-k pages per (sequence, KV head)        -> vx_topk_pages
  *                  both, fused with the newest-page refresh   -> vx_index_pages
+ *   page table     device-side check of its contract         -> vx_check_pages
  *   whole step     indexer + attention, fused where possible  -> vx_decode_step
  *                  the same, without a workspace argument     -> vx_decode_step_static
  *   attention      exact softmax over the selected pages      -> vx_sparse_decode
@@ -415,6 +416,24 @@ vx_status vx_bound_decode_step(const vx_pages* pages, const vx_geom* geom,
 vx_status vx_plan_decode(const vx_pages* pages, const vx_geom* geom,
                          int32_t sel_stride, int32_t num_splits,
                          int32_t num_cus, vx_plan* plan);
+
+/* Device-side check of the page table (Vortex paper note, "System design >
+ * 2. vTensor": the page-index structure) against the contract above, which
+ * the other entry points assume and do not check: one kernel writes to
+ * counts[0..3) (device int32, caller-owned) the number of violations of each
+ * rule, all zero for a well-formed table:
+ *   counts[0]  indptr out of order: indptr[0] != 0, indptr[b+1] < indptr[b],
+ *              or indptr[B] != total_pages
+ *   counts[1]  sequences with seq_lens[b] < 0, seq_lens[b] > capacity *
+ *              page_size, or a capacity above max_pages
+ *   counts[2]  page-table entries (in use or capacity) outside
+ *              [0, num_pool_pages)
+ * It reads indptr[0..B], seq_lens[0..B) and page_ids[0..total_pages) and
+ * nothing through their values, so a corrupted table cannot make it fault.
+ * Host checks as for every entry point; counts == NULL is
+ * VX_ERR_INVALID_ARG. Asynchronous like the rest: the counts are valid once
+ * the stream reaches them. */
+vx_status vx_check_pages(const vx_pages* pages, int32_t* counts, hipStream_t stream);
 
 const char* vx_status_string(vx_status status);
 const char* vx_last_error(void);

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "VxError", "VxPages", "VxGeom", "VxPlan", "load", "lib_path", "status_string",
     "vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
-    "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_bounds_update",
+    "vx_sparse_decode", "vx_decode_step", "vx_plan_decode", "vx_check_pages", "vx_bounds_update",
     "vx_bound_scores", "vx_bound_decode_step", "vx_decode_step_static", "vx_append_decode_step", "VX_F32", "VX_BF16", "VX_TOPK_EXACT", "VX_TOPK_APPROX",
     "ENTRY_POINTS",
 ]
@@ -28,8 +28,8 @@ VX_TOPK_EXACT, VX_TOPK_APPROX = 0, 1
 ENTRY_POINTS = ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
                 "vx_bounds_update", "vx_bound_scores", "vx_bound_decode_step",
                 "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static",
-                "vx_append_decode_step", "vx_plan_decode", "vx_status_string", "vx_last_error",
-                "vx_abi_version")
+                "vx_append_decode_step", "vx_plan_decode", "vx_check_pages", "vx_status_string",
+                "vx_last_error", "vx_abi_version")
 
 _DTYPES = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
 
@@ -104,6 +104,7 @@ def load() -> ctypes.CDLL:
                                           c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                           POINTER(c_size_t), c_void_p]
     lib.vx_plan_decode.argtypes = [P, G, c_int32, c_int32, c_int32, POINTER(VxPlan)]
+    lib.vx_check_pages.argtypes = [P, c_void_p, c_void_p]
     lib.vx_bounds_update.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.vx_bound_scores.argtypes = [P, G, c_void_p, c_void_p, c_void_p, c_int32, c_float,
                                     c_void_p, c_void_p]
@@ -115,7 +116,7 @@ def load() -> ctypes.CDLL:
     for name in ("vx_centroid_update", "vx_page_scores", "vx_topk_pages", "vx_index_pages",
                  "vx_sparse_decode", "vx_decode_step", "vx_decode_step_static",
                  "vx_append_decode_step", "vx_plan_decode", "vx_bounds_update", "vx_bound_scores",
-                 "vx_bound_decode_step"):
+                 "vx_bound_decode_step", "vx_check_pages"):
         getattr(lib, name).restype = c_int32
     lib.vx_status_string.argtypes = [c_int32]
     lib.vx_status_string.restype = c_char_p
@@ -300,6 +301,12 @@ def vx_bound_decode_step(pages: VxPages, geom: VxGeom, q, k_pool, v_pool, bounds
                                        _ptr(lse), num_splits, _ptr(workspace),
                                        ctypes.byref(nbytes), _stream(stream)))
     return nbytes.value
+
+
+def vx_check_pages(pages: VxPages, counts, stream=None) -> None:
+    """counts: device int32[3], written with the page table's contract
+    violations (indptr order, sequence lengths, page ids out of the pool)."""
+    _check(load().vx_check_pages(ctypes.byref(pages), _ptr(counts), _stream(stream)))
 
 
 def vx_plan_decode(pages: VxPages, geom: VxGeom, sel_stride: int, num_splits: int = 0,

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvx.so")
 SOURCES = ["vx_capi.hip", "centroid.hip", "scores.hip", "indexer.hip", "topk.hip", "attention.hip",
-           "mla.hip", "decode.hip", "bounds.hip"]
+           "mla.hip", "decode.hip", "bounds.hip", "pages.hip"]
 ARCH = "gfx950"
 # no packed fp32 instructions in generated code
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -318,7 +318,7 @@ vx_status static_scratch(void** out) {
 
 extern "C" {
 
-int32_t vx_abi_version(void) { return 7; }
+int32_t vx_abi_version(void) { return 8; }
 
 const char* vx_status_string(vx_status s) {
   switch (s) {
@@ -342,6 +342,14 @@ vx_status vx_plan_decode(const vx_pages* pages, const vx_geom* geom, int32_t sel
   VX_CHECK(sel_stride >= 1, VX_ERR_INVALID_ARG, "sel_stride < 1");
   if (num_cus <= 0 && (st = device_cus(&num_cus)) != VX_OK) return st;
   return make_plan(pages, geom, sel_stride, num_splits, num_cus, plan);
+}
+
+vx_status vx_check_pages(const vx_pages* pages, int32_t* counts, hipStream_t stream) {
+  vx_status st;
+  if ((st = check_pages(pages)) != VX_OK) return st;
+  VX_CHECK(counts, VX_ERR_INVALID_ARG, "counts is NULL");
+  return hip_status(vx::launch_check_pages(meta_of(pages), pages->max_pages, counts, stream),
+                    "page check kernel launch");
 }
 
 vx_status vx_centroid_update(const vx_pages* pages, const vx_geom* geom, void* k_pool,

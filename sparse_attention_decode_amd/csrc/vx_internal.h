@@ -252,6 +252,8 @@ hipError_t launch_decode_step_gqa(const Meta& m, const vx_geom& g, const void* q
 // order[r] = the sequence with the r-th most pages in use (ties: lower index
 // first), for the whole-step kernel's block order. batch <= kMaxOrderedBatch.
 hipError_t launch_rank_sequences(const Meta& m, int32_t* order, hipStream_t s);
+// counts[0..3) = violations of the page-table contract (vx_check_pages).
+hipError_t launch_check_pages(const Meta& m, int max_pages, int32_t* counts, hipStream_t s);
 // MLA scores on the bf16 centroids; refresh != 0 first recomputes each
 // sequence's newest page (fp32 centroid and its bf16 copy) from k_pool.
 hipError_t launch_scores_mla_sized(const Meta& m, const vx_geom& g, const void* q,

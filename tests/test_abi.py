@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(V.ENTRY_POINTS) <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vx_abi_version() == 7
+    assert lib.vx_abi_version() == 8
 
 
 def pages(batch=2, page_size=16, pool=10, nnz=8, maxp=4, ptrs=True):
@@ -405,3 +405,11 @@ def test_append_decode_step_argument_checks():
     assert call(stride=5) == V.VX_ERR_INVALID_ARG
     assert call(out=None) == V.VX_ERR_INVALID_ARG
     assert call(geom=geom(hq=24, hkv=8)) == V.VX_ERR_UNSUPPORTED
+
+
+def test_check_pages_argument_checks():
+    counts = BAD
+    assert status_of(V.vx_check_pages, pages(), None) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_check_pages, pages(page_size=32), counts) == V.VX_ERR_UNSUPPORTED
+    assert status_of(V.vx_check_pages, pages(ptrs=False), counts) == V.VX_ERR_INVALID_ARG
+    assert status_of(V.vx_check_pages, pages(maxp=9), counts) == V.VX_ERR_INVALID_ARG
