@@ -137,3 +137,15 @@ def test_run_names_map_to_bench_flags():
     assert B.run_parts("largebatch_bf16_cb16") == ("largebatch_bf16", "_cb16",
                                                    "--workload largebatch_bf16 --score-bf16")
     assert set(B.STEP_KERNEL_TAIL) == {""} | set(B.RUN_VARIANTS)
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so,
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
