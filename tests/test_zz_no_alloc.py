@@ -63,3 +63,41 @@ def test_static_scratch_limit():
                                 V.VX_TOPK_EXACT, None, bad, bad, 131, bad, bad, bad, 130)
     assert e.value.status == V.VX_ERR_WORKSPACE, e.value
     assert "static scratch" in str(e.value)
+
+
+def static_call(b, w, num_splits):
+    V.vx_decode_step_static(b.pages, b.geom, w.q, w.k_pool, w.v_pool, b.centroids, b.cent_bf16,
+                            True, b.score_scale, b.sm_scale, b.k, b.n_sink, b.n_local, b.mode,
+                            w.d_rand_u32, b.scores, b.sel, b.k_out, b.sel_count, b.out, b.lse,
+                            num_splits, torch.cuda.current_stream().cuda_stream)
+
+
+@pytest.mark.parametrize("name,kw,splits", [
+    ("mla_bf16", dict(batch=3, lengths=("list", (20000, 9000, 4100))), 0),
+    ("gqa_bf16", dict(batch=3, lengths=("list", (3000, 900, 2500))), 3),
+])
+def test_static_step_under_graph_capture(name, kw, splits):
+    """The call the entry point exists for: captured in a HIP graph (no
+    allocation inside the capture), replayed four times with eager work on
+    the same buffers between replays; every replay gives vx_decode_step's
+    bits."""
+    w = W.make(W.spec(name, **kw), "cuda", seed=11)
+    a, b = both(w, splits)  # eager: the address lookup happens here, outside the capture
+    assert_same(a, b, f"{name} eager")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream, capture_error_mode="thread_local"):
+        static_call(b, w, splits)
+    torch.cuda.synchronize()
+    for i in range(4):
+        b.out.fill_(float(i + 1))
+        b.sel.fill_(-7)
+        b.lse.fill_(0.5)
+        static_call(b, w, splits)  # eager use of the same scratch between replays
+        torch.cuda.synchronize()
+        b.out.fill_(0.0)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert_same(a, b, f"{name} replay {i}")
